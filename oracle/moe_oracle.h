@@ -1,0 +1,103 @@
+/*
+ * moe_oracle.h - plain, slow CPU oracle of one Mixture-of-Experts FFN layer.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may include, link,
+ * load or call this code: only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg use it. It shares no code with the GPU library.
+ *
+ * What it computes (sources: the Colibri pages --
+ *   «Colibri 是什么» (xxqk.cn) §2.1 MoE flow, §2.3 dispatch/expert/combine
+ *     kernels, §3.2 router projection and top-k;
+ *   «Colibri：面向MoE模型的高性能C语言推理引擎» (zskr.cn) §1 gate -> top-k
+ *     -> experts -> weighted sum, §2.2 fused gate matmul + softmax + top-k,
+ *     §3.3 per-expert forward then weighted sum, §4.2 Mixtral w1/w2/w3 shapes;
+ *   «Colibri 是什么» (nxbn.cn) §4.3 expert GEMMs w1*x, w3*x, w2*swiglu_out;
+ *   «Colibri不是一只蜂鸟» (discosf.com) §4.3 (out_dim, in_dim) row-major
+ *     expert matrices and a (hidden_dim, n_experts) router matrix):
+ *
+ *   logits[t][e] = sum_i x[t][i] * W_r[i][e] + b_r[e]            (fp32 result)
+ *   TopK(t)      = first k experts in the order (logit desc, index asc)
+ *   w[t][j]      = exp(l_j - l_0) / sum_{j'<k} exp(l_j' - l_0)    (over the k winners)
+ *   FFN_e(v)     = W_d[e] (SiLU(W_g[e] v) .* (W_u[e] v)),  SiLU(z) = z / (1 + e^-z)
+ *   y[t]         = sum_j w[t][j] * FFN_{e_tj}(x[t])
+ *
+ * and the dispatch as a stable counting sort of the (token, slot) assignments
+ * by expert, in token order.
+ *
+ * Precision: inputs are widened exactly to fp32 (bf16 bits << 16); every dot
+ * product accumulates in double in index order; logits are rounded once to
+ * fp32 (selection uses those fp32 values); routing weights are computed in
+ * double and also reported as fp32; the FFN and the combine stay in double
+ * (h is not rounded), so y is the exact function of the given inputs up to
+ * double rounding.
+ *
+ * Errors: functions return 0 on success and a negative value for an invalid
+ * argument (null pointer, non-positive size, k > E, unknown dtype). Buffers are
+ * caller-owned host memory; nothing is allocated that outlives a call.
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { MOE_ORACLE_F32 = 0, MOE_ORACLE_BF16 = 1 };
+
+/* Host description of one layer. Matrices are row-major:
+ *   w_router [d][E], b_router [E] fp32 (NULL = zeros),
+ *   w_gate, w_up [E][f][d], w_down [E][d][f].
+ * dtype says how w_* and x are stored (fp32 values or bf16 bit patterns). */
+typedef struct {
+    int32_t d, f, E, k, dtype;
+    const void* w_router;
+    const float* b_router;
+    const void* w_gate;
+    const void* w_up;
+    const void* w_down;
+} moe_oracle_layer_t;
+
+/* Exact widening of n elements of a tensor of the given dtype to fp32. */
+int moe_oracle_widen(const void* src, int dtype, int64_t n, float* dst);
+
+/* Router projection: logits [T][E] fp32 (the double sum rounded once). */
+int moe_oracle_router(const moe_oracle_layer_t* L, const void* x, int32_t T, float* logits);
+
+/* Top-k by (logit desc, index asc) and the renormalised softmax over the k
+ * winners. ids [T][k] int32; w [T][k] fp32; w_f64 [T][k] (nullable). */
+int moe_oracle_topk(const float* logits, int32_t T, int32_t E, int32_t k,
+                    int32_t* ids, float* w, double* w_f64);
+
+/* Stable counting sort of assignments (t, j) by expert ids[t*k+j].
+ * counts [E], offsets [E+1], perm [T*k] token ids, perm_slot [T*k] slots,
+ * inv [T*k]: inv[t*k+j] = position p of that assignment. Any output but
+ * counts and offsets may be NULL. Fails if an id is outside [0, E). */
+int moe_oracle_dispatch(const int32_t* ids, int32_t T, int32_t k, int32_t E,
+                        int32_t* counts, int32_t* offsets, int32_t* perm,
+                        int32_t* perm_slot, int32_t* inv);
+
+/* FFN of expert e on one input row v [d] (dtype of the layer), in double:
+ * out [d]. If h_out is not NULL it receives the f values of h. */
+int moe_oracle_expert_ffn(const moe_oracle_layer_t* L, int32_t e, const void* v,
+                          double* out, double* h_out);
+
+/* Whole layer for the tokens in token_list (NULL = all T tokens, in order).
+ * Routing uses the oracle's own logits unless forced_ids [T][k] is given, in
+ * which case those experts are used and their weights come from the oracle's
+ * logits of those experts, taken in the forced slot order (slot 0 is the
+ * reference of the exponent shift).
+ *   y        [n][d] double, row r belongs to token token_list[r] (required)
+ *   Y_slots  [n][k][d] double per-slot expert outputs (nullable)
+ * Returns 0 or a negative error. Parallel over tokens with OpenMP; every
+ * element's arithmetic is independent of the thread count. */
+int moe_oracle_forward(const moe_oracle_layer_t* L, const void* x, int32_t T,
+                       const int32_t* forced_ids, const int32_t* token_list, int32_t n,
+                       double* y, double* Y_slots);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ORACLE_H */

@@ -1,0 +1,201 @@
+"""Benchmark of the MoE FFN layer on one MI355X.
+
+One step = one full forward of the layer (router, dispatch, gate/up GEMM,
+down GEMM, combine) over one batch of synthetic tokens whose inputs and weights
+are already resident in HBM. Default workload: the Mixtral-8x7B-shaped prefill
+layer (T=4096, d_model=4096, E=8, top-2, d_ff=14336, bf16).
+
+Prints one JSON line with the throughput (tokens/s), the roofline position of
+the dominant kernel (measured live with HIP events on the layer's stream), and
+the CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec at 1 GPU; % of peak MFMA (prefill) / HBM GB/s (decode)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (vector and matrix)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+WORKLOAD_NAMES = {
+    "mixtral": "mixtral-8x7b-prefill",
+    "fine-grained": "fine-grained-128e-top4",
+    "decode": "mixtral-8x7b-decode",
+    "skewed": "skewed-64e-top2",
+    "skewed-masked": "skewed-64e-top2-20-empty",
+    "tiny-f32": "tiny-f32",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
+                    help="tokens of the oracle sample (0 = sized to ~20 s of CPU work)")
+    return ap.parse_args()
+
+
+def to_dev(a):
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if a.dtype == np.uint16:
+        t = t.view(torch.int16).view(torch.bfloat16)
+    return t.to("cuda")
+
+
+def gemm_flops_per_assignment(cfg):
+    """Algorithmic flops per (token, slot) assignment of each expert GEMM."""
+    return {"gate_up_gemm": 4.0 * cfg.d * cfg.f, "down_gemm": 2.0 * cfg.d * cfg.f}
+
+
+def active_weight_bytes(cfg, counts, stage):
+    es = cfg.elem_bytes()
+    n_active = int((counts > 0).sum())
+    per = {"gate_up_gemm": 2 * cfg.d * cfg.f * es, "down_gemm": cfg.d * cfg.f * es}[stage]
+    return n_active * per
+
+
+def cpu_baseline(cfg, inp, sample_tokens: int):
+    import oracle
+
+    gomp = ctypes.CDLL("libgomp.so.1")
+    threads = int(gomp.omp_get_max_threads())
+    L = oracle.Layer.from_inputs(inp, cfg.k)
+    x = inp["x"]
+    per_tok_macs = cfg.d * cfg.E + 3 * cfg.d * cfg.f * cfg.k
+    if sample_tokens <= 0:
+        # About 15 s of wall time at ~0.5 GMAC/s per thread for this scalar code.
+        sample_tokens = int(15.0 * threads * 0.5e9 / per_tok_macs)
+        sample_tokens = min(cfg.T, max(threads, sample_tokens))
+    toks = np.arange(sample_tokens, dtype=np.int32)
+    t0 = time.perf_counter()
+    L.forward(x, tokens=toks)
+    dt = time.perf_counter() - t0
+    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {sample_tokens} tokens of the workload (router, top-k and their {cfg.k} "
+                      f"experts' SwiGLU FFN + combine in double), wall {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this layer build has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import sparse_moe_gemm_amd as cm
+
+    cfg = synth.CONFIGS[args.workload]
+    t_gen = time.perf_counter()
+    inp = synth.make_inputs(cfg)
+    t_gen = time.perf_counter() - t_gen
+
+    layer = cm.MoELayer(to_dev(inp["w_router"]), to_dev(inp["b_router"]), to_dev(inp["w_gate"]),
+                        to_dev(inp["w_up"]), to_dev(inp["w_down"]), cfg.k, max_tokens=cfg.T,
+                        flags=cm.FLAG_ASYNC | cm.FLAG_STAGE_TIMING)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    x = to_dev(inp["x"])
+    y = torch.empty_like(x)
+    rt = layer.routing_buffers(cfg.T)
+    keep = {"expert_counts": rt["expert_counts"]}
+    stream = layer.stream
+
+    for _ in range(args.warmup):
+        layer.forward(x, y, keep)
+    torch.cuda.synchronize()
+
+    # Timed region: K back-to-back forwards, events on the layer's stream.
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    t_wall = time.perf_counter()
+    for _ in range(args.steps):
+        layer.forward(x, y, keep)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / args.steps
+
+    # Per-kernel durations: the same K forwards again, reading the library's
+    # per-stage HIP events (recorded on the same stream) after each one.
+    stage_sum = {s: 0.0 for s in cm.STAGES}
+    for _ in range(args.steps):
+        layer.forward(x, y, keep)
+        for s, v in layer.stage_times().items():
+            stage_sum[s] += v
+    stage_ms = {s: v / args.steps for s, v in stage_sum.items()}
+    counts = keep["expert_counts"].cpu().numpy()
+    layer.close()
+
+    tokens_per_s = cfg.T / (ms_per_step * 1e-3)
+    A = cfg.T * cfg.k
+    layer_tflops = cfg.flops() / (ms_per_step * 1e-3) / 1e12
+    peak_mm = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
+
+    fpa = gemm_flops_per_assignment(cfg)
+    dom = max(fpa, key=lambda s: fpa[s] * 1.0)  # gate/up carries 2/3 of the flops
+    decode_like = cfg.T * cfg.k <= 2 * cfg.E * 16
+    if decode_like:
+        # weight streaming bound: algorithmic bytes = active experts' weights
+        dom = max(("gate_up_gemm", "down_gemm"), key=lambda s: stage_ms[s])
+        achieved = active_weight_bytes(cfg, counts, dom) / (stage_ms[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": dom}
+    else:
+        achieved = fpa[dom] * A / (stage_ms[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak_mm, "unit": "TFLOP/s",
+                "frac": achieved / peak_mm, "traffic": None, "kernel": dom}
+
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded SplitMix64 + Box-Muller, bf16 RNE; no trained weights)",
+        "config": {"workload": WORKLOAD_NAMES[args.workload], "T": cfg.T, "d_model": cfg.d,
+                   "n_experts": cfg.E, "top_k": cfg.k, "d_ff": cfg.f, "router_bias": cfg.bias or None},
+        "roofline": roof,
+        "layer_tflops": layer_tflops,
+        "layer_mfma_frac": layer_tflops / peak_mm,
+        "stage_ms": stage_ms,
+        "empty_experts": int((counts == 0).sum()),
+        "wall_s_timed": t_wall,
+        "input_gen_s": t_gen,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,134 @@
+/*
+ * colibri_moe.h - C ABI of one Mixture-of-Experts FFN layer on an MI355X (gfx950).
+ *
+ * The layer (the computation the Colibri engine pages describe: «Colibri 是什么»
+ * (xxqk.cn) §2.1 and §2.3; «Colibri：面向MoE模型的高性能C语言推理引擎»
+ * (zskr.cn) §1 and §3.3):
+ *
+ *   logits[t][e] = sum_i x[t][i] * W_r[i][e] + b_r[e]                 (fp32)
+ *   TopK(t)      = the k largest logits, equal logits -> lower expert index,
+ *                  slot 0 = largest
+ *   w[t][j]      = exp(l_j - l_0) / sum_{j'<k} exp(l_j' - l_0)       (softmax over the winners)
+ *   y[t]         = sum_j w[t][j] * W_down[e] (SiLU(W_gate[e] x[t]) .* (W_up[e] x[t])),  e = ids[t][j]
+ *
+ * computed on the GPU as: fused router (projection + top-k + softmax), dispatch
+ * (histogram, prefix sum, stable permutation by expert), grouped gate/up GEMM
+ * with a SiLU*up epilogue, grouped down GEMM, weighted combine. Experts that
+ * receive no token get no GEMM tiles and their weights are not read.
+ *
+ * Shape of the API: init / forward / free with a status code and a status
+ * string, as the pages' host interface has it (init, infer, free in
+ * «Colibri 是什么» (xxqk.cn) §2.3; the status enum, status string, fixed
+ * expert count and top-k at init, and device-resident caller buffers in
+ * «Colibri不是一只蜂鸟» (discosf.com) §4.4 and §6.1). All library memory is
+ * allocated once by init («Colibri不是一只蜂鸟» (discosf.com) §3.1); forward
+ * allocates nothing.
+ *
+ * Conventions
+ *  - Every tensor pointer is a DEVICE pointer on the device that was current at
+ *    init. Matrices are row-major, dense, no padding.
+ *  - dtype BF16: x, y and all weights are bf16 (raw 16-bit patterns); the router
+ *    bias is fp32; logits, routing weights and all accumulation are fp32.
+ *    dtype F32: everything fp32.
+ *  - The caller owns x, y, the weights it passes to init and every routing_out
+ *    buffer. Init copies (and repacks) the weights into library memory, so the
+ *    caller may free its weight buffers after init returns.
+ *  - Forward runs on the stream given at init (NULL = the default stream). It
+ *    is synchronous (returns when the GPU is done) unless COLIBRI_MOE_FLAG_ASYNC
+ *    is set, in which case it returns after enqueueing. A handle serves one
+ *    stream; calls on one handle must not overlap.
+ *  - On a non-OK return, outputs are undefined.
+ */
+#ifndef COLIBRI_MOE_H
+#define COLIBRI_MOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    COLIBRI_MOE_OK = 0,
+    COLIBRI_MOE_ERR_INVALID_ARG = 1,  /* null where required, T < 0 or > max_tokens, k < 1 or > E, bad dtype */
+    COLIBRI_MOE_ERR_UNSUPPORTED = 2,  /* d_model not a multiple of 128, d_ff not a multiple of 64,
+                                         E > 256, k > 8, max_tokens > 2^24 */
+    COLIBRI_MOE_ERR_ALIGNMENT = 3,    /* a tensor pointer not 16-byte aligned */
+    COLIBRI_MOE_ERR_OUT_OF_MEMORY = 4,/* init could not allocate its memory */
+    COLIBRI_MOE_ERR_HIP = 5           /* a HIP launch, copy or sync failed */
+} colibri_moe_status_t;
+
+typedef enum { COLIBRI_MOE_F32 = 0, COLIBRI_MOE_BF16 = 1 } colibri_moe_dtype_t;
+
+enum {
+    COLIBRI_MOE_FLAG_ASYNC = 1u << 0,       /* forward returns after enqueueing */
+    COLIBRI_MOE_FLAG_STAGE_TIMING = 1u << 1 /* record per-stage GPU times (hipEvents) */
+};
+
+typedef struct {
+    int32_t d_model;     /* d: token width */
+    int32_t d_ff;        /* f: expert hidden width */
+    int32_t n_experts;   /* E, 1..256 */
+    int32_t top_k;       /* k, 1..min(8, E) */
+    int32_t max_tokens;  /* largest T forward will accept; sizes the workspace */
+    colibri_moe_dtype_t dtype;
+    uint32_t flags;      /* COLIBRI_MOE_FLAG_* */
+} colibri_moe_config_t;
+
+/* Device pointers, read only during init (copied and repacked). */
+typedef struct {
+    const void* w_router;  /* [d_model][E], dtype */
+    const float* b_router; /* [E] fp32, or NULL for zeros */
+    const void* w_gate;    /* [E][d_ff][d_model], dtype */
+    const void* w_up;      /* [E][d_ff][d_model], dtype */
+    const void* w_down;    /* [E][d_model][d_ff], dtype */
+} colibri_moe_weights_t;
+
+/* Optional routing outputs of forward, caller-owned device buffers; any field
+ * may be NULL (then that output is not written). A = T * k assignments,
+ * assignment a = t * k + j is slot j of token t. */
+typedef struct {
+    float* logits;          /* [T][E] fp32 router logits (bias included) */
+    int32_t* topk_ids;      /* [T][k] selected experts, slot 0 = largest logit */
+    float* topk_w;          /* [T][k] routing weights, sum to 1 per token */
+    int32_t* expert_counts; /* [E] assignments per expert */
+    int32_t* expert_offsets;/* [E+1] exclusive prefix sum of counts */
+    int32_t* perm;          /* [A] token of sorted position p (segments by expert, tokens ascending) */
+    int32_t* perm_slot;     /* [A] slot j of sorted position p */
+    int32_t* inv;           /* [A] inv[t*k+j] = sorted position of assignment (t, j) */
+} colibri_moe_routing_t;
+
+typedef struct colibri_moe colibri_moe_t; /* opaque handle */
+
+/* Validate cfg, allocate all device memory for max_tokens, copy and repack the
+ * weights, synchronize. hip_stream is a hipStream_t (NULL = default stream)
+ * used by every later forward. On success *out receives the handle. */
+colibri_moe_status_t colibri_moe_init(colibri_moe_t** out, const colibri_moe_config_t* cfg,
+                                      const colibri_moe_weights_t* w, void* hip_stream);
+
+/* y [T][d_model] = MoE layer of x [T][d_model]. T = 0 returns OK and does
+ * nothing. routing_out may be NULL. Allocates nothing. */
+colibri_moe_status_t colibri_moe_forward(colibri_moe_t* h, const void* x, int32_t T, void* y,
+                                         const colibri_moe_routing_t* routing_out);
+
+/* Release everything init allocated (waits for the handle's stream first).
+ * NULL is a no-op. The library keeps a registry of live handles: forward and
+ * free reject a pointer that is not a live handle (never created, or already
+ * freed) with INVALID_ARG instead of touching it. */
+colibri_moe_status_t colibri_moe_free(colibri_moe_t* h);
+
+/* Static text for a status value. */
+const char* colibri_moe_status_string(colibri_moe_status_t s);
+
+/* Stage names and GPU times (ms) of the last forward when the handle was
+ * created with COLIBRI_MOE_FLAG_STAGE_TIMING (waits for that forward to
+ * finish). Stages: 0 router, 1 dispatch, 2 gate/up GEMM, 3 down GEMM,
+ * 4 combine. Writes min(n, 5) values; returns the number of stages. */
+int32_t colibri_moe_stage_times(colibri_moe_t* h, float* ms, int32_t n);
+const char* colibri_moe_stage_name(int32_t stage);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* COLIBRI_MOE_H */

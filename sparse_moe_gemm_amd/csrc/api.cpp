@@ -1,0 +1,349 @@
+// api.cpp - the C ABI (include/colibri_moe.h): validation, one-shot device
+// memory, init-time weight repacking, and the five launches of a forward.
+//
+// Shape of the interface: the pages' init / infer / free with status codes
+// («Colibri 是什么» (xxqk.cn) §2.3, «Colibri不是一只蜂鸟» (discosf.com) §4.4).
+// All device memory is allocated by init in one allocation and carved into
+// weights and workspace («Colibri不是一只蜂鸟» (discosf.com) §3.1 and §5.4:
+// allocate once, no runtime allocation, no fragmentation); forward only
+// enqueues kernels.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <new>
+#include <unordered_set>
+
+#include "../../include/colibri_moe.h"
+#include "common.hpp"
+
+using namespace cmoe;
+
+namespace {
+
+constexpr uint32_t kMagic = 0xC011B41Eu;
+constexpr int kStages = 5;
+constexpr int32_t kMaxTokensLimit = 1 << 24;
+
+const char* const kStageNames[kStages] = {"router", "dispatch", "gate_up_gemm", "down_gemm", "combine"};
+
+}  // namespace
+
+struct colibri_moe {
+    uint32_t magic;
+    colibri_moe_config_t cfg;
+    int device;
+    hipStream_t stream;
+    int esize;
+    void* arena;
+    size_t arena_bytes;
+    // weights (library copies, repacked)
+    void* w_rt;   // [E][d]
+    float* b_r;   // [E]
+    void* w_gu;   // [E][2f][d], gate/up interleaved by 16 rows
+    void* w_d;    // [E][d][f]
+    // workspace, sized for max_tokens
+    float* topw;
+    int32_t* ids;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* perm;
+    int32_t* perm_slot;
+    int32_t* inv;
+    void* H;      // [A][f] dtype
+    float* Ys;    // [A][d] fp32
+    bool timing;
+    hipEvent_t ev[kStages + 1];
+};
+
+namespace {
+
+std::mutex g_mu;
+std::unordered_set<colibri_moe*> g_live;
+
+bool is_live(colibri_moe* h)
+{
+    std::lock_guard<std::mutex> lk(g_mu);
+    return g_live.count(h) != 0;
+}
+
+bool aligned16(const void* p)
+{
+    return ((uintptr_t)p & 15u) == 0;
+}
+
+size_t round_up(size_t v, size_t a)
+{
+    return (v + a - 1) / a * a;
+}
+
+// Carves sub-buffers out of one allocation, 256-byte aligned.
+struct Carver {
+    size_t off = 0;
+    size_t take(size_t bytes)
+    {
+        const size_t at = off;
+        off = round_up(off + bytes, 256);
+        return at;
+    }
+};
+
+colibri_moe_status_t validate_config(const colibri_moe_config_t* c)
+{
+    if (c->dtype != COLIBRI_MOE_F32 && c->dtype != COLIBRI_MOE_BF16)
+        return COLIBRI_MOE_ERR_INVALID_ARG;
+    if (c->d_model <= 0 || c->d_ff <= 0 || c->n_experts <= 0 || c->max_tokens <= 0)
+        return COLIBRI_MOE_ERR_INVALID_ARG;
+    if (c->top_k < 1 || c->top_k > c->n_experts)
+        return COLIBRI_MOE_ERR_INVALID_ARG;
+    if (c->n_experts > kMaxExperts || c->top_k > kMaxTopK)
+        return COLIBRI_MOE_ERR_UNSUPPORTED;
+    if (c->d_model % 128 != 0 || c->d_ff % 64 != 0)
+        return COLIBRI_MOE_ERR_UNSUPPORTED;
+    if (c->max_tokens > kMaxTokensLimit)
+        return COLIBRI_MOE_ERR_UNSUPPORTED;
+    return COLIBRI_MOE_OK;
+}
+
+#define CMOE_HIP(call)                      \
+    do {                                    \
+        if ((call) != hipSuccess)           \
+            return COLIBRI_MOE_ERR_HIP;     \
+    } while (0)
+
+void release(colibri_moe* h)
+{
+    if (h->arena)
+        (void)hipFree(h->arena);
+    for (int i = 0; i <= kStages; ++i)
+        if (h->ev[i])
+            (void)hipEventDestroy(h->ev[i]);
+    h->magic = 0;
+    delete h;
+}
+
+colibri_moe_status_t init_impl(colibri_moe* h, const colibri_moe_weights_t* w)
+{
+    const colibri_moe_config_t& c = h->cfg;
+    const size_t es = (size_t)h->esize;
+    const size_t d = c.d_model, f = c.d_ff, E = c.n_experts, k = c.top_k;
+    const size_t A = (size_t)c.max_tokens * k;
+
+    Carver cv;
+    const size_t o_wrt = cv.take(E * d * es);
+    const size_t o_br = cv.take(E * sizeof(float));
+    const size_t o_wgu = cv.take(E * 2 * f * d * es);
+    const size_t o_wd = cv.take(E * d * f * es);
+    const size_t o_topw = cv.take(A * sizeof(float));
+    const size_t o_ids = cv.take(A * sizeof(int32_t));
+    const size_t o_cnt = cv.take(E * sizeof(int32_t));
+    const size_t o_off = cv.take((E + 1) * sizeof(int32_t));
+    const size_t o_perm = cv.take(A * sizeof(int32_t));
+    const size_t o_ps = cv.take(A * sizeof(int32_t));
+    const size_t o_inv = cv.take(A * sizeof(int32_t));
+    const size_t o_h = cv.take(A * f * es);
+    const size_t o_ys = cv.take(A * d * sizeof(float));
+    h->arena_bytes = cv.off;
+
+    if (hipMalloc(&h->arena, h->arena_bytes) != hipSuccess) {
+        h->arena = nullptr;
+        (void)hipGetLastError();
+        return COLIBRI_MOE_ERR_OUT_OF_MEMORY;
+    }
+    uint8_t* base = (uint8_t*)h->arena;
+    h->w_rt = base + o_wrt;
+    h->b_r = (float*)(base + o_br);
+    h->w_gu = base + o_wgu;
+    h->w_d = base + o_wd;
+    h->topw = (float*)(base + o_topw);
+    h->ids = (int32_t*)(base + o_ids);
+    h->counts = (int32_t*)(base + o_cnt);
+    h->offsets = (int32_t*)(base + o_off);
+    h->perm = (int32_t*)(base + o_perm);
+    h->perm_slot = (int32_t*)(base + o_ps);
+    h->inv = (int32_t*)(base + o_inv);
+    h->H = base + o_h;
+    h->Ys = (float*)(base + o_ys);
+
+    hipStream_t s = h->stream;
+    CMOE_HIP(launch_transpose_router(w->w_router, h->w_rt, (int)d, (int)E, (int)es, s));
+    if (w->b_router)
+        CMOE_HIP(hipMemcpyAsync(h->b_r, w->b_router, E * sizeof(float), hipMemcpyDeviceToDevice, s));
+    else
+        CMOE_HIP(hipMemsetAsync(h->b_r, 0, E * sizeof(float), s));
+    CMOE_HIP(launch_interleave_gate_up(w->w_gate, w->w_up, h->w_gu, (int)E, (int)f, (int)d, (int)es, s));
+    CMOE_HIP(hipMemcpyAsync(h->w_d, w->w_down, E * d * f * es, hipMemcpyDeviceToDevice, s));
+    if (h->timing)
+        for (int i = 0; i <= kStages; ++i)
+            CMOE_HIP(hipEventCreate(&h->ev[i]));
+    CMOE_HIP(hipStreamSynchronize(s));
+    return COLIBRI_MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+colibri_moe_status_t colibri_moe_init(colibri_moe_t** out, const colibri_moe_config_t* cfg,
+                                      const colibri_moe_weights_t* w, void* hip_stream)
+{
+    if (!out || !cfg || !w)
+        return COLIBRI_MOE_ERR_INVALID_ARG;
+    *out = nullptr;
+    colibri_moe_status_t st = validate_config(cfg);
+    if (st != COLIBRI_MOE_OK)
+        return st;
+    if (!w->w_router || !w->w_gate || !w->w_up || !w->w_down)
+        return COLIBRI_MOE_ERR_INVALID_ARG;
+    if (!aligned16(w->w_router) || !aligned16(w->w_gate) || !aligned16(w->w_up) || !aligned16(w->w_down) ||
+        ((uintptr_t)w->b_router & 3u))
+        return COLIBRI_MOE_ERR_ALIGNMENT;
+
+    colibri_moe* h = new (std::nothrow) colibri_moe();
+    if (!h)
+        return COLIBRI_MOE_ERR_OUT_OF_MEMORY;
+    h->magic = kMagic;
+    h->cfg = *cfg;
+    h->stream = (hipStream_t)hip_stream;
+    h->esize = cfg->dtype == COLIBRI_MOE_BF16 ? 2 : 4;
+    h->timing = (cfg->flags & COLIBRI_MOE_FLAG_STAGE_TIMING) != 0;
+    if (hipGetDevice(&h->device) != hipSuccess) {
+        release(h);
+        return COLIBRI_MOE_ERR_HIP;
+    }
+    st = init_impl(h, w);
+    if (st != COLIBRI_MOE_OK) {
+        release(h);
+        return st;
+    }
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        g_live.insert(h);
+    }
+    *out = h;
+    return COLIBRI_MOE_OK;
+}
+
+colibri_moe_status_t colibri_moe_forward(colibri_moe_t* h, const void* x, int32_t T, void* y,
+                                         const colibri_moe_routing_t* r)
+{
+    if (!h || !is_live(h) || h->magic != kMagic)
+        return COLIBRI_MOE_ERR_INVALID_ARG;
+    const colibri_moe_config_t& c = h->cfg;
+    if (T < 0 || T > c.max_tokens)
+        return COLIBRI_MOE_ERR_INVALID_ARG;
+    if (T == 0)
+        return COLIBRI_MOE_OK;
+    if (!x || !y)
+        return COLIBRI_MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(y))
+        return COLIBRI_MOE_ERR_ALIGNMENT;
+
+    colibri_moe_routing_t ro = {};
+    if (r)
+        ro = *r;
+    // Caller-provided routing buffers double as the working buffers (no copy).
+    float* topw = ro.topk_w ? ro.topk_w : h->topw;
+    int32_t* ids = ro.topk_ids ? ro.topk_ids : h->ids;
+    int32_t* counts = ro.expert_counts ? ro.expert_counts : h->counts;
+    int32_t* offsets = ro.expert_offsets ? ro.expert_offsets : h->offsets;
+    int32_t* perm = ro.perm ? ro.perm : h->perm;
+    int32_t* perm_slot = ro.perm_slot ? ro.perm_slot : h->perm_slot;
+    int32_t* inv = ro.inv ? ro.inv : h->inv;
+    if (((uintptr_t)ids & 15u) || ((uintptr_t)topw & 3u) || ((uintptr_t)counts & 3u) ||
+        ((uintptr_t)offsets & 3u) || ((uintptr_t)perm & 3u) || ((uintptr_t)perm_slot & 3u) ||
+        ((uintptr_t)inv & 3u) || ((uintptr_t)ro.logits & 3u))
+        return COLIBRI_MOE_ERR_ALIGNMENT;
+
+    const bool bf = c.dtype == COLIBRI_MOE_BF16;
+    hipStream_t s = h->stream;
+    const bool tm = h->timing;
+    if (tm)
+        CMOE_HIP(hipEventRecord(h->ev[0], s));
+
+    RouterArgs ra{x, h->w_rt, h->b_r, T, c.d_model, c.n_experts, c.top_k, ro.logits, ids, topw};
+    CMOE_HIP(bf ? launch_router_bf16(ra, s) : launch_router_f32(ra, s));
+    if (tm)
+        CMOE_HIP(hipEventRecord(h->ev[1], s));
+
+    DispatchArgs da{ids, T, c.top_k, c.n_experts, counts, offsets, perm, perm_slot, inv};
+    CMOE_HIP(launch_dispatch(da, s));
+    if (tm)
+        CMOE_HIP(hipEventRecord(h->ev[2], s));
+
+    GemmArgs gu{x, h->w_gu, h->H, offsets, perm, perm_slot, T * c.top_k, c.n_experts, c.top_k, c.d_model,
+                c.d_ff};
+    CMOE_HIP(bf ? launch_gate_up_bf16(gu, s) : launch_gate_up_f32(gu, s));
+    if (tm)
+        CMOE_HIP(hipEventRecord(h->ev[3], s));
+
+    GemmArgs dn{h->H, h->w_d, h->Ys, offsets, perm, perm_slot, T * c.top_k, c.n_experts, c.top_k, c.d_model,
+                c.d_ff};
+    CMOE_HIP(bf ? launch_down_bf16(dn, s) : launch_down_f32(dn, s));
+    if (tm)
+        CMOE_HIP(hipEventRecord(h->ev[4], s));
+
+    CombineArgs ca{h->Ys, topw, y, T, c.top_k, c.d_model, bf ? 1 : 0};
+    CMOE_HIP(launch_combine(ca, s));
+    if (tm)
+        CMOE_HIP(hipEventRecord(h->ev[5], s));
+
+    if (!(c.flags & COLIBRI_MOE_FLAG_ASYNC))
+        CMOE_HIP(hipStreamSynchronize(s));
+    return COLIBRI_MOE_OK;
+}
+
+colibri_moe_status_t colibri_moe_free(colibri_moe_t* h)
+{
+    if (!h)
+        return COLIBRI_MOE_OK;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        if (!g_live.erase(h))
+            return COLIBRI_MOE_ERR_INVALID_ARG;
+    }
+    const bool ok = hipStreamSynchronize(h->stream) == hipSuccess;
+    release(h);
+    return ok ? COLIBRI_MOE_OK : COLIBRI_MOE_ERR_HIP;
+}
+
+const char* colibri_moe_status_string(colibri_moe_status_t s)
+{
+    switch (s) {
+    case COLIBRI_MOE_OK:
+        return "ok";
+    case COLIBRI_MOE_ERR_INVALID_ARG:
+        return "invalid argument";
+    case COLIBRI_MOE_ERR_UNSUPPORTED:
+        return "unsupported configuration";
+    case COLIBRI_MOE_ERR_ALIGNMENT:
+        return "pointer not 16-byte aligned";
+    case COLIBRI_MOE_ERR_OUT_OF_MEMORY:
+        return "out of device memory";
+    case COLIBRI_MOE_ERR_HIP:
+        return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int32_t colibri_moe_stage_times(colibri_moe_t* h, float* ms, int32_t n)
+{
+    if (!h || !is_live(h) || !h->timing)
+        return -1;
+    if (hipEventSynchronize(h->ev[kStages]) != hipSuccess)
+        return -1;
+    for (int i = 0; i < kStages && i < n; ++i) {
+        float v = 0.f;
+        if (hipEventElapsedTime(&v, h->ev[i], h->ev[i + 1]) != hipSuccess)
+            return -1;
+        if (ms)
+            ms[i] = v;
+    }
+    return kStages;
+}
+
+const char* colibri_moe_stage_name(int32_t stage)
+{
+    return (stage >= 0 && stage < kStages) ? kStageNames[stage] : nullptr;
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// combine.hip - weighted sum of each token's k expert outputs.
+//
+// The combine kernel of «Colibri 是什么» (xxqk.cn) §2.3 (the k expert outputs
+// weighted by the gating scores and summed) and the final step of
+// «Colibri：面向MoE模型的高性能C语言推理引擎» (zskr.cn) §3.3:
+//   y[t][o] = sum_{j<k} w[t][j] * Ys[t*k + j][o]
+// accumulated in fp32 in slot order (fused multiply-add), then rounded to
+// the output dtype (round to nearest even for bf16). The down GEMM already
+// wrote each expert output at its assignment row t*k+j, so each thread reads
+// k contiguous-by-slot rows with 16-byte loads; the kernel is bound by HBM.
+#include "common.hpp"
+
+namespace cmoe {
+
+namespace {
+
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs g)
+{
+    const int64_t groups = (int64_t)g.T * (g.d / 4);
+    for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < groups;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t t = idx / (g.d / 4);
+        const int o = (int)(idx % (g.d / 4)) * 4;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int j = 0; j < g.k; ++j) {
+            const float wj = g.w[t * g.k + j];
+            const float4 v = *(const float4*)(g.ys + (t * g.k + j) * g.d + o);
+            acc.x = fmaf(wj, v.x, acc.x);
+            acc.y = fmaf(wj, v.y, acc.y);
+            acc.z = fmaf(wj, v.z, acc.z);
+            acc.w = fmaf(wj, v.w, acc.w);
+        }
+        if (g.bf16_out) {
+            uint2 packed;
+            packed.x = (uint32_t)f32_to_bf16_bits(acc.x) | ((uint32_t)f32_to_bf16_bits(acc.y) << 16);
+            packed.y = (uint32_t)f32_to_bf16_bits(acc.z) | ((uint32_t)f32_to_bf16_bits(acc.w) << 16);
+            *(uint2*)((uint16_t*)g.y + t * g.d + o) = packed;
+        } else {
+            *(float4*)((float*)g.y + t * g.d + o) = acc;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s)
+{
+    const int64_t groups = (int64_t)a.T * (a.d / 4);
+    int64_t blocks = (groups + 255) / 256;
+    if (blocks > 8192)
+        blocks = 8192;
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace cmoe

@@ -1,0 +1,106 @@
+// common.hpp - types and small device helpers shared by the gfx950 kernels of
+// the MoE layer, plus the host-side launch declarations used by api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cmoe {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;       // CDNA wavefront width
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopK = 8;
+
+// Raw 16-byte vector moved between global memory, LDS and MFMA operands.
+struct alignas(16) Vec16 {
+    uint32_t w[4];
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const Vec16& v)
+{
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b)
+{
+    return __uint_as_float((uint32_t)b << 16);
+}
+
+// Round to nearest even (gfx950 converts in hardware).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f)
+{
+    return __builtin_bit_cast(uint16_t, static_cast<bf16>(f));
+}
+
+__device__ __forceinline__ float silu(float z)
+{
+    return z / (1.0f + __expf(-z));
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launchers (each defined in the .hip file of its kernel).
+// All enqueue on `s` and return the launch status.
+// ---------------------------------------------------------------------------
+
+struct RouterArgs {
+    const void* x;      // [T][d] dtype
+    const void* w_rt;   // router weights transposed: [E][d] dtype
+    const float* b;     // [E] fp32 (never NULL: zeros when the caller gave none)
+    int T, d, E, k;
+    float* logits;      // [T][E] (may be NULL)
+    int32_t* ids;       // [T][k]
+    float* w;           // [T][k]
+};
+hipError_t launch_router_bf16(const RouterArgs& a, hipStream_t s);
+hipError_t launch_router_f32(const RouterArgs& a, hipStream_t s);
+
+struct DispatchArgs {
+    const int32_t* ids; // [A]
+    int T, k, E;
+    int32_t* counts;    // [E]
+    int32_t* offsets;   // [E+1]
+    int32_t* perm;      // [A]
+    int32_t* perm_slot; // [A]
+    int32_t* inv;       // [A]
+};
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
+
+struct GemmArgs {
+    // gate/up: A rows are x[perm[p]] ([T][d]); B = interleaved gate/up weights
+    //   [E][2f][d]; out = H [A][f].
+    // down:    A rows are H[p] ([A][f]);        B = down weights [E][d][f];
+    //   out = Ys [A][d] fp32, row p written to assignment row perm[p]*k+perm_slot[p].
+    const void* a;
+    const void* b;
+    void* out;
+    const int32_t* offsets;   // [E+1]
+    const int32_t* perm;      // [A]
+    const int32_t* perm_slot; // [A]
+    int A_max;                // T*k of this call (bounds the tile grid)
+    int E, k, d, f;
+};
+hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t s);
+hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gate_up_f32(const GemmArgs& a, hipStream_t s);
+hipError_t launch_down_f32(const GemmArgs& a, hipStream_t s);
+
+struct CombineArgs {
+    const float* ys;    // [T*k][d] fp32, row t*k+j
+    const float* w;     // [T][k]
+    void* y;            // [T][d] dtype
+    int T, k, d;
+    int bf16_out;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+// Init-time weight repacks.
+hipError_t launch_transpose_router(const void* w_r, void* w_rt, int d, int E, int esize, hipStream_t s);
+hipError_t launch_interleave_gate_up(const void* wg, const void* wu, void* wgu, int E, int f, int d,
+                                     int esize, hipStream_t s);
+
+}  // namespace cmoe

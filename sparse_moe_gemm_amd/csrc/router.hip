@@ -1,0 +1,244 @@
+// router.hip - fused router: projection, top-k and softmax over the winners.
+//
+// One launch computes, for a block of 16 tokens,
+//   logits[t][e] = sum_i x[t][i] * W_r[i][e] + b_r[e]      (fp32 accumulation)
+// then selects the k largest logits per token (equal logits -> lower expert
+// index, slot 0 = largest) and the renormalised softmax over those k:
+//   w[t][j] = exp(l_j - l_0) / sum_j' exp(l_j' - l_0).
+// This is the router of «Colibri 是什么» (xxqk.cn) §3.2 (a linear projection plus
+// router bias, then a top-k selection on the logits) fused the way
+// «Colibri：面向MoE模型的高性能C语言推理引擎» (zskr.cn) §2.2 and
+// «Colibri不是一只蜂鸟» (discosf.com) §5.1 describe (projection, softmax and
+// top-k in one pass with the intermediates kept on chip). Selection only needs
+// the order of the logits, so exponentials are taken for the k winners only.
+//
+// bf16 path: the projection runs on v_mfma_f32_16x16x32_bf16 (16 tokens x 16
+// experts per MFMA); the 4 waves of a block split the reduction dimension in
+// interleaved 32-wide steps and add their partial sums through LDS in a fixed
+// order, so results are bit-reproducible.
+// fp32 path: plain FMA dot products (gfx950 has no faster fp32 matrix rate).
+#include "common.hpp"
+
+namespace cmoe {
+
+namespace {
+
+constexpr int kTok = 16;     // tokens per block
+constexpr int kThreads = 256;
+
+// Monotone map of a float to an unsigned key (larger float -> larger key).
+// -0 is first turned into +0 so that the two zeros tie, as they compare equal.
+__device__ __forceinline__ uint32_t order_key(float f)
+{
+    if (f == 0.0f)
+        f = 0.0f;
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        uint32_t lo = __shfl_xor((uint32_t)v, off, kWave);
+        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, kWave);
+        unsigned long long o = ((unsigned long long)hi << 32) | lo;
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+// Top-k + softmax for the block's tokens, reading logits (bias included) from
+// LDS `lg` laid out [kTok][ldl]. Each wave handles 4 tokens.
+__device__ void topk_softmax_epilogue(const float* lg, int ldl, int t0, int T, int E, int k,
+                                      int32_t* ids, float* wout)
+{
+    const int lane = threadIdx.x % kWave;
+    const int wv = threadIdx.x / kWave;
+    for (int r = wv; r < kTok; r += kThreads / kWave) {
+        const int t = t0 + r;
+        if (t >= T)
+            break;
+        unsigned long long key[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = lane + q * kWave;
+            key[q] = e < E ? (((unsigned long long)order_key(lg[r * ldl + e]) << 32) |
+                              (uint32_t)(0xFFFFu - e))
+                           : 0ull;
+        }
+        float lsel[kMaxTopK];
+        int isel[kMaxTopK];
+        for (int j = 0; j < k; ++j) {
+            unsigned long long best = key[0];
+#pragma unroll
+            for (int q = 1; q < 4; ++q)
+                best = key[q] > best ? key[q] : best;
+            best = wave_max_u64(best);
+            const int e = min(0xFFFF - (int)(best & 0xFFFFu), E - 1);
+            isel[j] = e;
+            lsel[j] = lg[r * ldl + e];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (key[q] == best)
+                    key[q] = 0ull;
+        }
+        if (lane == 0) {
+            const float l0 = lsel[0];
+            float ex[kMaxTopK];
+            float s = 0.0f;
+            for (int j = 0; j < k; ++j) {
+                ex[j] = __expf(lsel[j] - l0);
+                s += ex[j];
+            }
+            const float inv = 1.0f / s;
+            for (int j = 0; j < k; ++j) {
+                ids[(int64_t)t * k + j] = isel[j];
+                wout[(int64_t)t * k + j] = ex[j] * inv;
+            }
+        }
+    }
+}
+
+__device__ void store_logits(const float* lg, int ldl, int t0, int T, int E, float* logits)
+{
+    if (!logits)
+        return;
+    for (int i = threadIdx.x; i < kTok * E; i += kThreads) {
+        const int r = i / E, e = i % E;
+        if (t0 + r < T)
+            logits[(int64_t)(t0 + r) * E + e] = lg[r * ldl + e];
+    }
+}
+
+// NG = number of 16-expert column groups (E <= 16 * NG).
+template <int NG>
+__global__ __launch_bounds__(kThreads) void router_bf16_kernel(RouterArgs a)
+{
+    constexpr int EP = 16 * NG;      // padded expert count
+    constexpr int LDL = EP + 1;      // LDS row stride (floats)
+    __shared__ float part[kTok][LDL];
+
+    const int lane = threadIdx.x % kWave;
+    const int wv = threadIdx.x / kWave;
+    const int t0 = blockIdx.x * kTok;
+    const int d = a.d;
+
+    // Fragment rows: token row for A, expert row for B (clamped: padded rows
+    // read valid memory and their results are dropped).
+    const int trow = min(t0 + (lane & 15), a.T - 1);
+    const int kq = (lane >> 4) * 8;
+    const uint16_t* xr = (const uint16_t*)a.x + (int64_t)trow * d + kq;
+    const uint16_t* wr[NG];
+#pragma unroll
+    for (int n = 0; n < NG; ++n)
+        wr[n] = (const uint16_t*)a.w_rt + (int64_t)min(n * 16 + (lane & 15), a.E - 1) * d + kq;
+
+    floatx4 acc[NG];
+#pragma unroll
+    for (int n = 0; n < NG; ++n)
+        acc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    const int steps = d / 32;
+    for (int s = wv; s < steps; s += 4) {
+        const int k0 = s * 32;
+        Vec16 av = *(const Vec16*)(xr + k0);
+        Vec16 bv[NG];
+#pragma unroll
+        for (int n = 0; n < NG; ++n)
+            bv[n] = *(const Vec16*)(wr[n] + k0);
+#pragma unroll
+        for (int n = 0; n < NG; ++n)
+            acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv[n]), acc[n], 0, 0, 0);
+    }
+
+    // D layout of a 16x16 MFMA: lane holds rows 4*(lane/16)+i, column lane%16.
+    // The four partial sums are added in wave order ((w0 + w1) + w2) + w3.
+    for (int w = 0; w < 4; ++w) {
+        if (wv == w) {
+#pragma unroll
+            for (int n = 0; n < NG; ++n)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float& dst = part[(lane >> 4) * 4 + i][n * 16 + (lane & 15)];
+                    dst = (w == 0) ? acc[n][i] : dst + acc[n][i];
+                }
+        }
+        __syncthreads();
+    }
+    for (int i = threadIdx.x; i < kTok * a.E; i += kThreads) {
+        const int r = i / a.E, e = i % a.E;
+        part[r][e] += a.b[e];
+    }
+    __syncthreads();
+    store_logits(&part[0][0], LDL, t0, a.T, a.E, a.logits);
+    topk_softmax_epilogue(&part[0][0], LDL, t0, a.T, a.E, a.k, a.ids, a.w);
+}
+
+__global__ __launch_bounds__(kThreads) void router_f32_kernel(RouterArgs a)
+{
+    __shared__ float lg[kTok][kMaxExperts + 1];
+    const int t0 = blockIdx.x * kTok;
+    const float* x = (const float*)a.x;
+    const float* wt = (const float*)a.w_rt;
+    for (int i = threadIdx.x; i < kTok * a.E; i += kThreads) {
+        const int r = i / a.E, e = i % a.E;
+        const int t = min(t0 + r, a.T - 1);
+        const float* xr = x + (int64_t)t * a.d;
+        const float* wr = wt + (int64_t)e * a.d;
+        float s = 0.0f;
+        for (int c = 0; c < a.d; ++c)
+            s = fmaf(xr[c], wr[c], s);
+        lg[r][e] = s + a.b[e];
+    }
+    __syncthreads();
+    store_logits(&lg[0][0], kMaxExperts + 1, t0, a.T, a.E, a.logits);
+    topk_softmax_epilogue(&lg[0][0], kMaxExperts + 1, t0, a.T, a.E, a.k, a.ids, a.w);
+}
+
+__global__ void transpose_router_kernel(const uint8_t* src, uint8_t* dst, int d, int E, int esize)
+{
+    // dst[e][i] = src[i][e]
+    const int64_t n = (int64_t)d * E;
+    for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < n;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t e = idx / d, i = idx % d;
+        const uint8_t* s = src + (i * E + e) * esize;
+        uint8_t* o = dst + idx * esize;
+        for (int b = 0; b < esize; ++b)
+            o[b] = s[b];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_router_bf16(const RouterArgs& a, hipStream_t s)
+{
+    const dim3 grid((a.T + kTok - 1) / kTok), block(kThreads);
+    if (a.E <= 16)
+        hipLaunchKernelGGL(router_bf16_kernel<1>, grid, block, 0, s, a);
+    else if (a.E <= 32)
+        hipLaunchKernelGGL(router_bf16_kernel<2>, grid, block, 0, s, a);
+    else if (a.E <= 64)
+        hipLaunchKernelGGL(router_bf16_kernel<4>, grid, block, 0, s, a);
+    else if (a.E <= 128)
+        hipLaunchKernelGGL(router_bf16_kernel<8>, grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL(router_bf16_kernel<16>, grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_router_f32(const RouterArgs& a, hipStream_t s)
+{
+    hipLaunchKernelGGL(router_f32_kernel, dim3((a.T + kTok - 1) / kTok), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose_router(const void* w_r, void* w_rt, int d, int E, int esize, hipStream_t s)
+{
+    hipLaunchKernelGGL(transpose_router_kernel, dim3(256), dim3(256), 0, s, (const uint8_t*)w_r,
+                       (uint8_t*)w_rt, d, E, esize);
+    return hipGetLastError();
+}
+
+}  // namespace cmoe

@@ -1,0 +1,128 @@
+"""GPU parity of the whole layer through the C ABI against the CPU oracle.
+
+Small cases (every token checked) keep the shapes of the five workloads at
+sizes the oracle finishes in seconds, with several m- and n-tiles per expert and
+ragged tails; the full-size workloads check routing and dispatch on every token
+and the output on sampled tokens (the edges of every expert segment, i.e. the
+first and the ragged last m-tile rows, plus random tokens).
+"""
+import numpy as np
+import pytest
+
+import synth
+from moe_case import compare, make_layer, run_gpu, sample_tokens
+
+pytestmark = pytest.mark.gpu
+
+C = synth.LayerConfig
+SMALL = [
+    synth.CONFIGS["tiny-f32"],
+    C("mixtral-small", 700, 256, 8, 2, 512, "bf16"),
+    C("fine-grained-small", 1000, 256, 128, 4, 192, "bf16"),
+    C("decode-small", 32, 512, 8, 2, 1024, "bf16"),
+    C("skewed-small", 2000, 256, 64, 2, 128, "bf16", {0: 4.0, 3: 4.0}),
+    C("skewed-masked-small", 2000, 256, 64, 2, 128, "bf16",
+      {0: 4.0, 3: 4.0, **{e: -1.0e4 for e in range(44, 64)}}),
+    C("f32-ragged", 77, 256, 6, 3, 192, "f32", {2: 0.3}),
+    C("one-token", 1, 128, 8, 2, 64, "bf16"),
+    C("ragged-17", 17, 384, 16, 3, 320, "bf16"),
+    C("single-expert", 130, 128, 1, 1, 128, "bf16"),
+    C("k-equals-E", 90, 256, 4, 4, 128, "bf16"),
+    C("all-to-one", 300, 128, 8, 1, 128, "bf16", {5: 100.0}),
+    C("k8-E256", 64, 128, 256, 8, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=[c.name for c in SMALL])
+def test_small_layer_parity(cfg):
+    print(f"case {cfg}", flush=True)
+    inp = synth.make_inputs(cfg)
+    layer = make_layer(cfg, inp)
+    g = run_gpu(layer, inp["x"])
+    layer.close()
+    rep = compare(cfg, inp, g)
+    print(rep, flush=True)
+    if cfg.name == "all-to-one":
+        assert g["expert_counts"][5] == cfg.T and rep["empty_experts"] == cfg.E - 1
+    if cfg.name == "skewed-masked-small":
+        assert np.all(g["expert_counts"][44:] == 0)
+
+
+def test_empty_batch_and_errors():
+    import torch
+
+    import sparse_moe_gemm_amd as cm
+
+    cfg = C("errs", 8, 128, 4, 2, 64, "bf16")
+    inp = synth.make_inputs(cfg)
+    layer = make_layer(cfg, inp, max_tokens=8)
+    x = torch.zeros(16, 128, dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros_like(x)
+    assert cm.colibri_moe_forward(layer.handle, x.data_ptr(), 0, y.data_ptr()) == cm.OK
+    assert cm.colibri_moe_forward(layer.handle, x.data_ptr(), 9, y.data_ptr()) == cm.ERR_INVALID_ARG
+    assert cm.colibri_moe_forward(layer.handle, x.data_ptr(), -1, y.data_ptr()) == cm.ERR_INVALID_ARG
+    assert cm.colibri_moe_forward(layer.handle, x.data_ptr() + 2, 4, y.data_ptr()) == cm.ERR_ALIGNMENT
+    assert cm.colibri_moe_forward(layer.handle, 0, 4, y.data_ptr()) == cm.ERR_INVALID_ARG
+    h = layer.handle
+    layer.close()
+    assert cm.colibri_moe_free(h) == cm.ERR_INVALID_ARG
+    assert cm.colibri_moe_forward(h, x.data_ptr(), 4, y.data_ptr()) == cm.ERR_INVALID_ARG
+
+
+def test_handle_reuse_with_smaller_batch_and_determinism():
+    cfg = C("reuse", 500, 256, 16, 2, 256, "bf16", {1: 1.0})
+    inp = synth.make_inputs(cfg)
+    layer = make_layer(cfg, inp, max_tokens=512)
+    g1 = run_gpu(layer, inp["x"])
+    g2 = run_gpu(layer, inp["x"][:123])
+    g3 = run_gpu(layer, inp["x"])
+    layer.close()
+    for key in g1:
+        assert np.array_equal(g1[key], g3[key]), f"{key} not bit-reproducible"
+    fresh = make_layer(cfg, inp, max_tokens=123)
+    g4 = run_gpu(fresh, inp["x"][:123])
+    fresh.close()
+    for key in g2:
+        assert np.array_equal(g2[key], g4[key]), f"{key} depends on earlier calls"
+    assert np.array_equal(g2["y"], g1["y"][:123])
+    compare(cfg.with_(T=123), dict(inp, x=inp["x"][:123]), g2)
+
+
+def test_partial_routing_outputs():
+    import torch
+
+    cfg = C("partial", 200, 256, 8, 2, 128, "bf16")
+    inp = synth.make_inputs(cfg)
+    layer = make_layer(cfg, inp)
+    full = run_gpu(layer, inp["x"])
+    from moe_case import to_dev, to_f64
+
+    x = to_dev(inp["x"])
+    y0 = to_f64(layer.forward(x))
+    rt = layer.routing_buffers(cfg.T)
+    some = {"perm": rt["perm"], "topk_w": rt["topk_w"]}
+    y1 = to_f64(layer.forward(x, routing=some))
+    torch.cuda.synchronize()
+    layer.close()
+    assert np.array_equal(y0, full["y"]) and np.array_equal(y1, full["y"])
+    assert np.array_equal(some["perm"].cpu().numpy(), full["perm"])
+
+
+FULL = ["tiny-f32", "mixtral", "fine-grained", "decode", "skewed", "skewed-masked"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workload(name):
+    cfg = synth.CONFIGS[name]
+    print(f"full-size case {cfg}", flush=True)
+    inp = synth.make_inputs(cfg)
+    layer = make_layer(cfg, inp)
+    g = run_gpu(layer, inp["x"])
+    layer.close()
+    toks = None if cfg.T <= 64 else sample_tokens(g, cfg.T)
+    rep = compare(cfg, inp, g, tokens=toks)
+    print(name, rep, flush=True)
+    if name == "decode":
+        assert np.all(g["expert_counts"] > 0), "every expert is hit in the decode batch"
+    if name == "skewed-masked":
+        assert rep["empty_experts"] == 20

@@ -16,10 +16,9 @@ constexpr int kWave = 64;       // CDNA wavefront width
 constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 8;
 
-// Raw 16-byte vector moved between global memory, LDS and MFMA operands.
-struct alignas(16) Vec16 {
-    uint32_t w[4];
-};
+// Raw 16-byte vector moved between global memory, LDS and MFMA operands (a
+// native vector type, so it always lives in registers).
+typedef uint32_t Vec16 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const Vec16& v)
 {

@@ -101,19 +101,128 @@ __device__ void find_tile(const int32_t* offsets, int E, int NT, Tile* out)
     }
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One K-stage of a tile lives in LDS as rows of 8 16-byte chunks (64 bf16 of
+// K), chunk index XOR-swizzled per row. Stages are filled with gfx950's direct
+// global->LDS loads (global_load_lds_dwordx4): one instruction moves 64 lanes x
+// 16 B into 1 KiB of LDS, i.e. 8 rows; lane s lands in slot s, so the lane
+// fetches the chunk that the swizzle maps to that slot. No VGPR staging.
+template <int ROWS, int INS>
+__device__ __forceinline__ void issue_stage(const uint16_t* base, const uint32_t (&off)[INS], int k0,
+                                            Vec16* stage, int wave, int first_ins, int n_ins)
+{
+#pragma unroll
+    for (int i = 0; i < INS; ++i) {
+        if (i < first_ins || i >= n_ins)
+            continue;
+        Vec16* dst = stage + (wave * (ROWS / 4) + i * 8) * kCH;
+        __builtin_amdgcn_global_load_lds((const void*)(base + off[i] + k0), (lds_void_t*)dst, 16, 0, 0);
+    }
+}
+
+// Scheduling pins: R LDS reads spread evenly between M MFMAs (mask 0x008 =
+// MFMA, 0x100 = LDS read, as the sched_group_barrier builtin defines them).
+template <int R, int M, int r>
+__device__ __forceinline__ void sched_spread()
+{
+    if constexpr (r < R) {
+        constexpr int n = (M * (r + 1)) / R - (M * r) / R;
+        if constexpr (n > 0)
+            __builtin_amdgcn_sched_group_barrier(0x008, n, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        sched_spread<R, M, r + 1>();
+    }
+}
+
+// MFMA work on one LDS stage (two 32-wide k steps). PARTIAL tiles (the last
+// m-tile of an expert) skip the A-fragment reads and MFMAs of 16-row groups
+// that hold no valid row. For full tiles the instruction order is pinned:
+// the 16 fragment reads of the first k step, then the 64 MFMAs of that step
+// with the 16 reads of the second step spread between them, then the second
+// step's 64 MFMAs, so LDS latency hides behind matrix work.
+template <int BM, int BN, int WM, int WN, bool PARTIAL>
+__device__ __forceinline__ void mfma_stage(const Vec16* As, const Vec16* Bs, int wm, int wn, int lane, int mi_lim,
+                                           floatx4 (&acc)[WM / 16][WN / 16])
+{
+    constexpr int MI = WM / 16, NI = WN / 16, KS = kBK / 32;
+    const int lr = lane & 15;
+    bf16x8 bfr[KS][NI], afr[KS][MI];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const int c = ks * 4 + (lane >> 4);
+        const int col = c ^ ((lr >> 1) & 7);  // swz() of a row whose low 4 bits are lr
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+            bfr[ks][j] = as_bf16x8(Bs[(wn * WN + j * 16 + lr) * kCH + col]);
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            if (PARTIAL && i >= mi_lim)
+                continue;
+            afr[ks][i] = as_bf16x8(As[(wm * WM + i * 16 + lr) * kCH + col]);
+        }
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            if (PARTIAL && i >= mi_lim)
+                continue;
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
+        }
+    }
+    if constexpr (!PARTIAL && KS == 2) {
+        constexpr int R = MI + NI;  // fragment reads per k step
+        constexpr int M = MI * NI;  // MFMAs per k step
+        __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+        sched_spread<R, M, 0>();
+        __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
+    }
+}
+
+__device__ __forceinline__ void wait_stage_loads()
+{
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+}
+
+// The K loop of one tile: stage kt+1 is loaded straight into the other LDS
+// buffer while stage kt is multiplied; one barrier per stage.
+template <int BM, int BN, int WM, int WN, int A_INS, int B_INS, bool PARTIAL>
+__device__ __forceinline__ void tile_k_loop(const uint16_t* A, const uint32_t (&aoff)[A_INS], const uint16_t* B,
+                                            const uint32_t (&boff)[B_INS], Vec16* sA0, Vec16* sA1, Vec16* sB0,
+                                            Vec16* sB1, int KT, int wv, int wm, int wn, int lane, int a_ins,
+                                            int mi_lim, floatx4 (&acc)[WM / 16][WN / 16])
+{
+    issue_stage<BM, A_INS>(A, aoff, 0, sA0, wv, 0, a_ins);
+    issue_stage<BN, B_INS>(B, boff, 0, sB0, wv, 0, B_INS);
+    for (int kt = 0; kt < KT; ++kt) {
+        const bool odd = kt & 1;
+        wait_stage_loads();  // stage kt has landed; the other buffer is free
+        if (kt + 1 < KT) {
+            issue_stage<BM, A_INS>(A, aoff, (kt + 1) * kBK, odd ? sA0 : sA1, wv, 0, a_ins);
+            issue_stage<BN, B_INS>(B, boff, (kt + 1) * kBK, odd ? sB0 : sB1, wv, 0, B_INS);
+        }
+        mfma_stage<BM, BN, WM, WN, PARTIAL>(odd ? sA1 : sA0, odd ? sB1 : sB0, wm, wn, lane, mi_lim, acc);
+    }
+}
+
 template <int BM, int BN, int WM, int WN, int GN, bool GATE_UP>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void grouped_gemm_kernel(GemmArgs g)
 {
     constexpr int WAVES_N = BN / WN;
     constexpr int MI = WM / 16, NI = WN / 16;
-    constexpr int A_LD = BM * kCH / kThreads;  // 16-byte chunks per thread per stage
-    constexpr int B_LD = BN * kCH / kThreads;
+    constexpr int A_INS = BM / 4 / 8;  // direct-load instructions per wave per stage
+    constexpr int B_INS = BN / 4 / 8;
     static_assert((BM / WM) * (BN / WN) == kThreads / kWave, "4 waves");
-    static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for one load per thread");
+    static_assert(A_INS >= 1 && B_INS >= 1, "tile too small");
     static_assert(!GATE_UP || (NI % 2 == 0 && WN % 32 == 0), "gate/up pairs per wave");
 
-    __shared__ Vec16 sA[2][BM * kCH];
-    __shared__ Vec16 sB[2][BN * kCH];
+    // Two stages, separate arrays so the compiler sees the buffers as distinct.
+    __shared__ Vec16 sA0[BM * kCH], sA1[BM * kCH];
+    __shared__ Vec16 sB0[BN * kCH], sB1[BN * kCH];
     __shared__ Tile s_tile;
 
     const int N = GATE_UP ? 2 * g.f : g.d;  // weight rows per expert
@@ -130,30 +239,32 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g)
     const int row0 = seg0 + mt * BM;
     const int rows = min(BM, g.offsets[e + 1] - row0);
 
-    const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int wm = wv / WAVES_N, wn = wv % WAVES_N;
 
-    // Global sources of this thread's chunks (A rows gathered through perm for
-    // gate/up; rows past the segment end are clamped to its last row and their
-    // results are never stored).
-    const uint16_t* ga[A_LD];
-    int la[A_LD];
+    // Per-lane source offsets (elements) of the rows this wave loads. A rows are
+    // gathered through perm for gate/up; rows past the segment end are clamped
+    // to its last row (loaded only when they share an instruction with valid
+    // rows; their results are never stored).
+    const uint16_t* A = (const uint16_t*)g.a;
+    const uint16_t* B = (const uint16_t*)g.b + ((int64_t)e * N + (int64_t)nt * BN) * K;
+    const int rsub = lane / 8, pch = lane % 8;
+    uint32_t aoff[A_INS], boff[B_INS];
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-        const int id = tid + i * kThreads, r = id / kCH, c = id % kCH;
+    for (int i = 0; i < A_INS; ++i) {
+        const int r = wv * (BM / 4) + i * 8 + rsub;
         const int p = row0 + min(r, rows - 1);
         const int src = GATE_UP ? g.perm[p] : p;
-        ga[i] = (const uint16_t*)g.a + (int64_t)src * K + c * 8;
-        la[i] = r * kCH + swz(r, c);
+        aoff[i] = (uint32_t)src * (uint32_t)K + (uint32_t)((pch ^ swz(r, 0)) * 8);
     }
-    const uint16_t* gb[B_LD];
-    int lb[B_LD];
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-        const int id = tid + i * kThreads, r = id / kCH, c = id % kCH;
-        gb[i] = (const uint16_t*)g.b + ((int64_t)e * N + (int64_t)nt * BN + r) * K + c * 8;
-        lb[i] = r * kCH + swz(r, c);
+    for (int i = 0; i < B_INS; ++i) {
+        const int r = wv * (BN / 4) + i * 8 + rsub;
+        boff[i] = (uint32_t)r * (uint32_t)K + (uint32_t)((pch ^ swz(r, 0)) * 8);
     }
+    // A instructions of this wave that hold at least one valid row.
+    const int a_ins = min(A_INS, max(0, (rows - wv * (BM / 4) + 7) / 8));
 
     floatx4 acc[MI][NI];
 #pragma unroll
@@ -162,56 +273,14 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g)
         for (int j = 0; j < NI; ++j)
             acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    Vec16 ra[A_LD], rb[B_LD];
-    auto gload = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < A_LD; ++i)
-            ra[i] = *(const Vec16*)(ga[i] + k0);
-#pragma unroll
-        for (int i = 0; i < B_LD; ++i)
-            rb[i] = *(const Vec16*)(gb[i] + k0);
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < A_LD; ++i)
-            sA[buf][la[i]] = ra[i];
-#pragma unroll
-        for (int i = 0; i < B_LD; ++i)
-            sB[buf][lb[i]] = rb[i];
-    };
-
     const int KT = K / kBK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < KT)
-            gload((kt + 1) * kBK);
-#pragma unroll
-        for (int ks = 0; ks < kBK / 32; ++ks) {
-            bf16x8 af[MI], bfg[NI];
-            const int c = ks * 4 + (lane >> 4);
-#pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                const int r = wm * WM + i * 16 + (lane & 15);
-                af[i] = as_bf16x8(sA[buf][r * kCH + swz(r, c)]);
-            }
-#pragma unroll
-            for (int j = 0; j < NI; ++j) {
-                const int r = wn * WN + j * 16 + (lane & 15);
-                bfg[j] = as_bf16x8(sB[buf][r * kCH + swz(r, c)]);
-            }
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int j = 0; j < NI; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfg[j], acc[i][j], 0, 0, 0);
-        }
-        if (kt + 1 < KT)
-            lstore(buf ^ 1);
-        __syncthreads();
-    }
+    if (rows == BM)
+        tile_k_loop<BM, BN, WM, WN, A_INS, B_INS, false>(A, aoff, B, boff, sA0, sA1, sB0, sB1, KT, wv, wm, wn,
+                                                         lane, A_INS, MI, acc);
+    else
+        tile_k_loop<BM, BN, WM, WN, A_INS, B_INS, true>(A, aoff, B, boff, sA0, sA1, sB0, sB1, KT, wv, wm, wn,
+                                                        lane, a_ins, min(MI, max(0, (rows - wm * WM + 15) / 16)),
+                                                        acc);
 
     // Epilogue. Accumulator layout: lane holds rows 4*(lane/16)+q, column lane%16.
     if constexpr (GATE_UP) {
@@ -277,25 +346,34 @@ __global__ void interleave_gate_up_kernel(const uint8_t* wg, const uint8_t* wu, 
 
 }  // namespace
 
-// Tile shapes of the first kernel generation: 128x128 tiles, 4 waves of 64x64.
-constexpr int kBM = 128, kBN = 128, kWM = 64, kWN = 64, kGN = 4;
+// Tile shapes: 256x256 output tiles, 4 waves of 128x128 (256 fp32 accumulators
+// per lane, held in AGPRs), 2 x 64 KiB LDS stages: one workgroup per CU. When
+// the weight-row count is not a multiple of 256, 256x128 tiles (waves of
+// 128x64) are used instead.
+constexpr int kBM = 256, kGN = 8;
+
+template <bool GATE_UP>
+hipError_t launch_grouped(const GemmArgs& a, hipStream_t s)
+{
+    const int N = GATE_UP ? 2 * a.f : a.d;
+    const int mt = m_tile_bound<kBM>(a.A_max, a.E);
+    if (N % 256 == 0)
+        hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 256, 128, 128, kGN, GATE_UP>), dim3(mt * (N / 256)),
+                           dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 128, 128, 64, kGN, GATE_UP>), dim3(mt * (N / 128)),
+                           dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t s)
 {
-    const int NT = 2 * a.f / kBN;
-    const int grid = m_tile_bound<kBM>(a.A_max, a.E) * NT;
-    hipLaunchKernelGGL((grouped_gemm_kernel<kBM, kBN, kWM, kWN, kGN, true>), dim3(grid), dim3(kThreads), 0,
-                       s, a);
-    return hipGetLastError();
+    return launch_grouped<true>(a, s);
 }
 
 hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t s)
 {
-    const int NT = a.d / kBN;
-    const int grid = m_tile_bound<kBM>(a.A_max, a.E) * NT;
-    hipLaunchKernelGGL((grouped_gemm_kernel<kBM, kBN, kWM, kWN, kGN, false>), dim3(grid), dim3(kThreads), 0,
-                       s, a);
-    return hipGetLastError();
+    return launch_grouped<false>(a, s);
 }
 
 hipError_t launch_interleave_gate_up(const void* wg, const void* wu, void* wgu, int E, int f, int d,

@@ -47,8 +47,24 @@ def parse():
     ap.add_argument("--workload", default="mixtral", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
-                    help="tokens of the oracle sample (0 = sized to ~20 s of CPU work)")
+                    help="tokens of the oracle sample (0 = sized to ~15 s of CPU work)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (to scale HBM counters) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int):
+    """A plain device-to-device copy of known size: its FETCH_SIZE / WRITE_SIZE
+    readings give the factor between those counters and bytes moved."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 3}), flush=True)
 
 
 def to_dev(a):
@@ -105,6 +121,9 @@ def main():
     import synth
     import sparse_moe_gemm_amd as cm
 
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     cfg = synth.CONFIGS[args.workload]
     t_gen = time.perf_counter()
     inp = synth.make_inputs(cfg)

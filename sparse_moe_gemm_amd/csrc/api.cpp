@@ -9,11 +9,12 @@
 // enqueues kernels.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
 #include <mutex>
 #include <new>
 #include <unordered_set>
 
-#include "../../include/colibri_moe.h"
+#include "colibri_moe.h"
 #include "common.hpp"
 
 using namespace cmoe;
@@ -39,8 +40,8 @@ struct colibri_moe {
     // weights (library copies, repacked)
     void* w_rt;   // [E][d]
     float* b_r;   // [E]
-    void* w_gu;   // [E][2f][d], gate/up interleaved by 16 rows
-    void* w_d;    // [E][d][f]
+    void* w_gu;   // [E][2f][d], gate/up interleaved by 32 rows (bf16: blocked MFMA layout)
+    void* w_d;    // [E][d][f] (bf16: blocked MFMA layout)
     // workspace, sized for max_tokens
     float* topw;
     int32_t* ids;
@@ -53,6 +54,8 @@ struct colibri_moe {
     float* Ys;    // [A][d] fp32
     bool timing;
     hipEvent_t ev[kStages + 1];
+    int group_n;    // tile-order knobs of the grouped GEMMs
+    int xcd_remap;
 };
 
 namespace {
@@ -64,6 +67,15 @@ bool is_live(colibri_moe* h)
 {
     std::lock_guard<std::mutex> lk(g_mu);
     return g_live.count(h) != 0;
+}
+
+int env_int(const char* name, int dflt, int lo, int hi)
+{
+    const char* v = std::getenv(name);
+    if (!v || !*v)
+        return dflt;
+    const long x = std::strtol(v, nullptr, 10);
+    return (x < lo || x > hi) ? dflt : (int)x;
 }
 
 bool aligned16(const void* p)
@@ -100,6 +112,11 @@ colibri_moe_status_t validate_config(const colibri_moe_config_t* c)
     if (c->d_model % 128 != 0 || c->d_ff % 64 != 0)
         return COLIBRI_MOE_ERR_UNSUPPORTED;
     if (c->max_tokens > kMaxTokensLimit)
+        return COLIBRI_MOE_ERR_UNSUPPORTED;
+    // GEMM source offsets are 32-bit element offsets.
+    const int64_t lim = (int64_t)1 << 31;
+    if ((int64_t)c->max_tokens * c->d_model >= lim || (int64_t)c->max_tokens * c->top_k * c->d_ff >= lim ||
+        (int64_t)2 * c->d_ff * c->d_model >= lim)
         return COLIBRI_MOE_ERR_UNSUPPORTED;
     return COLIBRI_MOE_OK;
 }
@@ -170,8 +187,14 @@ colibri_moe_status_t init_impl(colibri_moe* h, const colibri_moe_weights_t* w)
         CMOE_HIP(hipMemcpyAsync(h->b_r, w->b_router, E * sizeof(float), hipMemcpyDeviceToDevice, s));
     else
         CMOE_HIP(hipMemsetAsync(h->b_r, 0, E * sizeof(float), s));
-    CMOE_HIP(launch_interleave_gate_up(w->w_gate, w->w_up, h->w_gu, (int)E, (int)f, (int)d, (int)es, s));
-    CMOE_HIP(hipMemcpyAsync(h->w_d, w->w_down, E * d * f * es, hipMemcpyDeviceToDevice, s));
+    if (c.dtype == COLIBRI_MOE_BF16) {
+        // blocked MFMA operand layout (gate/up interleaved by 32 rows)
+        CMOE_HIP(launch_pack_blocked(w->w_gate, w->w_up, h->w_gu, (int)E, (int)(2 * f), (int)d, 1, s));
+        CMOE_HIP(launch_pack_blocked(w->w_down, nullptr, h->w_d, (int)E, (int)d, (int)f, 0, s));
+    } else {
+        CMOE_HIP(launch_interleave_gate_up(w->w_gate, w->w_up, h->w_gu, (int)E, (int)f, (int)d, (int)es, s));
+        CMOE_HIP(hipMemcpyAsync(h->w_d, w->w_down, E * d * f * es, hipMemcpyDeviceToDevice, s));
+    }
     if (h->timing)
         for (int i = 0; i <= kStages; ++i)
             CMOE_HIP(hipEventCreate(&h->ev[i]));
@@ -206,6 +229,10 @@ colibri_moe_status_t colibri_moe_init(colibri_moe_t** out, const colibri_moe_con
     h->stream = (hipStream_t)hip_stream;
     h->esize = cfg->dtype == COLIBRI_MOE_BF16 ? 2 : 4;
     h->timing = (cfg->flags & COLIBRI_MOE_FLAG_STAGE_TIMING) != 0;
+    // Tile-order knobs of the grouped GEMMs (tuning only; results do not
+    // depend on them): CMOE_GROUP_N n-tiles per group, CMOE_XCD_REMAP 0/1.
+    h->group_n = env_int("CMOE_GROUP_N", 8, 1, 1 << 20);
+    h->xcd_remap = env_int("CMOE_XCD_REMAP", 1, 0, 1);
     if (hipGetDevice(&h->device) != hipSuccess) {
         release(h);
         return COLIBRI_MOE_ERR_HIP;
@@ -271,13 +298,13 @@ colibri_moe_status_t colibri_moe_forward(colibri_moe_t* h, const void* x, int32_
         CMOE_HIP(hipEventRecord(h->ev[2], s));
 
     GemmArgs gu{x, h->w_gu, h->H, offsets, perm, perm_slot, T * c.top_k, c.n_experts, c.top_k, c.d_model,
-                c.d_ff};
+                c.d_ff, h->group_n, h->xcd_remap};
     CMOE_HIP(bf ? launch_gate_up_bf16(gu, s) : launch_gate_up_f32(gu, s));
     if (tm)
         CMOE_HIP(hipEventRecord(h->ev[3], s));
 
     GemmArgs dn{h->H, h->w_d, h->Ys, offsets, perm, perm_slot, T * c.top_k, c.n_experts, c.top_k, c.d_model,
-                c.d_ff};
+                c.d_ff, h->group_n, h->xcd_remap};
     CMOE_HIP(bf ? launch_down_bf16(dn, s) : launch_down_f32(dn, s));
     if (tm)
         CMOE_HIP(hipEventRecord(h->ev[4], s));

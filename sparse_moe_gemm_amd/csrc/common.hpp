@@ -74,6 +74,7 @@ struct GemmArgs {
     //   [E][2f][d]; out = H [A][f].
     // down:    A rows are H[p] ([A][f]);        B = down weights [E][d][f];
     //   out = Ys [A][d] fp32, row p written to assignment row perm[p]*k+perm_slot[p].
+    // bf16 weights are in the blocked MFMA layout, fp32 weights row-major.
     const void* a;
     const void* b;
     void* out;
@@ -82,6 +83,8 @@ struct GemmArgs {
     const int32_t* perm_slot; // [A]
     int A_max;                // T*k of this call (bounds the tile grid)
     int E, k, d, f;
+    int group_n;              // n-tiles per tile group (tile order), >= 1
+    int xcd_remap;            // 1: give each XCD a contiguous range of tiles
 };
 hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t s);
 hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t s);
@@ -101,5 +104,9 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_transpose_router(const void* w_r, void* w_rt, int d, int E, int esize, hipStream_t s);
 hipError_t launch_interleave_gate_up(const void* wg, const void* wu, void* wgu, int E, int f, int d,
                                      int esize, hipStream_t s);
+// bf16 weights in the blocked MFMA operand layout (see gemm_bf16.hip); with
+// gate_up, w0/w1 are the gate/up matrices [E][N/2][K] and rows are interleaved.
+hipError_t launch_pack_blocked(const void* w0, const void* w1, void* out, int E, int N, int K, int gate_up,
+                               hipStream_t s);
 
 }  // namespace cmoe

@@ -5,7 +5,7 @@
 // vector rate, so these use plain FMA with LDS tiles: 64x64 output tiles, 256
 // threads, 4x4 outputs per thread, K staged 16 at a time. Tiles are mapped as
 // in the bf16 kernels (derived on the device from offsets[], empty experts get
-// none); the gate/up weights use the same 16-row gate/up interleave.
+// none); the gate/up weights use the same 32-row gate/up interleave.
 #include "common.hpp"
 
 namespace cmoe {
@@ -69,9 +69,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_f32_kernel(GemmArgs g)
             sA[lk][lr] = A[(int64_t)src * K + k0 + lk];
             const int c = col0 + lr;  // output column
             if (GATE_UP) {
-                const int64_t grow = (int64_t)e * 2 * g.f + (c / 16) * 32 + (c % 16);
+                const int64_t grow = (int64_t)e * 2 * g.f + (c / 32) * 64 + (c % 32);
                 sG[lk][lr] = B[grow * K + k0 + lk];
-                sU[lk][lr] = B[(grow + 16) * K + k0 + lk];
+                sU[lk][lr] = B[(grow + 32) * K + k0 + lk];
             } else {
                 sG[lk][lr] = B[((int64_t)e * g.d + c) * K + k0 + lk];
             }

@@ -38,15 +38,18 @@ namespace cmoe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBK = 64;            // k per LDS stage
-constexpr int kCH = kBK / 8;       // 16-byte chunks per row per stage
+constexpr int kBK = 32;            // k per LDS stage
+constexpr int kCH = kBK / 8;       // 16-byte chunks per A row per stage
+constexpr int kNBUF = 4;           // LDS ring of stages
+constexpr int kDIST = 3;           // stages in flight ahead of the one being multiplied
 constexpr int kXCD = 8;
 
-// XOR swizzle of the 16-byte chunk index inside an LDS row, so that the 16
-// lanes reading one column of chunks of 16 consecutive rows hit distinct banks.
+// XOR swizzle of the 16-byte chunk index inside an A row of the LDS stage:
+// the 16 lanes that read one chunk column of 16 consecutive rows (rows are 64 B
+// apart) land in 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int swz(int row, int chunk)
 {
-    return chunk ^ ((row >> 1) & 7);
+    return chunk ^ ((row >> 2) & 3);
 }
 
 struct Tile {
@@ -109,39 +112,52 @@ __device__ void find_tile(const int32_t* offsets, int E, int NT, int GN, int rem
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// One K-stage of A lives in LDS as rows of 8 16-byte chunks (64 bf16 of K),
-// chunk index XOR-swizzled per row. Stages are filled with direct global->LDS
-// loads (global_load_lds_dwordx4): one instruction moves 64 lanes x 16 B into
-// 1 KiB of LDS, i.e. 8 rows; lane s lands in slot s, so the lane fetches the
-// chunk that the swizzle maps to that slot. No VGPR staging.
-template <int INS>
-__device__ __forceinline__ void issue_a_stage(const uint16_t* base, const uint32_t (&off)[INS], int k0,
-                                              Vec16* stage, int n_ins)
+// LDS stage layout (one 32-wide K stage of a 256 x 256 tile):
+//   A: BM rows x 4 chunks of 16 B (8 bf16), chunk index swizzled per row;
+//   B: BN/32 x 2 blocks of 1 KiB, each a 32-row x 16-k weight block in MFMA
+//      operand order (lane l's 8 values at l*16 B), copied whole from the
+//      blocked weight layout.
+// Both are filled with direct global->LDS loads (global_load_lds_dwordx4: 64
+// lanes x 16 B into 1 KiB of LDS, lane s into slot s); no VGPR staging.
+template <int BM, int BN>
+struct Stage {
+    Vec16 a[BM * kCH];
+    Vec16 b[(BN / 32) * 2 * 64];
+};
+
+// One direct global->LDS load: 64 lanes x 16 B from per-lane addresses into
+// the 1 KiB of LDS at the wave-uniform address lds (through M0). Written as
+// inline assembly on purpose: the ordering of these LDS writes against the
+// LDS reads of other stages is handled explicitly (vmcnt wait + barrier at
+// each stage), and an opaque instruction keeps the compiler from inserting
+// its own conservative full waits before every LDS read, which would drain the
+// stages in flight. Nothing else in these kernels uses M0.
+__device__ __forceinline__ void dma16(const void* gptr, const void* lds)
+{
+    const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_void_t*)lds);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(a)
+                 : "memory");
+}
+
+// This wave's share of one stage's loads: A_INS instructions of 16 A rows each
+// and B_INS whole weight blocks.
+template <int BM, int BN, int A_INS, int B_INS>
+__device__ __forceinline__ void issue_stage(const uint16_t* A, const uint32_t (&aoff)[A_INS], const Vec16* bsrc,
+                                            int KB, int kt, Stage<BM, BN>* st, int wv)
 {
 #pragma unroll
-    for (int i = 0; i < INS; ++i) {
-        if (i >= n_ins)
-            continue;
-        Vec16* dst = stage + i * 8 * kCH;
-        __builtin_amdgcn_global_load_lds((const void*)(base + off[i] + k0), (lds_void_t*)dst, 16, 0, 0);
+    for (int i = 0; i < A_INS; ++i)
+        dma16(A + aoff[i] + kt * kBK, st->a + (wv * A_INS + i) * 64);
+#pragma unroll
+    for (int i = 0; i < B_INS; ++i) {
+        const int blk = wv * B_INS + i;  // = row block * 2 + k block within the stage
+        dma16(bsrc + ((int64_t)(blk >> 1) * KB + kt * 2 + (blk & 1)) * 64, st->b + blk * 64);
     }
 }
 
-// B fragments of one stage: NI 32-row blocks x KS k-steps, 16 B per lane each,
-// from the blocked weight layout (bw points at this lane's slot of the wave's
-// first block row; kb0 = first k-block of the stage; KB = k-blocks per row).
-template <int NI, int KS>
-__device__ __forceinline__ void load_b_stage(const Vec16* bw, int kb0, int KB, Vec16 (&bq)[KS][NI])
-{
-#pragma unroll
-    for (int j = 0; j < NI; ++j)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            bq[ks][j] = bw[((int64_t)j * KB + kb0 + ks) * 64];
-}
-
 // Scheduling pins: R LDS reads spread evenly between M MFMAs (mask 0x008 =
-// MFMA, 0x100 = LDS read, as the sched_group_barrier builtin defines them).
+// MFMA, 0x100 = LDS read, 0x010 = global load, as the sched_group_barrier
+// builtin defines them).
 template <int R, int M, int r>
 __device__ __forceinline__ void sched_spread()
 {
@@ -154,41 +170,31 @@ __device__ __forceinline__ void sched_spread()
     }
 }
 
-// One k step: its M MFMAs, with the R reads of the next step spread over the
-// first half of them (so they land before the next step starts).
-template <int N, int R, int M>
-__device__ __forceinline__ void sched_repeat()
-{
-    if constexpr (N > 0) {
-        sched_spread<R, M / 2, 0>();
-        __builtin_amdgcn_sched_group_barrier(0x008, M - M / 2, 0);
-        sched_repeat<N - 1, R, M>();
-    }
-}
-
-// MFMA work on one stage (four 16-wide k steps of 32x32x16 MFMAs): A fragments
-// from LDS, B fragments from registers. PARTIAL tiles (the last m-tile of an
-// expert) skip the A reads and MFMAs of 32-row groups that hold no valid row.
-// For full tiles the instruction order is pinned: the NLOAD global loads of
-// the next stage issued just before (when in the same block), the A reads of
-// the first k step, then each k step's MFMAs with the next step's reads spread
-// between them, so memory and LDS latency hide behind matrix work.
-template <int WM, int WN, bool PARTIAL, int NLOAD>
-__device__ __forceinline__ void mfma_stage(const Vec16* As, const Vec16 (&bq)[kBK / 16][WN / 32], int wm,
-                                           int lane, int mi_lim, floatx16 (&acc)[WM / 32][WN / 32])
+// MFMA work on one stage (two 16-wide k steps of 32x32x16 MFMAs). PARTIAL
+// tiles (the last m-tile of an expert) skip the A reads and MFMAs of 32-row
+// groups that hold no valid row. For full tiles the order is pinned: the
+// NLOAD global loads issued just before, the first k step's fragment reads,
+// its MFMAs with the second step's reads spread over their first half, then
+// the second step's MFMAs.
+template <int BM, int BN, int WM, int WN, bool PARTIAL, int NLOAD>
+__device__ __forceinline__ void mfma_stage(const Stage<BM, BN>* st, int wm, int wn, int lane, int mi_lim,
+                                           floatx16 (&acc)[WM / 32][WN / 32])
 {
     constexpr int MI = WM / 32, NI = WN / 32, KS = kBK / 16;
     const int lr = lane & 31;
-    bf16x8 afr[KS][MI];
+    bf16x8 afr[KS][MI], bfr[KS][NI];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         const int c = ks * 2 + (lane >> 5);
-        const int col = c ^ ((lr >> 1) & 7);  // swz() of a row whose low 5 bits are lr
+        const int col = c ^ ((lr >> 2) & 3);  // swz() of a row whose low 5 bits are lr
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+            bfr[ks][j] = as_bf16x8(st->b[((wn * NI + j) * 2 + ks) * 64 + lane]);
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
             if (PARTIAL && i >= mi_lim)
                 continue;
-            afr[ks][i] = as_bf16x8(As[(wm * WM + i * 32 + lr) * kCH + col]);
+            afr[ks][i] = as_bf16x8(st->a[(wm * WM + i * 32 + lr) * kCH + col]);
         }
     }
 #pragma unroll
@@ -199,76 +205,74 @@ __device__ __forceinline__ void mfma_stage(const Vec16* As, const Vec16 (&bq)[kB
                 continue;
 #pragma unroll
             for (int j = 0; j < NI; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[ks][i], as_bf16x8(bq[ks][j]), acc[i][j],
-                                                                   0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
         }
     }
     if constexpr (!PARTIAL) {
-        constexpr int R = MI;       // A reads per k step
+        constexpr int R = MI + NI;  // fragment reads per k step
         constexpr int M = MI * NI;  // MFMAs per k step
-        // the next stage's loads (if issued in this block) go first
         if constexpr (NLOAD > 0)
             __builtin_amdgcn_sched_group_barrier(0x010, NLOAD, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
-        sched_repeat<KS - 1, R, M>();
+        sched_spread<R, M / 2, 0>();
+        __builtin_amdgcn_sched_group_barrier(0x008, M - M / 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
     }
 }
 
-// Wait until this wave's loads of the current stage have landed, then
-// barrier. The scheduling barrier keeps the scheduler from moving the MFMAs
-// of the previous stage across the wait.
-__device__ __forceinline__ void wait_stage_loads()
+// Wait until at most N of this wave's loads are still in flight (the N most
+// recently issued), then barrier: the stage about to be multiplied has landed
+// for every wave, and every wave is done with the stage multiplied before.
+// The scheduling barrier keeps MFMAs of the previous stage from moving across.
+template <int N>
+__device__ __forceinline__ void wait_loads_barrier()
 {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
     __syncthreads();
 }
 
-// The K loop of one tile: stage kt+1 (A into the other LDS buffer, B into the
-// other register set) is loaded while stage kt is multiplied; one barrier per
-// stage. Unrolled by two so both register sets have fixed names.
-template <int WM, int WN, int A_INS, bool PARTIAL>
-__device__ __forceinline__ void tile_k_loop(const uint16_t* A, const uint32_t (&aoff)[A_INS], const Vec16* bw,
-                                            int KB, Vec16* sA0, Vec16* sA1, Vec16* sA0w, Vec16* sA1w, int KT,
-                                            int wm, int lane, int a_ins, int mi_lim,
-                                            floatx16 (&acc)[WM / 32][WN / 32])
+// The K loop of one tile: a ring of kNBUF LDS stages with kDIST stages in
+// flight ahead of the one being multiplied, one barrier per stage. (A single
+// copy of the MFMA code in the loop keeps the accumulators in place.)
+template <int BM, int BN, int WM, int WN, int A_INS, int B_INS, bool PARTIAL>
+__device__ __forceinline__ void tile_k_loop(const uint16_t* A, const uint32_t (&aoff)[A_INS], const Vec16* bsrc,
+                                            int KB, int KT, Stage<BM, BN>* ring, int wv, int wm, int wn, int lane,
+                                            int mi_lim, floatx16 (&acc)[WM / 32][WN / 32])
 {
-    constexpr int NI = WN / 32, KS = kBK / 16;
-    Vec16 bq0[KS][NI], bq1[KS][NI];
-    issue_a_stage<A_INS>(A, aoff, 0, sA0w, a_ins);
-    load_b_stage<NI, KS>(bw, 0, KB, bq0);
-    int kt = 0;
-    for (; kt + 2 <= KT; kt += 2) {
-        wait_stage_loads();  // stage kt landed (LDS buffer 0, registers bq0)
-        issue_a_stage<A_INS>(A, aoff, (kt + 1) * kBK, sA1w, a_ins);
-        load_b_stage<NI, KS>(bw, (kt + 1) * KS, KB, bq1);
-        mfma_stage<WM, WN, PARTIAL, A_INS + NI * KS>(sA0, bq0, wm, lane, mi_lim, acc);
-        wait_stage_loads();  // stage kt+1 landed (LDS buffer 1, registers bq1)
-        if (kt + 2 < KT) {
-            issue_a_stage<A_INS>(A, aoff, (kt + 2) * kBK, sA0w, a_ins);
-            load_b_stage<NI, KS>(bw, (kt + 2) * KS, KB, bq0);
-        }
-        mfma_stage<WM, WN, PARTIAL, 0>(sA1, bq1, wm, lane, mi_lim, acc);
-    }
-    if (kt < KT) {  // odd number of stages: the last one is in buffer 0
-        wait_stage_loads();
-        mfma_stage<WM, WN, PARTIAL, 0>(sA0, bq0, wm, lane, mi_lim, acc);
+    constexpr int PER = A_INS + B_INS;  // loads per wave per stage
+    static_assert(kDIST == 3 && kNBUF >= kDIST + 1, "ring layout");
+#pragma unroll
+    for (int s = 0; s < kDIST; ++s)
+        if (s < KT)
+            issue_stage<BM, BN, A_INS, B_INS>(A, aoff, bsrc, KB, s, &ring[s], wv);
+    for (int kt = 0; kt < KT; ++kt) {
+        const int ahead = KT - 1 - kt;  // stages after this one, already issued up to kDIST - 1
+        if (ahead >= 2)
+            wait_loads_barrier<2 * PER>();
+        else if (ahead == 1)
+            wait_loads_barrier<PER>();
+        else
+            wait_loads_barrier<0>();
+        if (kt + kDIST < KT)
+            issue_stage<BM, BN, A_INS, B_INS>(A, aoff, bsrc, KB, kt + kDIST, &ring[(kt + kDIST) % kNBUF], wv);
+        mfma_stage<BM, BN, WM, WN, PARTIAL, 0>(&ring[kt % kNBUF], wm, wn, lane, mi_lim, acc);
     }
 }
 
 template <int BM, int BN, int WM, int WN, bool GATE_UP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void grouped_gemm_kernel(GemmArgs g)
 {
-    constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+    constexpr int WAVES_N = BN / WN;
     constexpr int MI = WM / 32, NI = WN / 32;
-    constexpr int A_INS = BM / 4 / 8;  // direct-load instructions per wave per stage
-    static_assert(WAVES_M * WAVES_N == kThreads / kWave, "4 waves");
-    static_assert(A_INS >= 1, "tile too small");
+    constexpr int A_INS = BM * kCH / 64 / 4;      // A direct-load instructions per wave per stage
+    constexpr int B_INS = (BN / 32) * 2 / 4;      // weight blocks per wave per stage
+    static_assert((BM / WM) * WAVES_N == kThreads / kWave, "4 waves");
+    static_assert(A_INS * 4 * 16 == BM && B_INS * 4 == (BN / 32) * 2, "stage split over 4 waves");
     static_assert(!GATE_UP || (NI % 2 == 0 && WN % 64 == 0), "gate/up pairs per wave");
 
-    // Two A stages, separate arrays so the compiler sees the buffers as distinct.
-    __shared__ Vec16 sA0[BM * kCH], sA1[BM * kCH];
+    __shared__ Stage<BM, BN> ring[kNBUF];
     __shared__ Tile s_tile;
 
     const int N = GATE_UP ? 2 * g.f : g.d;  // weight rows per expert
@@ -290,27 +294,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int wm = wv / WAVES_N, wn = wv % WAVES_N;
 
-    // A: per-lane source offsets (elements) of the 8-row groups this wave
-    // loads into LDS. Rows are gathered through perm for gate/up; rows past the
-    // segment end are clamped to its last row (loaded only when they share an
-    // instruction with valid rows; their results are never stored).
+    // A: per-lane source offsets (elements) of this wave's 16-row groups. Rows
+    // are gathered through perm for gate/up; rows past the segment end are
+    // clamped to its last row (their results are never stored).
     const uint16_t* A = (const uint16_t*)g.a;
-    const int rsub = lane / 8, pch = lane % 8;
     uint32_t aoff[A_INS];
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
-        const int r = wv * (BM / 4) + i * 8 + rsub;
+        const int r = (wv * A_INS + i) * 16 + lane / 4;  // slot lane of this instruction
         const int p = row0 + min(r, rows - 1);
         const int src = GATE_UP ? g.perm[p] : p;
-        aoff[i] = (uint32_t)src * (uint32_t)K + (uint32_t)((pch ^ swz(r, 0)) * 8);
+        aoff[i] = (uint32_t)src * (uint32_t)K + (uint32_t)(swz(r, lane % 4) * 8);
     }
-    const int a_ins = min(A_INS, max(0, (rows - wv * (BM / 4) + 7) / 8));
-    Vec16* sA0w = sA0 + wv * (BM / 4) * kCH;  // this wave's slice of each stage
-    Vec16* sA1w = sA1 + wv * (BM / 4) * kCH;
-
-    // B: this lane's slot in the first 32-row block of the wave's columns.
-    const int nb0 = (nt * BN + wn * WN) / 32;
-    const Vec16* bw = (const Vec16*)g.b + ((int64_t)e * (N / 32) + nb0) * KB * 64 + lane;
+    // B: this lane's slot in the tile's first weight block.
+    const Vec16* bsrc = (const Vec16*)g.b + ((int64_t)e * (N / 32) + (int64_t)nt * (BN / 32)) * KB * 64 + lane;
 
     floatx16 acc[MI][NI];
 #pragma unroll
@@ -323,10 +320,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
     const int KT = K / kBK;
     if (rows == BM)
-        tile_k_loop<WM, WN, A_INS, false>(A, aoff, bw, KB, sA0, sA1, sA0w, sA1w, KT, wm, lane, A_INS, MI, acc);
+        tile_k_loop<BM, BN, WM, WN, A_INS, B_INS, false>(A, aoff, bsrc, KB, KT, ring, wv, wm, wn, lane, MI, acc);
     else
-        tile_k_loop<WM, WN, A_INS, true>(A, aoff, bw, KB, sA0, sA1, sA0w, sA1w, KT, wm, lane, a_ins,
-                                         min(MI, max(0, (rows - wm * WM + 31) / 32)), acc);
+        tile_k_loop<BM, BN, WM, WN, A_INS, B_INS, true>(A, aoff, bsrc, KB, KT, ring, wv, wm, wn, lane,
+                                                        min(MI, max(0, (rows - wm * WM + 31) / 32)), acc);
 
     // Epilogue. 32x32 accumulator layout: lane holds column lane%32 and, for
     // q = 0..15, row 8*(q/4) + 4*(lane/32) + q%4.

@@ -51,8 +51,10 @@ extern "C" {
 typedef enum {
     COLIBRI_MOE_OK = 0,
     COLIBRI_MOE_ERR_INVALID_ARG = 1,  /* null where required, T < 0 or > max_tokens, k < 1 or > E, bad dtype */
-    COLIBRI_MOE_ERR_UNSUPPORTED = 2,  /* d_model not a multiple of 128, d_ff not a multiple of 64,
-                                         E > 256, k > 8, max_tokens > 2^24 */
+    COLIBRI_MOE_ERR_UNSUPPORTED = 2,  /* d_model not a multiple of 128, d_ff not a multiple of 128
+                                         (bf16) or 64 (f32), E > 256, k > 8, max_tokens > 2^24,
+                                         or max_tokens*k*d_ff, max_tokens*d_model or
+                                         2*d_ff*d_model reaching 2^31 */
     COLIBRI_MOE_ERR_ALIGNMENT = 3,    /* a tensor pointer not 16-byte aligned */
     COLIBRI_MOE_ERR_OUT_OF_MEMORY = 4,/* init could not allocate its memory */
     COLIBRI_MOE_ERR_HIP = 5           /* a HIP launch, copy or sync failed */

@@ -109,7 +109,9 @@ colibri_moe_status_t validate_config(const colibri_moe_config_t* c)
         return COLIBRI_MOE_ERR_INVALID_ARG;
     if (c->n_experts > kMaxExperts || c->top_k > kMaxTopK)
         return COLIBRI_MOE_ERR_UNSUPPORTED;
-    if (c->d_model % 128 != 0 || c->d_ff % 64 != 0)
+    // bf16 GEMMs stage K in 32-wide steps, four per loop trip (K % 128); the
+    // fp32 GEMMs use 64-wide tiles.
+    if (c->d_model % 128 != 0 || c->d_ff % (c->dtype == COLIBRI_MOE_BF16 ? 128 : 64) != 0)
         return COLIBRI_MOE_ERR_UNSUPPORTED;
     if (c->max_tokens > kMaxTokensLimit)
         return COLIBRI_MOE_ERR_UNSUPPORTED;
@@ -231,8 +233,8 @@ colibri_moe_status_t colibri_moe_init(colibri_moe_t** out, const colibri_moe_con
     h->timing = (cfg->flags & COLIBRI_MOE_FLAG_STAGE_TIMING) != 0;
     // Tile-order knobs of the grouped GEMMs (tuning only; results do not
     // depend on them): CMOE_GROUP_N n-tiles per group, CMOE_XCD_REMAP 0/1.
-    h->group_n = env_int("CMOE_GROUP_N", 8, 1, 1 << 20);
-    h->xcd_remap = env_int("CMOE_XCD_REMAP", 1, 0, 1);
+    h->group_n = env_int("CMOE_GROUP_N", 16, 1, 1 << 20);
+    h->xcd_remap = env_int("CMOE_XCD_REMAP", 0, 0, 1);
     if (hipGetDevice(&h->device) != hipSuccess) {
         release(h);
         return COLIBRI_MOE_ERR_HIP;

@@ -40,8 +40,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBK = 32;            // k per LDS stage
 constexpr int kCH = kBK / 8;       // 16-byte chunks per A row per stage
-constexpr int kNBUF = 4;           // LDS ring of stages
-constexpr int kDIST = 3;           // stages in flight ahead of the one being multiplied
 constexpr int kXCD = 8;
 
 // XOR swizzle of the 16-byte chunk index inside an A row of the LDS stage:
@@ -127,11 +125,11 @@ struct Stage {
 
 // One direct global->LDS load: 64 lanes x 16 B from per-lane addresses into
 // the 1 KiB of LDS at the wave-uniform address lds (through M0). Written as
-// inline assembly on purpose: the ordering of these LDS writes against the
-// LDS reads of other stages is handled explicitly (vmcnt wait + barrier at
-// each stage), and an opaque instruction keeps the compiler from inserting
-// its own conservative full waits before every LDS read, which would drain the
-// stages in flight. Nothing else in these kernels uses M0.
+// inline assembly on purpose: the ordering of these LDS writes against the LDS
+// reads of other stages is handled explicitly (a vmcnt wait and a barrier per
+// stage), and an opaque instruction keeps the compiler from adding its own
+// full waits before LDS reads, which would drain the stages in flight.
+// Nothing else in these kernels uses M0.
 __device__ __forceinline__ void dma16(const void* gptr, const void* lds)
 {
     const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_void_t*)lds);
@@ -139,126 +137,156 @@ __device__ __forceinline__ void dma16(const void* gptr, const void* lds)
                  : "memory");
 }
 
-// This wave's share of one stage's loads: A_INS instructions of 16 A rows each
-// and B_INS whole weight blocks.
+// This wave's share of one stage's loads: A_INS instructions of 16 A rows each,
+// then B_INS whole weight blocks; instruction q is issued by issue(q, ...).
 template <int BM, int BN, int A_INS, int B_INS>
-__device__ __forceinline__ void issue_stage(const uint16_t* A, const uint32_t (&aoff)[A_INS], const Vec16* bsrc,
-                                            int KB, int kt, Stage<BM, BN>* st, int wv)
-{
-#pragma unroll
-    for (int i = 0; i < A_INS; ++i)
-        dma16(A + aoff[i] + kt * kBK, st->a + (wv * A_INS + i) * 64);
-#pragma unroll
-    for (int i = 0; i < B_INS; ++i) {
-        const int blk = wv * B_INS + i;  // = row block * 2 + k block within the stage
-        dma16(bsrc + ((int64_t)(blk >> 1) * KB + kt * 2 + (blk & 1)) * 64, st->b + blk * 64);
-    }
-}
+struct StageLoader {
+    const uint16_t* A;
+    const uint32_t* aoff;
+    const Vec16* bsrc;
+    int KB, wv;
 
-// Scheduling pins: R LDS reads spread evenly between M MFMAs (mask 0x008 =
-// MFMA, 0x100 = LDS read, 0x010 = global load, as the sched_group_barrier
-// builtin defines them).
-template <int R, int M, int r>
-__device__ __forceinline__ void sched_spread()
-{
-    if constexpr (r < R) {
-        constexpr int n = (M * (r + 1)) / R - (M * r) / R;
-        if constexpr (n > 0)
-            __builtin_amdgcn_sched_group_barrier(0x008, n, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        sched_spread<R, M, r + 1>();
+    __device__ __forceinline__ void issue(int q, int kt, Stage<BM, BN>* st) const
+    {
+        if (q < A_INS) {
+            dma16(A + aoff[q] + kt * kBK, st->a + (wv * A_INS + q) * 64);
+        } else {
+            const int blk = wv * B_INS + (q - A_INS);  // = row block * 2 + k block within the stage
+            dma16(bsrc + ((int64_t)(blk >> 1) * KB + kt * 2 + (blk & 1)) * 64, st->b + blk * 64);
+        }
     }
-}
+    __device__ __forceinline__ void issue_all(int kt, Stage<BM, BN>* st) const
+    {
+#pragma unroll
+        for (int q = 0; q < A_INS + B_INS; ++q)
+            issue(q, kt, st);
+    }
+};
 
-// MFMA work on one stage (two 16-wide k steps of 32x32x16 MFMAs). PARTIAL
-// tiles (the last m-tile of an expert) skip the A reads and MFMAs of 32-row
-// groups that hold no valid row. For full tiles the order is pinned: the
-// NLOAD global loads issued just before, the first k step's fragment reads,
-// its MFMAs with the second step's reads spread over their first half, then
-// the second step's MFMAs.
-template <int BM, int BN, int WM, int WN, bool PARTIAL, int NLOAD>
-__device__ __forceinline__ void mfma_stage(const Stage<BM, BN>* st, int wm, int wn, int lane, int mi_lim,
-                                           floatx16 (&acc)[WM / 32][WN / 32])
+// One stage: wait for its loads and barrier, then its MFMAs (two 16-wide k
+// steps of 32x32x16) while this wave's loads of a later stage are issued.
+// Full tiles use a fixed, hand-placed instruction order (sched_barrier
+// between the pieces keeps the compiler's scheduler from regrouping them):
+// the first k step's fragment reads; then its MFMAs with the second step's
+// reads after every other MFMA and a global load after every fourth; then
+// the second step's MFMAs with the remaining loads. No wave ever issues a
+// burst of memory instructions while its matrix pipe sits idle.
+// PARTIAL tiles (the last m-tile of an expert) skip the A reads and MFMAs of
+// 32-row groups that hold no valid row, and issue their loads up front.
+template <int BM, int BN, int WM, int WN, int A_INS, int B_INS, bool PARTIAL>
+__device__ __forceinline__ void stage_step(const StageLoader<BM, BN, A_INS, B_INS>& ld, int kt_load,
+                                           Stage<BM, BN>* ld_st, const Stage<BM, BN>* st, int wm, int wn,
+                                           int lane, int mi_lim, floatx16 (&acc)[WM / 32][WN / 32])
 {
     constexpr int MI = WM / 32, NI = WN / 32, KS = kBK / 16;
+    constexpr int NLD = A_INS + B_INS;
+    static_assert(KS == 2, "two k steps per stage");
+    // Stage kt landed for this wave once at most two later stages (2 * NLD
+    // loads) are in flight; the barrier makes that true for every wave and
+    // frees the buffer the later stage is loaded into. (A bare s_barrier: a
+    // __syncthreads() fence would wait for all loads in flight.)
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NLD) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+
     const int lr = lane & 31;
-    bf16x8 afr[KS][MI], bfr[KS][NI];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    auto read_a = [&](int ks, int i) {
         const int c = ks * 2 + (lane >> 5);
-        const int col = c ^ ((lr >> 2) & 3);  // swz() of a row whose low 5 bits are lr
+        return as_bf16x8(st->a[(wm * WM + i * 32 + lr) * kCH + (c ^ ((lr >> 2) & 3))]);
+    };
+    auto read_b = [&](int ks, int j) { return as_bf16x8(st->b[((wn * NI + j) * 2 + ks) * 64 + lane]); };
+
+    if constexpr (PARTIAL) {
+        ld.issue_all(kt_load, ld_st);
 #pragma unroll
-        for (int j = 0; j < NI; ++j)
-            bfr[ks][j] = as_bf16x8(st->b[((wn * NI + j) * 2 + ks) * 64 + lane]);
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-            if (PARTIAL && i >= mi_lim)
-                continue;
-            afr[ks][i] = as_bf16x8(st->a[(wm * WM + i * 32 + lr) * kCH + col]);
-        }
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-            if (PARTIAL && i >= mi_lim)
-                continue;
+        for (int ks = 0; ks < KS; ++ks) {
+            bf16x8 bfr[NI];
 #pragma unroll
             for (int j = 0; j < NI; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
-        }
-    }
-    if constexpr (!PARTIAL) {
-        constexpr int R = MI + NI;  // fragment reads per k step
-        constexpr int M = MI * NI;  // MFMAs per k step
-        if constexpr (NLOAD > 0)
-            __builtin_amdgcn_sched_group_barrier(0x010, NLOAD, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
-        sched_spread<R, M / 2, 0>();
-        __builtin_amdgcn_sched_group_barrier(0x008, M - M / 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
-    }
-}
-
-// Wait until at most N of this wave's loads are still in flight (the N most
-// recently issued), then barrier: the stage about to be multiplied has landed
-// for every wave, and every wave is done with the stage multiplied before.
-// The scheduling barrier keeps MFMAs of the previous stage from moving across.
-template <int N>
-__device__ __forceinline__ void wait_loads_barrier()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-    __syncthreads();
-}
-
-// The K loop of one tile: a ring of kNBUF LDS stages with kDIST stages in
-// flight ahead of the one being multiplied, one barrier per stage. (A single
-// copy of the MFMA code in the loop keeps the accumulators in place.)
-template <int BM, int BN, int WM, int WN, int A_INS, int B_INS, bool PARTIAL>
-__device__ __forceinline__ void tile_k_loop(const uint16_t* A, const uint32_t (&aoff)[A_INS], const Vec16* bsrc,
-                                            int KB, int KT, Stage<BM, BN>* ring, int wv, int wm, int wn, int lane,
-                                            int mi_lim, floatx16 (&acc)[WM / 32][WN / 32])
-{
-    constexpr int PER = A_INS + B_INS;  // loads per wave per stage
-    static_assert(kDIST == 3 && kNBUF >= kDIST + 1, "ring layout");
+                bfr[j] = read_b(ks, j);
 #pragma unroll
-    for (int s = 0; s < kDIST; ++s)
-        if (s < KT)
-            issue_stage<BM, BN, A_INS, B_INS>(A, aoff, bsrc, KB, s, &ring[s], wv);
-    for (int kt = 0; kt < KT; ++kt) {
-        const int ahead = KT - 1 - kt;  // stages after this one, already issued up to kDIST - 1
-        if (ahead >= 2)
-            wait_loads_barrier<2 * PER>();
-        else if (ahead == 1)
-            wait_loads_barrier<PER>();
-        else
-            wait_loads_barrier<0>();
-        if (kt + kDIST < KT)
-            issue_stage<BM, BN, A_INS, B_INS>(A, aoff, bsrc, KB, kt + kDIST, &ring[(kt + kDIST) % kNBUF], wv);
-        mfma_stage<BM, BN, WM, WN, PARTIAL, 0>(&ring[kt % kNBUF], wm, wn, lane, mi_lim, acc);
+            for (int i = 0; i < MI; ++i) {
+                if (i >= mi_lim)
+                    continue;
+                const bf16x8 a = read_a(ks, i);
+#pragma unroll
+                for (int j = 0; j < NI; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfr[j], acc[i][j], 0, 0, 0);
+            }
+        }
+    } else {
+        constexpr int M = MI * NI;  // MFMAs per k step
+        constexpr int R = MI + NI;  // fragment reads per k step
+        constexpr int L0 = NLD / 2; // loads placed in the first k step, the rest in the second
+        bf16x8 f0a[MI], f0b[NI], f1a[MI], f1b[NI];
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+            f0b[j] = read_b(0, j);
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+            f0a[i] = read_a(0, i);
+        __builtin_amdgcn_sched_barrier(0);
+        int nread = 0, nld = 0;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const int i = m / NI, j = m % NI;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0a[i], f0b[j], acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            // spread: after MFMA m, reads up to ceil((m+1) R / M), loads up to (m+1) L0 / M
+#pragma unroll
+            for (; nread < ((m + 1) * R + M - 1) / M; ++nread) {
+                if (nread < NI)
+                    f1b[nread] = read_b(1, nread);
+                else
+                    f1a[nread - NI] = read_a(1, nread - NI);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (; nld < ((m + 1) * L0) / M; ++nld) {
+                ld.issue(nld, kt_load, ld_st);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const int i = m / NI, j = m % NI;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1a[i], f1b[j], acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (; nld < L0 + ((m + 1) * (NLD - L0)) / M; ++nld) {
+                ld.issue(nld, kt_load, ld_st);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (; nld < NLD; ++nld)
+            ld.issue(nld, kt_load, ld_st);
     }
+}
+
+// The K loop of one tile: a ring of four LDS stages (separate arrays, so the
+// compiler can tell them apart) with three stages in flight ahead of the one
+// being multiplied, one barrier per stage. Requires KT % 4 == 0. Stages past
+// the end are replaced by reloads of the last stage, which keeps the number of
+// loads per stage, and so every wait count, the same.
+template <int BM, int BN, int WM, int WN, int A_INS, int B_INS, bool PARTIAL>
+__device__ __forceinline__ void tile_k_loop(const StageLoader<BM, BN, A_INS, B_INS>& ld, int KT,
+                                            Stage<BM, BN>* s0, Stage<BM, BN>* s1, Stage<BM, BN>* s2,
+                                            Stage<BM, BN>* s3, int wm, int wn, int lane, int mi_lim,
+                                            floatx16 (&acc)[WM / 32][WN / 32])
+{
+    ld.issue_all(0, s0);
+    ld.issue_all(1, s1);
+    ld.issue_all(2, s2);
+    const int last = KT - 1;
+    for (int kt = 0; kt < KT; kt += 4) {
+        stage_step<BM, BN, WM, WN, A_INS, B_INS, PARTIAL>(ld, min(kt + 3, last), s3, s0, wm, wn, lane, mi_lim, acc);
+        stage_step<BM, BN, WM, WN, A_INS, B_INS, PARTIAL>(ld, min(kt + 4, last), s0, s1, wm, wn, lane, mi_lim, acc);
+        stage_step<BM, BN, WM, WN, A_INS, B_INS, PARTIAL>(ld, min(kt + 5, last), s1, s2, wm, wn, lane, mi_lim, acc);
+        stage_step<BM, BN, WM, WN, A_INS, B_INS, PARTIAL>(ld, min(kt + 6, last), s2, s3, wm, wn, lane, mi_lim, acc);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the trailing reloads
 }
 
 template <int BM, int BN, int WM, int WN, bool GATE_UP>
@@ -272,7 +300,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     static_assert(A_INS * 4 * 16 == BM && B_INS * 4 == (BN / 32) * 2, "stage split over 4 waves");
     static_assert(!GATE_UP || (NI % 2 == 0 && WN % 64 == 0), "gate/up pairs per wave");
 
-    __shared__ Stage<BM, BN> ring[kNBUF];
+    __shared__ Stage<BM, BN> st0, st1, st2, st3;
     __shared__ Tile s_tile;
 
     const int N = GATE_UP ? 2 * g.f : g.d;  // weight rows per expert
@@ -318,11 +346,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             for (int q = 0; q < 16; ++q)
                 acc[i][j][q] = 0.f;
 
-    const int KT = K / kBK;
+    const int KT = K / kBK;  // a multiple of 4 (K % 128 == 0)
+    const StageLoader<BM, BN, A_INS, B_INS> ld{A, aoff, bsrc, KB, wv};
     if (rows == BM)
-        tile_k_loop<BM, BN, WM, WN, A_INS, B_INS, false>(A, aoff, bsrc, KB, KT, ring, wv, wm, wn, lane, MI, acc);
+        tile_k_loop<BM, BN, WM, WN, A_INS, B_INS, false>(ld, KT, &st0, &st1, &st2, &st3, wm, wn, lane, MI, acc);
     else
-        tile_k_loop<BM, BN, WM, WN, A_INS, B_INS, true>(A, aoff, bsrc, KB, KT, ring, wv, wm, wn, lane,
+        tile_k_loop<BM, BN, WM, WN, A_INS, B_INS, true>(ld, KT, &st0, &st1, &st2, &st3, wm, wn, lane,
                                                         min(MI, max(0, (rows - wm * WM + 31) / 32)), acc);
 
     // Epilogue. 32x32 accumulator layout: lane holds column lane%32 and, for

@@ -59,6 +59,7 @@ FAKE = 0x100000  # never dereferenced: validation fails before any use
     (dict(n_experts=16, top_k=9), cm.ERR_UNSUPPORTED),
     (dict(d_model=192), cm.ERR_UNSUPPORTED),
     (dict(d_ff=100), cm.ERR_UNSUPPORTED),
+    (dict(d_ff=192), cm.ERR_UNSUPPORTED),
     (dict(max_tokens=(1 << 24) + 1), cm.ERR_UNSUPPORTED),
 ])
 def test_init_rejects_bad_configs(kw, status):

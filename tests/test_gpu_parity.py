@@ -18,18 +18,18 @@ C = synth.LayerConfig
 SMALL = [
     synth.CONFIGS["tiny-f32"],
     C("mixtral-small", 700, 256, 8, 2, 512, "bf16"),
-    C("fine-grained-small", 1000, 256, 128, 4, 192, "bf16"),
+    C("fine-grained-small", 1000, 256, 128, 4, 256, "bf16"),
     C("decode-small", 32, 512, 8, 2, 1024, "bf16"),
     C("skewed-small", 2000, 256, 64, 2, 128, "bf16", {0: 4.0, 3: 4.0}),
     C("skewed-masked-small", 2000, 256, 64, 2, 128, "bf16",
       {0: 4.0, 3: 4.0, **{e: -1.0e4 for e in range(44, 64)}}),
     C("f32-ragged", 77, 256, 6, 3, 192, "f32", {2: 0.3}),
-    C("one-token", 1, 128, 8, 2, 64, "bf16"),
-    C("ragged-17", 17, 384, 16, 3, 320, "bf16"),
+    C("one-token", 1, 128, 8, 2, 128, "bf16"),
+    C("ragged-17", 17, 384, 16, 3, 384, "bf16"),
     C("single-expert", 130, 128, 1, 1, 128, "bf16"),
     C("k-equals-E", 90, 256, 4, 4, 128, "bf16"),
     C("all-to-one", 300, 128, 8, 1, 128, "bf16", {5: 100.0}),
-    C("k8-E256", 64, 128, 256, 8, 64, "bf16"),
+    C("k8-E256", 64, 128, 256, 8, 128, "bf16"),
 ]
 
 
@@ -53,7 +53,7 @@ def test_empty_batch_and_errors():
 
     import sparse_moe_gemm_amd as cm
 
-    cfg = C("errs", 8, 128, 4, 2, 64, "bf16")
+    cfg = C("errs", 8, 128, 4, 2, 128, "bf16")
     inp = synth.make_inputs(cfg)
     layer = make_layer(cfg, inp, max_tokens=8)
     x = torch.zeros(16, 128, dtype=torch.bfloat16, device="cuda")

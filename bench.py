@@ -88,6 +88,30 @@ def active_weight_bytes(cfg, counts, stage):
     return n_active * per
 
 
+def profiled_traffic(workload: str):
+    """HBM bytes per launch of the gate/up GEMM from the committed rocprofv3
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's readings), or
+    None when that summary is missing or was taken on a different kernel source."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"gate_up_gemm_{workload}_rocprof.md")
+    src = os.path.join(ROOT, "sparse_moe_gemm_amd", "csrc", "gemm_bf16.hip")
+    if not os.path.exists(path):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("|"):
+            key, _, val = line.partition(":")
+            fields[key.strip()] = val.strip()
+    if fields.get("source_sha256(sparse_moe_gemm_amd/csrc/gemm_bf16.hip)") != sha:
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(cfg, inp, sample_tokens: int):
     import oracle
 
@@ -182,11 +206,12 @@ def main():
         dom = max(("gate_up_gemm", "down_gemm"), key=lambda s: stage_ms[s])
         achieved = active_weight_bytes(cfg, counts, dom) / (stage_ms[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": dom}
+                "frac": achieved / PEAK_HBM_GBS,
+                "traffic": profiled_traffic(args.workload) if dom == "gate_up_gemm" else None, "kernel": dom}
     else:
         achieved = fpa[dom] * A / (stage_ms[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak_mm, "unit": "TFLOP/s",
-                "frac": achieved / peak_mm, "traffic": None, "kernel": dom}
+                "frac": achieved / peak_mm, "traffic": profiled_traffic(args.workload), "kernel": dom}
 
     out = {
         "metric": METRIC,

@@ -121,8 +121,8 @@ def cpu_baseline(cfg, inp, sample_tokens: int):
     x = inp["x"]
     per_tok_macs = cfg.d * cfg.E + 3 * cfg.d * cfg.f * cfg.k
     if sample_tokens <= 0:
-        # About 15 s of wall time at ~0.5 GMAC/s per thread for this scalar code.
-        sample_tokens = int(15.0 * threads * 0.5e9 / per_tok_macs)
+        # About 15 s of wall time at ~2 GMAC/s per thread for this scalar code.
+        sample_tokens = int(15.0 * threads * 2.0e9 / per_tok_macs)
         sample_tokens = min(cfg.T, max(threads, sample_tokens))
     toks = np.arange(sample_tokens, dtype=np.int32)
     t0 = time.perf_counter()

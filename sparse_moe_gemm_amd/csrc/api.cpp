@@ -51,11 +51,11 @@ struct colibri_moe {
     int32_t* perm_slot;
     int32_t* inv;
     void* H;      // [A][f] dtype
-    float* Ys;    // [A][d] fp32
+    float* Ys;    // down GEMM output: kMaxSplit (bf16) or 1 (f32) partials of [A][d] fp32
     bool timing;
     hipEvent_t ev[kStages + 1];
-    int group_n;    // tile-order knobs of the grouped GEMMs
-    int xcd_remap;
+    int group_n;    // tile order of the grouped GEMMs (n-tiles per group)
+    int cus;        // compute units of the device (persistent GEMM grid)
 };
 
 namespace {
@@ -160,7 +160,8 @@ colibri_moe_status_t init_impl(colibri_moe* h, const colibri_moe_weights_t* w)
     const size_t o_ps = cv.take(A * sizeof(int32_t));
     const size_t o_inv = cv.take(A * sizeof(int32_t));
     const size_t o_h = cv.take(A * f * es);
-    const size_t o_ys = cv.take(A * d * sizeof(float));
+    const size_t n_ys = c.dtype == COLIBRI_MOE_BF16 ? (size_t)cmoe::kMaxSplit : 1;
+    const size_t o_ys = cv.take(n_ys * A * d * sizeof(float));
     h->arena_bytes = cv.off;
 
     if (hipMalloc(&h->arena, h->arena_bytes) != hipSuccess) {
@@ -231,11 +232,13 @@ colibri_moe_status_t colibri_moe_init(colibri_moe_t** out, const colibri_moe_con
     h->stream = (hipStream_t)hip_stream;
     h->esize = cfg->dtype == COLIBRI_MOE_BF16 ? 2 : 4;
     h->timing = (cfg->flags & COLIBRI_MOE_FLAG_STAGE_TIMING) != 0;
-    // Tile-order knobs of the grouped GEMMs (tuning only; results do not
-    // depend on them): CMOE_GROUP_N n-tiles per group, CMOE_XCD_REMAP 0/1.
-    h->group_n = env_int("CMOE_GROUP_N", 16, 1, 1 << 20);
-    h->xcd_remap = env_int("CMOE_XCD_REMAP", 0, 0, 1);
-    if (hipGetDevice(&h->device) != hipSuccess) {
+    // Tile order of the grouped GEMMs (tuning only; results do not depend
+    // on it): CMOE_GROUP_N n-tiles per group.
+    h->group_n = env_int("CMOE_GROUP_N", 64, 1, 1 << 20);
+    if (hipGetDevice(&h->device) != hipSuccess ||
+        hipDeviceGetAttribute(&h->cus, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess ||
+        h->cus <= 0) {
+        (void)hipGetLastError();
         release(h);
         return COLIBRI_MOE_ERR_HIP;
     }
@@ -299,19 +302,20 @@ colibri_moe_status_t colibri_moe_forward(colibri_moe_t* h, const void* x, int32_
     if (tm)
         CMOE_HIP(hipEventRecord(h->ev[2], s));
 
-    GemmArgs gu{x, h->w_gu, h->H, offsets, perm, perm_slot, T * c.top_k, c.n_experts, c.top_k, c.d_model,
-                c.d_ff, h->group_n, h->xcd_remap};
+    const int A = T * c.top_k;
+    GemmArgs gu{x, h->w_gu, h->H, offsets, perm, A, c.n_experts, c.top_k, c.d_model, c.d_ff, h->group_n, 1, h->cus};
     CMOE_HIP(bf ? launch_gate_up_bf16(gu, s) : launch_gate_up_f32(gu, s));
     if (tm)
         CMOE_HIP(hipEventRecord(h->ev[3], s));
 
-    GemmArgs dn{h->H, h->w_d, h->Ys, offsets, perm, perm_slot, T * c.top_k, c.n_experts, c.top_k, c.d_model,
-                c.d_ff, h->group_n, h->xcd_remap};
+    const int split = bf ? down_split_bf16(A, c.n_experts, c.d_model, c.d_ff, h->cus) : 1;
+    GemmArgs dn{h->H, h->w_d, h->Ys, offsets, perm, A, c.n_experts, c.top_k, c.d_model, c.d_ff, h->group_n, split,
+                h->cus};
     CMOE_HIP(bf ? launch_down_bf16(dn, s) : launch_down_f32(dn, s));
     if (tm)
         CMOE_HIP(hipEventRecord(h->ev[4], s));
 
-    CombineArgs ca{h->Ys, topw, y, T, c.top_k, c.d_model, bf ? 1 : 0};
+    CombineArgs ca{h->Ys, inv, topw, y, T, c.top_k, c.d_model, split, bf ? 1 : 0};
     CMOE_HIP(launch_combine(ca, s));
     if (tm)
         CMOE_HIP(hipEventRecord(h->ev[5], s));

@@ -3,11 +3,14 @@
 // The combine kernel of «Colibri 是什么» (xxqk.cn) §2.3 (the k expert outputs
 // weighted by the gating scores and summed) and the final step of
 // «Colibri：面向MoE模型的高性能C语言推理引擎» (zskr.cn) §3.3:
-//   y[t][o] = sum_{j<k} w[t][j] * Ys[t*k + j][o]
+//   y[t][o] = sum_{j<k} w[t][j] * Ys[inv[t*k + j]][o]
 // accumulated in fp32 in slot order (fused multiply-add), then rounded to
-// the output dtype (round to nearest even for bf16). The down GEMM already
-// wrote each expert output at its assignment row t*k+j, so each thread reads
-// k contiguous-by-slot rows with 16-byte loads; the kernel is bound by HBM.
+// the output dtype (round to nearest even for bf16). The down GEMM wrote each
+// expert output at its sorted position p; inv maps assignment t*k+j to it.
+// When the down GEMM split K, Ys holds `split` partial sums per row (at
+// strides of T*k rows), added in split order before the weighting. Each
+// thread handles 4 consecutive outputs with 16-byte loads; the kernel is
+// bound by HBM.
 #include "common.hpp"
 
 namespace cmoe {
@@ -22,9 +25,18 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs g)
         const int64_t t = idx / (g.d / 4);
         const int o = (int)(idx % (g.d / 4)) * 4;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        const int64_t stride = (int64_t)g.T * g.k * g.d;
         for (int j = 0; j < g.k; ++j) {
             const float wj = g.w[t * g.k + j];
-            const float4 v = *(const float4*)(g.ys + (t * g.k + j) * g.d + o);
+            const float* row = g.ys + (int64_t)g.inv[t * g.k + j] * g.d + o;
+            float4 v = *(const float4*)row;
+            for (int s = 1; s < g.split; ++s) {
+                const float4 u = *(const float4*)(row + s * stride);
+                v.x += u.x;
+                v.y += u.y;
+                v.z += u.z;
+                v.w += u.w;
+            }
             acc.x = fmaf(wj, v.x, acc.x);
             acc.y = fmaf(wj, v.y, acc.y);
             acc.z = fmaf(wj, v.z, acc.z);

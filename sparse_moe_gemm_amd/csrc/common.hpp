@@ -71,31 +71,39 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
 
 struct GemmArgs {
     // gate/up: A rows are x[perm[p]] ([T][d]); B = interleaved gate/up weights
-    //   [E][2f][d]; out = H [A][f].
+    //   [E][2f][d]; out = H [A][f] (row p = sorted position p).
     // down:    A rows are H[p] ([A][f]);        B = down weights [E][d][f];
-    //   out = Ys [A][d] fp32, row p written to assignment row perm[p]*k+perm_slot[p].
+    //   out = Ys: split partial sums over K, partial s at Ys + s*A*d, each
+    //   [A][d] fp32 with row p = sorted position p (combine gathers them
+    //   through inv).
     // bf16 weights are in the blocked MFMA layout, fp32 weights row-major.
     const void* a;
     const void* b;
     void* out;
     const int32_t* offsets;   // [E+1]
     const int32_t* perm;      // [A]
-    const int32_t* perm_slot; // [A]
-    int A_max;                // T*k of this call (bounds the tile grid)
+    int A_max;                // A = T*k of this call (bounds the tile grid)
     int E, k, d, f;
     int group_n;              // n-tiles per tile group (tile order), >= 1
-    int xcd_remap;            // 1: give each XCD a contiguous range of tiles
+    int split;                // K splits of the down GEMM (1 or 2; gate/up: 1)
+    int grid;                 // workgroups of a persistent launch (compute units)
 };
 hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t s);
 hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t s);
+// K splits the bf16 down GEMM uses for a call with A = T*k assignments on
+// `cus` compute units (1 or 2; the Ys workspace holds kMaxSplit partials).
+constexpr int kMaxSplit = 2;
+int down_split_bf16(int A, int E, int d, int f, int cus);
 hipError_t launch_gate_up_f32(const GemmArgs& a, hipStream_t s);
 hipError_t launch_down_f32(const GemmArgs& a, hipStream_t s);
 
 struct CombineArgs {
-    const float* ys;    // [T*k][d] fp32, row t*k+j
+    const float* ys;    // split partials, each [A][d] fp32 by sorted position
+    const int32_t* inv; // [A]: sorted position of assignment t*k+j
     const float* w;     // [T][k]
     void* y;            // [T][d] dtype
     int T, k, d;
+    int split;          // number of partials, at ys + s*T*k*d
     int bf16_out;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);

@@ -6,31 +6,32 @@
 // SiLU epilogue inlined into the first GEMM), with weight tiles staged in
 // shared memory (LDS) as §5.1 of that page describes.
 //
-//   gate/up:  H[p][c]  = SiLU(sum_i X[perm[p]][i] Wg[e][c][i]) * (sum_i X[perm[p]][i] Wu[e][c][i])
-//   down:     Ys[q][o] = sum_c H[p][c] Wd[e][o][c],     q = perm[p]*k + perm_slot[p]
+//   gate/up:  H[p][c]    = SiLU(sum_i X[perm[p]][i] Wg[e][c][i]) * (sum_i X[perm[p]][i] Wu[e][c][i])
+//   down:     Ys_s[p][o] = sum_{c in K split s} H[p][c] Wd[e][o][c]
 // for every sorted position p of expert e's segment [offsets[e], offsets[e+1]).
 //
 // Operands: v_mfma_f32_32x32x16_bf16 (it keeps the matrix pipe full from a
-// single wave per SIMD; the 16x16x32 form does not) takes, from lane l, 8
-// consecutive k of row l%32 of A and of B. Token rows (A) are K-contiguous and
-// are gathered through perm straight into LDS with gfx950's direct
-// global->LDS loads; each wave reads its A fragments from there. Weights (B)
-// do not pass through LDS at all: init stores them pre-blocked in MFMA operand
-// order (32 rows x 16 k per 1 KiB block, lane-major), so each wave fetches its
-// B fragments with fully coalesced 16-byte loads straight into VGPRs, one
-// stage ahead. This halves LDS traffic, which otherwise caps the MFMA rate.
-// Gate and up weights are interleaved in blocks of 32 rows (32 gate rows,
-// then the 32 up rows of the same hidden units), so each wave holds the gate
-// and up accumulators of the same outputs and applies SiLU(g)*u in registers.
+// single wave per SIMD) takes, from lane l, 8 consecutive k of row l%32 of A
+// and of B. Init stores the weights pre-blocked in MFMA operand order (32 rows
+// x 16 k per 1 KiB block, lane-major). For every 32-wide K stage of a tile the
+// token rows (A; gathered through perm for gate/up) and whole weight blocks
+// (B) are copied into LDS by gfx950's buffer->LDS loads, which use no VGPRs
+// and whose addressing is scalar apart from one per-lane offset; the waves
+// read their fragments from LDS with 16-byte reads. Gate and up weights are
+// interleaved in blocks of 32 rows, so each wave holds the gate and up
+// accumulators of the same outputs and applies SiLU(g)*u in registers.
 //
 // Work decomposition: a tile is (expert, m-tile of BM sorted rows, n-tile of
-// BN weight rows). Experts with no rows have no tiles, so their weights are
-// never read. The host only knows an upper bound of the tile count (the counts
-// live on the device); each workgroup derives its tile from offsets[] and
-// exits if it has none. Workgroup ids are spread over the 8 XCDs round-robin,
-// so consecutive tile indices are handed to the same XCD, and tiles are
-// ordered expert -> group of GN n-tiles -> m-tile -> n-tile: the workgroups
-// one XCD runs together share weight panels and token panels in its L2.
+// BN weight rows, K split). Experts with no rows have no tiles, so their
+// weights are never read. The kernel is persistent: one workgroup per compute
+// unit takes tiles blockIdx.x, + gridDim.x, ... and runs all their K stages as
+// one stream through a ring of five LDS stages, so the first stages of the
+// next tile load while the current one finishes and writes its outputs. The
+// tile count depends on the routing and lives on the device: every wave
+// derives it, and the tile behind an index, from offsets[] held in registers.
+// Tiles are ordered expert -> split -> group of GN n-tiles -> m-tile ->
+// n-tile; workgroups are spread over the 8 XCDs round robin, so the tiles one
+// XCD runs together share a few token and weight panels in its L2.
 #include "common.hpp"
 
 namespace cmoe {
@@ -38,9 +39,10 @@ namespace cmoe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBK = 32;            // k per LDS stage
-constexpr int kCH = kBK / 8;       // 16-byte chunks per A row per stage
-constexpr int kXCD = 8;
+constexpr int kBK = 32;                 // k per LDS stage
+constexpr int kCH = kBK / 8;            // 16-byte chunks per A row per stage
+constexpr int kRing = 5;                // LDS stages in the ring
+constexpr int kAhead = kRing - 1;       // stages in flight ahead of the one multiplied
 
 // XOR swizzle of the 16-byte chunk index inside an A row of the LDS stage:
 // the 16 lanes that read one chunk column of 16 consecutive rows (rows are 64 B
@@ -50,243 +52,345 @@ __device__ __forceinline__ int swz(int row, int chunk)
     return chunk ^ ((row >> 2) & 3);
 }
 
-struct Tile {
-    int e, m, n, valid;
-};
-
-// Map this workgroup to a tile. Executed by wave 0; result in *out.
-template <int BM>
-__device__ void find_tile(const int32_t* offsets, int E, int NT, int GN, int remap, Tile* out)
-{
-    const int lane = threadIdx.x;
-    int tl[4];
-    int sum = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int e = lane * 4 + q;
-        const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
-        tl[q] = ((c + BM - 1) / BM) * NT;
-        sum += tl[q];
-    }
-    int incl = sum;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int o = __shfl_up(incl, off, kWave);
-        if (lane >= off)
-            incl += o;
-    }
-    const int total = __shfl(incl, kWave - 1, kWave);
-    const int wg = blockIdx.x;
-    if (wg >= total) {
-        if (lane == 0)
-            out->valid = 0;
-        return;
-    }
-    // XCD-aware renumbering: workgroup wg runs on XCD wg % 8; give each XCD a
-    // contiguous range of tile indices.
-    const int xcd = wg % kXCD, local = wg / kXCD;
-    const int base = total / kXCD, rem = total % kXCD;
-    const int L = remap ? xcd * base + min(xcd, rem) + local : wg;
-    int start = incl - sum;
-    if (L >= start && L < incl) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if (L >= start && L < start + tl[q]) {
-                const int e = lane * 4 + q;
-                const int Me = tl[q] / NT;
-                const int l = L - start;
-                const int g = l / (Me * GN);
-                const int gn = min(GN, NT - g * GN);
-                const int idx = l - g * Me * GN;
-                out->e = e;
-                out->m = idx / gn;
-                out->n = g * GN + idx % gn;
-                out->valid = 1;
-            }
-            start += tl[q];
-        }
-    }
-}
-
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// LDS stage layout (one 32-wide K stage of a 256 x 256 tile):
+// SiLU with the hardware reciprocal (about 1 ulp) instead of an IEEE divide;
+// the result is rounded to bf16 right after.
+__device__ __forceinline__ float silu_rcp(float z)
+{
+    return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p)
+{
+    return (uint32_t)(size_t)(lds_void_t*)p;
+}
+
+// LDS stage layout (one 32-wide K stage of a BM x BN tile):
 //   A: BM rows x 4 chunks of 16 B (8 bf16), chunk index swizzled per row;
 //   B: BN/32 x 2 blocks of 1 KiB, each a 32-row x 16-k weight block in MFMA
 //      operand order (lane l's 8 values at l*16 B), copied whole from the
 //      blocked weight layout.
-// Both are filled with direct global->LDS loads (global_load_lds_dwordx4: 64
-// lanes x 16 B into 1 KiB of LDS, lane s into slot s); no VGPR staging.
 template <int BM, int BN>
 struct Stage {
     Vec16 a[BM * kCH];
     Vec16 b[(BN / 32) * 2 * 64];
 };
+template <int BM, int BN>
+struct Ring {
+    Stage<BM, BN> st[kRing];
+};
 
-// One direct global->LDS load: 64 lanes x 16 B from per-lane addresses into
-// the 1 KiB of LDS at the wave-uniform address lds (through M0). Written as
-// inline assembly on purpose: the ordering of these LDS writes against the LDS
-// reads of other stages is handled explicitly (a vmcnt wait and a barrier per
-// stage), and an opaque instruction keeps the compiler from adding its own
-// full waits before LDS reads, which would drain the stages in flight.
-// Nothing else in these kernels uses M0.
-__device__ __forceinline__ void dma16(const void* gptr, const void* lds)
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource of a raw byte buffer: base address, size in bytes (loads
+// past it return zeros instead of touching memory), stride 0.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes)
 {
-    const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_void_t*)lds);
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(a)
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int32_t)((a >> 32) & 0xFFFFu));
+    r[2] = __builtin_amdgcn_readfirstlane((int32_t)bytes);
+    r[3] = 0x00020000;  // raw buffer, 32-bit data format (CDNA)
+    return r;
+}
+
+// One direct buffer->LDS load: 64 lanes x 16 B from rsrc + voff (per lane) +
+// soff (wave-uniform) into the 1 KiB of LDS at byte address lds (through M0),
+// lane s into slot s. Written as inline assembly on purpose: the ordering of
+// these LDS writes against the LDS reads of other stages is handled
+// explicitly (vmcnt waits and barriers), and an opaque instruction keeps the
+// compiler from adding its own full waits before LDS reads, which would drain
+// the stages in flight. Nothing else in these kernels uses M0.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc),
+                 "s"(soff), "s"(lds)
                  : "memory");
 }
 
-// This wave's share of one stage's loads: A_INS instructions of 16 A rows each,
-// then B_INS whole weight blocks; instruction q is issued by issue(q, ...).
-template <int BM, int BN, int A_INS, int B_INS>
-struct StageLoader {
-    const uint16_t* A;
-    const uint32_t* aoff;
-    const Vec16* bsrc;
-    int KB, wv;
-
-    __device__ __forceinline__ void issue(int q, int kt, Stage<BM, BN>* st) const
-    {
-        if (q < A_INS) {
-            dma16(A + aoff[q] + kt * kBK, st->a + (wv * A_INS + q) * 64);
-        } else {
-            const int blk = wv * B_INS + (q - A_INS);  // = row block * 2 + k block within the stage
-            dma16(bsrc + ((int64_t)(blk >> 1) * KB + kt * 2 + (blk & 1)) * 64, st->b + blk * 64);
-        }
-    }
-    __device__ __forceinline__ void issue_all(int kt, Stage<BM, BN>* st) const
-    {
-#pragma unroll
-        for (int q = 0; q < A_INS + B_INS; ++q)
-            issue(q, kt, st);
-    }
+// Where the loads of one stage come from: the tile's weight panel, the
+// per-lane byte offsets of its A rows (chunk included) and the k stage.
+template <int A_INS>
+struct LoadSrc {
+    i32x4 rb;
+    uint32_t aoff[A_INS];
+    int kt;
 };
 
-// One stage: wait for its loads and barrier, then its MFMAs (two 16-wide k
-// steps of 32x32x16) while this wave's loads of a later stage are issued.
-// Full tiles use a fixed, hand-placed instruction order (sched_barrier
-// between the pieces keeps the compiler's scheduler from regrouping them):
-// the first k step's fragment reads; then its MFMAs with the second step's
-// reads after every other MFMA and a global load after every fourth; then
-// the second step's MFMAs with the remaining loads. No wave ever issues a
-// burst of memory instructions while its matrix pipe sits idle.
-// PARTIAL tiles (the last m-tile of an expert) skip the A reads and MFMAs of
-// 32-row groups that hold no valid row, and issue their loads up front.
-template <int BM, int BN, int WM, int WN, int A_INS, int B_INS, bool PARTIAL>
-__device__ __forceinline__ void stage_step(const StageLoader<BM, BN, A_INS, B_INS>& ld, int kt_load,
-                                           Stage<BM, BN>* ld_st, const Stage<BM, BN>* st, int wm, int wn,
-                                           int lane, int mi_lim, floatx16 (&acc)[WM / 32][WN / 32])
+// Load q of this wave's share of one stage into the stage at LDS byte address
+// lds: A_INS instructions of 16 A rows each, then B_INS whole weight blocks.
+template <int BM, int BN, int A_INS, int B_INS>
+__device__ __forceinline__ void issue_load(int q, const i32x4& ra, const LoadSrc<A_INS>& ls, int KB, int wv,
+                                           uint32_t lane16, uint32_t lds)
 {
-    constexpr int MI = WM / 32, NI = WN / 32, KS = kBK / 16;
-    constexpr int NLD = A_INS + B_INS;
-    static_assert(KS == 2, "two k steps per stage");
-    // Stage kt landed for this wave once at most two later stages (2 * NLD
-    // loads) are in flight; the barrier makes that true for every wave and
-    // frees the buffer the later stage is loaded into. (A bare s_barrier: a
-    // __syncthreads() fence would wait for all loads in flight.)
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NLD) : "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-
-    const int lr = lane & 31;
-    auto read_a = [&](int ks, int i) {
-        const int c = ks * 2 + (lane >> 5);
-        return as_bf16x8(st->a[(wm * WM + i * 32 + lr) * kCH + (c ^ ((lr >> 2) & 3))]);
-    };
-    auto read_b = [&](int ks, int j) { return as_bf16x8(st->b[((wn * NI + j) * 2 + ks) * 64 + lane]); };
-
-    if constexpr (PARTIAL) {
-        ld.issue_all(kt_load, ld_st);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            bf16x8 bfr[NI];
-#pragma unroll
-            for (int j = 0; j < NI; ++j)
-                bfr[j] = read_b(ks, j);
-#pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                if (i >= mi_lim)
-                    continue;
-                const bf16x8 a = read_a(ks, i);
-#pragma unroll
-                for (int j = 0; j < NI; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfr[j], acc[i][j], 0, 0, 0);
-            }
-        }
+    using St = Stage<BM, BN>;
+    constexpr uint32_t kOffA = (uint32_t)offsetof(St, a);
+    constexpr uint32_t kOffB = (uint32_t)offsetof(St, b);
+    if (q < A_INS) {
+        dma16(ra, ls.aoff[q], (uint32_t)ls.kt * (kBK * 2), lds + kOffA + (uint32_t)(wv * A_INS + q) * 1024u);
     } else {
-        constexpr int M = MI * NI;  // MFMAs per k step
-        constexpr int R = MI + NI;  // fragment reads per k step
-        constexpr int L0 = NLD / 2; // loads placed in the first k step, the rest in the second
-        bf16x8 f0a[MI], f0b[NI], f1a[MI], f1b[NI];
-#pragma unroll
-        for (int j = 0; j < NI; ++j)
-            f0b[j] = read_b(0, j);
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-            f0a[i] = read_a(0, i);
-        __builtin_amdgcn_sched_barrier(0);
-        int nread = 0, nld = 0;
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const int i = m / NI, j = m % NI;
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0a[i], f0b[j], acc[i][j], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            // spread: after MFMA m, reads up to ceil((m+1) R / M), loads up to (m+1) L0 / M
-#pragma unroll
-            for (; nread < ((m + 1) * R + M - 1) / M; ++nread) {
-                if (nread < NI)
-                    f1b[nread] = read_b(1, nread);
-                else
-                    f1a[nread - NI] = read_a(1, nread - NI);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-#pragma unroll
-            for (; nld < ((m + 1) * L0) / M; ++nld) {
-                ld.issue(nld, kt_load, ld_st);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const int i = m / NI, j = m % NI;
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1a[i], f1b[j], acc[i][j], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (; nld < L0 + ((m + 1) * (NLD - L0)) / M; ++nld) {
-                ld.issue(nld, kt_load, ld_st);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-#pragma unroll
-        for (; nld < NLD; ++nld)
-            ld.issue(nld, kt_load, ld_st);
+        const int blk = wv * B_INS + (q - A_INS);  // = row block * 2 + k block within the stage
+        const uint32_t soff = ((uint32_t)(blk >> 1) * (uint32_t)KB + (uint32_t)ls.kt * 2u + (uint32_t)(blk & 1)) * 1024u;
+        dma16(ls.rb, lane16, soff, lds + kOffB + (uint32_t)blk * 1024u);
     }
 }
 
-// The K loop of one tile: a ring of four LDS stages (separate arrays, so the
-// compiler can tell them apart) with three stages in flight ahead of the one
-// being multiplied, one barrier per stage. Requires KT % 4 == 0. Stages past
-// the end are replaced by reloads of the last stage, which keeps the number of
-// loads per stage, and so every wait count, the same.
-template <int BM, int BN, int WM, int WN, int A_INS, int B_INS, bool PARTIAL>
-__device__ __forceinline__ void tile_k_loop(const StageLoader<BM, BN, A_INS, B_INS>& ld, int KT,
-                                            Stage<BM, BN>* s0, Stage<BM, BN>* s1, Stage<BM, BN>* s2,
-                                            Stage<BM, BN>* s3, int wm, int wn, int lane, int mi_lim,
-                                            floatx16 (&acc)[WM / 32][WN / 32])
-{
-    ld.issue_all(0, s0);
-    ld.issue_all(1, s1);
-    ld.issue_all(2, s2);
-    const int last = KT - 1;
-    for (int kt = 0; kt < KT; kt += 4) {
-        stage_step<BM, BN, WM, WN, A_INS, B_INS, PARTIAL>(ld, min(kt + 3, last), s3, s0, wm, wn, lane, mi_lim, acc);
-        stage_step<BM, BN, WM, WN, A_INS, B_INS, PARTIAL>(ld, min(kt + 4, last), s0, s1, wm, wn, lane, mi_lim, acc);
-        stage_step<BM, BN, WM, WN, A_INS, B_INS, PARTIAL>(ld, min(kt + 5, last), s1, s2, wm, wn, lane, mi_lim, acc);
-        stage_step<BM, BN, WM, WN, A_INS, B_INS, PARTIAL>(ld, min(kt + 6, last), s2, s3, wm, wn, lane, mi_lim, acc);
+// Fragment readers of one LDS stage for wave (wm, wn): A fragment i (rows
+// wm*WM + i*32 ..) and B fragment j (weight rows wn*WN + j*32 ..) of k step ks.
+template <int BM, int BN, int WM, int WN>
+struct FragReader {
+    const Stage<BM, BN>* st;
+    int wm, wn, lane;
+    __device__ __forceinline__ bf16x8 a(int ks, int i) const
+    {
+        const int lr = lane & 31;
+        const int c = ks * 2 + (lane >> 5);
+        return as_bf16x8(st->a[(wm * WM + i * 32 + lr) * kCH + (c ^ ((lr >> 2) & 3))]);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the trailing reloads
+    __device__ __forceinline__ bf16x8 b(int ks, int j) const
+    {
+        return as_bf16x8(st->b[((wn * (WN / 32) + j) * 2 + ks) * 64 + lane]);
+    }
+};
+
+// One K stage, software-pipelined so that the matrix pipe never waits on a
+// barrier or on a fragment read:
+//   first half:  MFMAs of k step 0 (fragments fa/fb, read during the previous
+//                stage); the reads of k step 1's fragments spread over its
+//                first half; half of this wave's loads of the stage kAhead
+//                later spread over all of it.
+//   middle:      wait for those reads and until the next stage has landed for
+//                this wave, then barrier. After it every wave has landed the
+//                next stage and has finished every read of this stage and of
+//                all earlier ones.
+//   second half: MFMAs of k step 1; the reads of the NEXT stage's k step 0
+//                fragments into fa/fb; the other half of the loads.
+// The loads issued in stage s fill the ring slot of stage s-1, whose last
+// reads completed before the middle barrier of stage s-1. The wait count is
+// exact: loads complete in issue order, and when the middle of stage s is
+// reached, the loads issued after those of stage s+1 are the ones of stages
+// s+2 and s+3 and the first half of stage s+4's. The instruction order is
+// fixed by hand (sched_barrier between the pieces keeps the compiler's
+// scheduler from regrouping them).
+// The last m-tile of an expert runs the same code: its rows past the segment
+// end repeat the last valid row and their results are dropped. (A variant
+// that skips their MFMAs needs more registers than the persistent loop has.)
+template <int BM, int BN, int WM, int WN, int A_INS, int B_INS>
+__device__ __forceinline__ void stage(const i32x4& ra, const LoadSrc<A_INS>& ls, uint32_t ld_lds, int KB, int wv,
+                                      uint32_t lane16, const Stage<BM, BN>* st, const Stage<BM, BN>* st_next,
+                                      int wm, int wn, int lane, bf16x8 (&fa)[WM / 32],
+                                      bf16x8 (&fb)[WN / 32], floatx16 (&acc)[WM / 32][WN / 32])
+{
+    constexpr int MI = WM / 32, NI = WN / 32;
+    constexpr int NLD = A_INS + B_INS;
+    constexpr int M = MI * NI;   // MFMAs per k step
+    constexpr int R = MI + NI;   // fragment reads per k step
+    constexpr int RS = M / 2;    // reads are spread over the first RS MFMAs
+    constexpr int L0 = NLD / 2;  // loads in the first half
+    static_assert(kBK == 32, "two k steps per stage");
+    const FragReader<BM, BN, WM, WN> rd{st, wm, wn, lane}, rn{st_next, wm, wn, lane};
+    bf16x8 ga[MI], gb[NI];
+
+    int nread = 0, nld = 0;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const int i = m / NI, j = m % NI;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (; nread < R && nread < ((m + 1) * R + RS - 1) / RS; ++nread) {
+            if (nread < NI)
+                gb[nread] = rd.b(1, nread);
+            else
+                ga[nread - NI] = rd.a(1, nread - NI);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (; nld < ((m + 1) * L0) / M; ++nld) {
+            issue_load<BM, BN, A_INS, B_INS>(nld, ra, ls, KB, wv, lane16, ld_lds);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(%0)" ::"n"(2 * NLD + L0) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
+    nread = 0;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const int i = m / NI, j = m % NI;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[i], gb[j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (; nread < R && nread < ((m + 1) * R + RS - 1) / RS; ++nread) {
+            if (nread < NI)
+                fb[nread] = rn.b(0, nread);
+            else
+                fa[nread - NI] = rn.a(0, nread - NI);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (; nld < L0 + ((m + 1) * (NLD - L0)) / M; ++nld) {
+            issue_load<BM, BN, A_INS, B_INS>(nld, ra, ls, KB, wv, lane16, ld_lds);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// Per-lane view of the m-tiles: lane l holds experts 4l .. 4l+3 (E <= 256).
+struct TileTable {
+    int off[4];  // segment start offsets[e]
+    int cnt[4];  // rows of the expert
+    int mpre;    // m-tiles of all experts below 4l
+    int msum;    // m-tiles of this lane's experts
+};
+
+template <int BM>
+__device__ __forceinline__ int make_table(const int32_t* offsets, int E, int lane, TileTable& t)
+{
+    int ms = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = lane * 4 + q;
+        const int o0 = e < E ? offsets[e] : 0;
+        const int o1 = e < E ? offsets[e + 1] : 0;
+        t.off[q] = o0;
+        t.cnt[q] = o1 - o0;
+        ms += (o1 - o0 + BM - 1) / BM;
+    }
+    int incl = ms;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int o = __shfl_up(incl, d, kWave);
+        if (lane >= d)
+            incl += o;
+    }
+    t.mpre = incl - ms;
+    t.msum = ms;
+    return __builtin_amdgcn_readfirstlane(__shfl(incl, kWave - 1, kWave));  // total m-tiles (uniform)
+}
+
+struct Tile {
+    int e, m, n, s;
+    int row0, rows;  // first sorted row and valid rows of the m-tile
+    int kt0, nkt;    // K stages of the split
+};
+
+// Tile behind index L (< total). Tiles of one m-tile are consecutive in the
+// global m-tile order, NT * S of them, so L / (NT * S) is the global m-tile
+// index j; the lane whose experts cover j holds the expert.
+template <int BM>
+__device__ __forceinline__ Tile decode(const TileTable& t, int L, int NT, int S, int GN, int KT)
+{
+    const int per_m = NT * S;
+    const int j = L / per_m;
+    const uint64_t hit = __ballot(j >= t.mpre && j < t.mpre + t.msum);
+    const int ln = __builtin_ctzll(hit);
+    int base = __builtin_amdgcn_readlane(t.mpre, ln);
+    int e = 0, Me = 0, cnt = 0, seg0 = 0;
+    bool found = false;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int c = __builtin_amdgcn_readlane(t.cnt[q], ln);
+        const int o = __builtin_amdgcn_readlane(t.off[q], ln);
+        const int me = (c + BM - 1) / BM;
+        if (!found) {
+            if (j < base + me) {
+                found = true;
+                e = ln * 4 + q;
+                Me = me;
+                cnt = c;
+                seg0 = o;
+            } else {
+                base += me;
+            }
+        }
+    }
+    Tile r;
+    const int local = L - base * per_m;
+    r.s = local / (Me * NT);
+    const int rem = local - r.s * Me * NT;
+    const int grp = rem / (Me * GN);
+    const int gn = min(GN, NT - grp * GN);
+    const int idx = rem - grp * Me * GN;
+    r.e = e;
+    r.m = idx / gn;
+    r.n = grp * GN + (idx - r.m * gn);
+    r.row0 = seg0 + r.m * BM;
+    r.rows = min(BM, cnt - r.m * BM);
+    const int per_s = KT / S;
+    r.kt0 = r.s * per_s;
+    r.nkt = (r.s == S - 1) ? KT - r.kt0 : per_s;
+    // The divisions above run on the vector ALU; pin the (uniform) results to
+    // scalar registers so everything derived from them stays scalar.
+    r.e = __builtin_amdgcn_readfirstlane(r.e);
+    r.m = __builtin_amdgcn_readfirstlane(r.m);
+    r.n = __builtin_amdgcn_readfirstlane(r.n);
+    r.s = __builtin_amdgcn_readfirstlane(r.s);
+    r.row0 = __builtin_amdgcn_readfirstlane(r.row0);
+    r.rows = __builtin_amdgcn_readfirstlane(r.rows);
+    r.kt0 = __builtin_amdgcn_readfirstlane(r.kt0);
+    r.nkt = __builtin_amdgcn_readfirstlane(r.nkt);
+    return r;
+}
+
+// Buffer resource of a tile's weight panel (blocked layout), bounded by the
+// end of its expert's weights.
+template <int BN>
+__device__ __forceinline__ i32x4 panel_rsrc(const void* b, const Tile& t, int N, int KB)
+{
+    const uint8_t* p = (const uint8_t*)b + (((int64_t)t.e * (N / 32) + (int64_t)t.n * (BN / 32)) * KB) * 1024;
+    return make_rsrc(p, (uint32_t)((N / 32 - t.n * (BN / 32)) * KB) * 1024u);
+}
+
+// The K stages of one tile, continuing the stream: stage j multiplies ring
+// slot b and loads stream stage j + kAhead, which is stage j + kAhead of this
+// tile, or of the next tile (its A rows are `held`), or, past the last
+// tile, a reload of this tile's last stage that nobody reads (it keeps the
+// loads per stage, and so every wait count, the same).
+template <int BM, int BN, int WM, int WN, int A_INS, int B_INS>
+__device__ __forceinline__ void tile_stages(const i32x4& ra, const LoadSrc<A_INS>& cs, int nkt, bool has_nxt,
+                                            const i32x4& nrb, int nkt0, const uint32_t (&cpart)[A_INS],
+                                            uint32_t Kbytes, int KB, int wv, uint32_t lane16, Ring<BM, BN>& ring,
+                                            uint32_t ring0, int& b, int wm, int wn, int lane,
+                                            bf16x8 (&fa)[WM / 32], bf16x8 (&fb)[WN / 32],
+                                            const uint32_t (&held)[A_INS], floatx16 (&acc)[WM / 32][WN / 32])
+{
+    constexpr uint32_t kStageBytes = sizeof(Stage<BM, BN>);
+    int j = 0;
+    do {  // a tile has at least kAhead stages
+        const int ja = j + kAhead;
+        LoadSrc<A_INS> ls = cs;
+        if (ja < nkt) {
+            ls.kt = cs.kt + ja;
+        } else if (has_nxt) {
+            ls.rb = nrb;
+#pragma unroll
+            for (int i = 0; i < A_INS; ++i)
+                ls.aoff[i] = held[i] * Kbytes + cpart[i];
+            ls.kt = nkt0 + (ja - nkt);
+        } else {
+            ls.kt = cs.kt + nkt - 1;
+        }
+        const int bl = b + kAhead >= kRing ? b + kAhead - kRing : b + kAhead;
+        const int bn = b + 1 >= kRing ? 0 : b + 1;
+        stage<BM, BN, WM, WN, A_INS, B_INS>(ra, ls, ring0 + (uint32_t)bl * kStageBytes, KB, wv, lane16,
+                                            &ring.st[b], &ring.st[bn], wm, wn, lane, fa, fb, acc);
+        b = bn;
+    } while (++j < nkt);
+}
+
+// Source row of slot r of a tile's A rows: token perm[p] (gate/up) or the
+// sorted position p itself (down); rows past the segment end are clamped to
+// its last row (their results are never stored).
+template <bool GATE_UP>
+__device__ __forceinline__ int row_src(const int32_t* perm, const Tile& t, int r)
+{
+    const int p = t.row0 + min(r, t.rows - 1);
+    return GATE_UP ? perm[p] : p;
 }
 
 template <int BM, int BN, int WM, int WN, bool GATE_UP>
@@ -294,48 +398,67 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 {
     constexpr int WAVES_N = BN / WN;
     constexpr int MI = WM / 32, NI = WN / 32;
-    constexpr int A_INS = BM * kCH / 64 / 4;      // A direct-load instructions per wave per stage
+    constexpr int A_INS = BM * kCH / 64 / 4;      // A loads per wave per stage
     constexpr int B_INS = (BN / 32) * 2 / 4;      // weight blocks per wave per stage
+    constexpr int NLD = A_INS + B_INS;
     static_assert((BM / WM) * WAVES_N == kThreads / kWave, "4 waves");
     static_assert(A_INS * 4 * 16 == BM && B_INS * 4 == (BN / 32) * 2, "stage split over 4 waves");
     static_assert(!GATE_UP || (NI % 2 == 0 && WN % 64 == 0), "gate/up pairs per wave");
+    static_assert(sizeof(Ring<BM, BN>) <= 160 * 1024, "LDS");
 
-    __shared__ Stage<BM, BN> st0, st1, st2, st3;
-    __shared__ Tile s_tile;
+    __shared__ Ring<BM, BN> ring;
 
     const int N = GATE_UP ? 2 * g.f : g.d;  // weight rows per expert
     const int K = GATE_UP ? g.d : g.f;
     const int NT = N / BN;
-    const int KB = K / 16;                 // 16-wide k blocks per weight row block
-
-    if (threadIdx.x < kWave)
-        find_tile<BM>(g.offsets, g.E, NT, g.group_n, g.xcd_remap, &s_tile);
-    __syncthreads();
-    if (!s_tile.valid)
-        return;
-    const int e = s_tile.e, mt = s_tile.m, nt = s_tile.n;
-    const int seg0 = g.offsets[e];
-    const int row0 = seg0 + mt * BM;
-    const int rows = min(BM, g.offsets[e + 1] - row0);
-
+    const int KB = K / 16;   // 16-wide k blocks per weight row block
+    const int KT = K / kBK;  // K stages (a multiple of 4, at least 4)
+    const int S = GATE_UP ? 1 : g.split;
     const int lane = threadIdx.x % kWave;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int wm = wv / WAVES_N, wn = wv % WAVES_N;
 
-    // A: per-lane source offsets (elements) of this wave's 16-row groups. Rows
-    // are gathered through perm for gate/up; rows past the segment end are
-    // clamped to its last row (their results are never stored).
-    const uint16_t* A = (const uint16_t*)g.a;
-    uint32_t aoff[A_INS];
+    TileTable tt;
+    const int total = make_table<BM>(g.offsets, g.E, lane, tt) * NT * S;
+    int L = blockIdx.x;
+    if (L >= total)
+        return;
+    const int G = gridDim.x;
+
+    // Per-lane slot rows and swizzled chunk byte offsets of this wave's A loads.
+    const uint32_t Kbytes = (uint32_t)K * 2u;
+    int slot[A_INS];
+    uint32_t cpart[A_INS];
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
-        const int r = (wv * A_INS + i) * 16 + lane / 4;  // slot lane of this instruction
-        const int p = row0 + min(r, rows - 1);
-        const int src = GATE_UP ? g.perm[p] : p;
-        aoff[i] = (uint32_t)src * (uint32_t)K + (uint32_t)(swz(r, lane % 4) * 8);
+        slot[i] = (wv * A_INS + i) * 16 + lane / 4;
+        cpart[i] = (uint32_t)swz(slot[i], lane % 4) * 16u;
     }
-    // B: this lane's slot in the tile's first weight block.
-    const Vec16* bsrc = (const Vec16*)g.b + ((int64_t)e * (N / 32) + (int64_t)nt * (BN / 32)) * KB * 64 + lane;
+    const uint32_t a_rows = GATE_UP ? (uint32_t)(g.A_max / g.k) : (uint32_t)g.A_max;
+    const i32x4 ra = make_rsrc(g.a, a_rows * Kbytes);
+    const uint32_t lane16 = (uint32_t)lane * 16u;
+
+    Tile cur = decode<BM>(tt, L, NT, S, g.group_n, KT);
+    LoadSrc<A_INS> cs;
+    cs.rb = panel_rsrc<BN>(g.b, cur, N, KB);
+    cs.kt = cur.kt0;
+#pragma unroll
+    for (int i = 0; i < A_INS; ++i)
+        cs.aoff[i] = (uint32_t)row_src<GATE_UP>(g.perm, cur, slot[i]) * Kbytes + cpart[i];
+    bool has_nxt = L + G < total;
+    Tile nxt = cur;
+    i32x4 nrb = cs.rb;
+    uint32_t held[A_INS];
+#pragma unroll
+    for (int i = 0; i < A_INS; ++i)
+        held[i] = 0;
+    if (has_nxt) {
+        nxt = decode<BM>(tt, L + G, NT, S, g.group_n, KT);
+        nrb = panel_rsrc<BN>(g.b, nxt, N, KB);
+#pragma unroll
+        for (int i = 0; i < A_INS; ++i)
+            held[i] = (uint32_t)row_src<GATE_UP>(g.perm, nxt, slot[i]);
+    }
 
     floatx16 acc[MI][NI];
 #pragma unroll
@@ -346,59 +469,158 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             for (int q = 0; q < 16; ++q)
                 acc[i][j][q] = 0.f;
 
-    const int KT = K / kBK;  // a multiple of 4 (K % 128 == 0)
-    const StageLoader<BM, BN, A_INS, B_INS> ld{A, aoff, bsrc, KB, wv};
-    if (rows == BM)
-        tile_k_loop<BM, BN, WM, WN, A_INS, B_INS, false>(ld, KT, &st0, &st1, &st2, &st3, wm, wn, lane, MI, acc);
-    else
-        tile_k_loop<BM, BN, WM, WN, A_INS, B_INS, true>(ld, KT, &st0, &st1, &st2, &st3, wm, wn, lane,
-                                                        min(MI, max(0, (rows - wm * WM + 31) / 32)), acc);
+    // Prologue: the first kAhead stages of the stream (all of the first tile,
+    // which has at least kAhead stages), then the k step 0 fragments of the
+    // first one.
+    const uint32_t ring0 = lds_addr(&ring);
+    constexpr uint32_t kStageBytes = sizeof(Stage<BM, BN>);
+#pragma unroll
+    for (int p = 0; p < kAhead; ++p) {
+        LoadSrc<A_INS> ls = cs;
+        ls.kt = cs.kt + p;
+#pragma unroll
+        for (int q = 0; q < NLD; ++q)
+            issue_load<BM, BN, A_INS, B_INS>(q, ra, ls, KB, wv, lane16, ring0 + (uint32_t)p * kStageBytes);
+    }
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kAhead - 1) * NLD) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    bf16x8 fa[MI], fb[NI];
+    {
+        const FragReader<BM, BN, WM, WN> r0{&ring.st[0], wm, wn, lane};
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+            fb[j] = r0.b(0, j);
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+            fa[i] = r0.a(0, i);
+    }
+    int b = 0;
 
-    // Epilogue. 32x32 accumulator layout: lane holds column lane%32 and, for
-    // q = 0..15, row 8*(q/4) + 4*(lane/32) + q%4.
-    if constexpr (GATE_UP) {
-        uint16_t* H = (uint16_t*)g.out;
+    for (;;) {
+        tile_stages<BM, BN, WM, WN, A_INS, B_INS>(ra, cs, cur.nkt, has_nxt, nrb, nxt.kt0, cpart, Kbytes, KB, wv,
+                                                  lane16, ring, ring0, b, wm, wn, lane, fa, fb, held, acc);
+
+        // The tile after next: decode it and fetch its token rows now, so the
+        // fetch overlaps the epilogue. Its first use is pinned after the
+        // epilogue (below); loads complete in issue order, so the wait the
+        // compiler puts there also covers the loads of the next tile's first
+        // stages, which have had the whole epilogue to land.
+        const bool has_nn = has_nxt && L + 2 * G < total;
+        Tile nn = nxt;
+        i32x4 nnrb = nrb;
+        uint32_t nheld[A_INS];
 #pragma unroll
-        for (int i = 0; i < MI; ++i) {
+        for (int i = 0; i < A_INS; ++i)
+            nheld[i] = held[i];
+        if (has_nn) {
+            nn = decode<BM>(tt, L + 2 * G, NT, S, g.group_n, KT);
+            nnrb = panel_rsrc<BN>(g.b, nn, N, KB);
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int r = wm * WM + i * 32 + 8 * (q / 4) + 4 * (lane >> 5) + (q % 4);
-                if (r >= rows)
-                    continue;
-                uint16_t* hrow = H + (int64_t)(row0 + r) * g.f;
+            for (int i = 0; i < A_INS; ++i)
+                nheld[i] = (uint32_t)row_src<GATE_UP>(g.perm, nn, slot[i]);
+        }
+
+        // Epilogue of the tile. 32x32 accumulator layout: lane holds column
+        // lane%32 and, for q = 0..15, row 8*(q/4) + 4*(lane/32) + q%4. Rows
+        // past the segment end were computed from the clamped last row, so
+        // their results equal that row's: they are stored to it again (same
+        // values), which keeps the epilogue free of branches. The lane's row
+        // base goes through an opaque move so that the row and address
+        // arithmetic is not hoisted out of the tile loop.
+        int rbase = wm * WM + 4 * (lane >> 5);
+        asm volatile("" : "+v"(rbase));
+        if constexpr (GATE_UP) {
+            // Through LDS, one (32-row group, gate/up block pair) at a time:
+            // the accumulators go from AGPRs straight into this wave's 8 KiB
+            // of the ring slot the tile's last stage used (free until the
+            // next stage refills it, after the barrier below), as fp32 rows of
+            // 32 with the 16-byte chunk index XORed with row%8 (conflict-free
+            // writes and reads); each lane then reads back 16 consecutive
+            // gate and up values of one row, applies SiLU(g)*u and stores 16
+            // bf16 of H with two 16-byte stores.
+            static_assert(BN == 256 && WN == 128 && NI == 4, "gate/up epilogue layout");
+            const int bfree = b == 0 ? kRing - 1 : b - 1;
+            float* ep = (float*)&ring.st[bfree] + wv * 2048;
+            const int wr = 8 * 0 + 4 * (lane >> 5);  // row of q = 0 inside the 32-row group
+            const int wc = lane & 31;
+            const int rr = lane >> 1;                  // row read back by this lane
+            const int rc = (lane & 1) * 4;             // first 16-byte chunk read back
+            uint16_t* H = (uint16_t*)g.out;
 #pragma unroll
-                for (int j = 0; j < NI; j += 2) {
-                    const int wrow = nt * BN + wn * WN + j * 32;  // first gate row of the pair
-                    const int col = wrow / 2 + (lane & 31);
-                    const float gv = acc[i][j][q], uv = acc[i][j + 1][q];
-                    hrow[col] = f32_to_bf16_bits(silu(gv) * uv);
+            for (int i = 0; i < MI; ++i) {
+#pragma unroll
+                for (int jp = 0; jp < NI; jp += 2) {
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) {
+                        const int r = wr + 8 * (q / 4) + (q % 4);
+                        const int o = r * 32 + (((wc >> 2) ^ (r & 7)) << 2) + (wc & 3);
+                        ep[o] = acc[i][jp][q];
+                        ep[1024 + o] = acc[i][jp + 1][q];
+                    }
+                    uint32_t hv[8];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int o = rr * 32 + (((rc + t) ^ (rr & 7)) << 2);
+                        const floatx4 gv = *(const floatx4*)(ep + o);
+                        const floatx4 uv = *(const floatx4*)(ep + 1024 + o);
+                        hv[2 * t] = (uint32_t)f32_to_bf16_bits(silu_rcp(gv[0]) * uv[0]) |
+                                    ((uint32_t)f32_to_bf16_bits(silu_rcp(gv[1]) * uv[1]) << 16);
+                        hv[2 * t + 1] = (uint32_t)f32_to_bf16_bits(silu_rcp(gv[2]) * uv[2]) |
+                                        ((uint32_t)f32_to_bf16_bits(silu_rcp(gv[3]) * uv[3]) << 16);
+                    }
+                    const int row = min(rbase - 4 * (lane >> 5) + i * 32 + rr, cur.rows - 1);
+                    const int col = (cur.n * BN + wn * WN + jp * 32) / 2 + rc * 4;
+                    Vec16* dst = (Vec16*)(H + (int64_t)(cur.row0 + row) * g.f + col);
+                    dst[0] = Vec16{hv[0], hv[1], hv[2], hv[3]};
+                    dst[1] = Vec16{hv[4], hv[5], hv[6], hv[7]};
+                }
+            }
+            // Every wave is done with the slot before the next stage loads it.
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        } else {
+            float* Ys = (float*)g.out + (int64_t)cur.s * g.A_max * g.d;
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int r = min(rbase + i * 32 + 8 * (q / 4) + (q % 4), cur.rows - 1);
+                    float* yrow = Ys + (int64_t)(cur.row0 + r) * g.d + cur.n * BN + wn * WN + (lane & 31);
+#pragma unroll
+                    for (int j = 0; j < NI; ++j)
+                        yrow[j * 32] = acc[i][j][q];
                 }
             }
         }
-    } else {
-        float* Ys = (float*)g.out;
 #pragma unroll
-        for (int i = 0; i < MI; ++i) {
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int r = wm * WM + i * 32 + 8 * (q / 4) + 4 * (lane >> 5) + (q % 4);
-                if (r >= rows)
-                    continue;
-                const int p = row0 + r;
-                float* yrow = Ys + ((int64_t)g.perm[p] * g.k + g.perm_slot[p]) * g.d;
+            for (int j = 0; j < NI; ++j)
 #pragma unroll
-                for (int j = 0; j < NI; ++j)
-                    yrow[nt * BN + wn * WN + j * 32 + (lane & 31)] = acc[i][j][q];
-            }
-        }
-    }
-}
+                for (int q = 0; q < 16; ++q)
+                    acc[i][j][q] = 0.f;
+        if constexpr (GATE_UP)
+            asm volatile("" : "+v"(nheld[0]), "+v"(nheld[1]), "+v"(nheld[2]), "+v"(nheld[3]) : : "memory");
+        if (!has_nxt)
+            break;
 
-template <int BM>
-int m_tile_bound(int A_max, int E)
-{
-    // sum_e ceil(c_e / BM) <= floor(A / BM) + E  for sum_e c_e = A
-    return A_max / BM + E;
+        // Switch to the next tile; its loads are already in flight.
+        cur = nxt;
+        cs.rb = nrb;
+        cs.kt = cur.kt0;
+#pragma unroll
+        for (int i = 0; i < A_INS; ++i)
+            cs.aoff[i] = held[i] * Kbytes + cpart[i];
+        L += G;
+        has_nxt = has_nn;
+        nxt = nn;
+        nrb = nnrb;
+#pragma unroll
+        for (int i = 0; i < A_INS; ++i)
+            held[i] = nheld[i];
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the trailing reloads
 }
 
 // Init-time weight repack into the blocked MFMA operand layout: for expert e,
@@ -455,21 +677,41 @@ __global__ void interleave_gate_up_kernel(const uint8_t* wg, const uint8_t* wu, 
 }  // namespace
 
 // Tile shapes: 256x256 output tiles, 4 waves of 128x128 (256 fp32 accumulators
-// per lane, held in AGPRs), 2 x 32 KiB LDS stages of A. When the weight-row
-// count is not a multiple of 256, 256x128 tiles (waves of 128x64) are used.
+// per lane, held in AGPRs), a ring of 5 x 32 KiB LDS stages. When the
+// weight-row count is not a multiple of 256 (down GEMM with d_model % 256 ==
+// 128), 256x128 tiles (waves of 128x64, 5 x 24 KiB stages).
 constexpr int kBM = 256;
+
+int down_split_bf16(int A, int E, int d, int f, int cus)
+{
+    // Split K in two when the down GEMM has fewer than three tiles per compute
+    // unit: whole-tile rounds then waste much of the last round, and halves
+    // fill it better at the price of one more fp32 partial for combine to read.
+    const int BN = d % 256 == 0 ? 256 : 128;
+    const int64_t tiles = ((int64_t)A / kBM + E) * (d / BN);
+    const int KT = f / kBK;
+    return (KT >= 16 && tiles < 3 * (int64_t)cus) ? 2 : 1;
+}
 
 template <bool GATE_UP>
 hipError_t launch_grouped(const GemmArgs& a, hipStream_t s)
 {
     const int N = GATE_UP ? 2 * a.f : a.d;
-    const int mt = m_tile_bound<kBM>(a.A_max, a.E);
-    if (N % 256 == 0)
-        hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 256, 128, 128, GATE_UP>), dim3(mt * (N / 256)),
-                           dim3(kThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 128, 128, 64, GATE_UP>), dim3(mt * (N / 128)),
-                           dim3(kThreads), 0, s, a);
+    const int S = GATE_UP ? 1 : a.split;
+    const int BN = N % 256 == 0 ? 256 : 128;
+    const int64_t bound = ((int64_t)a.A_max / kBM + a.E) * (N / BN) * S;  // tiles, upper bound
+    const int grid = (int)(bound < a.grid ? bound : a.grid);
+    if (grid <= 0)
+        return hipSuccess;
+    if constexpr (GATE_UP) {
+        // 2 * d_ff is a multiple of 256 (d_ff % 128 == 0 is checked at init)
+        hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 256, 128, 128, true>), dim3(grid), dim3(kThreads), 0, s, a);
+    } else {
+        if (BN == 256)
+            hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 256, 128, 128, false>), dim3(grid), dim3(kThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 128, 128, 64, false>), dim3(grid), dim3(kThreads), 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_f32_kernel(GemmArgs g)
             for (int j = 0; j < 4; ++j)
                 out[(int64_t)p * g.f + col0 + tx * 4 + j] = silu(ag[i][j]) * au[i][j];
         } else {
-            float* yrow = out + ((int64_t)g.perm[p] * g.k + g.perm_slot[p]) * g.d;
+            float* yrow = out + (int64_t)p * g.d;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 yrow[col0 + tx * 4 + j] = ag[i][j];

@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdlib>
+#include <algorithm>
 #include <mutex>
 #include <new>
 #include <unordered_set>
@@ -56,6 +57,8 @@ struct colibri_moe {
     hipEvent_t ev[kStages + 1];
     int group_n;    // tile order of the grouped GEMMs (n-tiles per group)
     int cus;        // compute units of the device (persistent GEMM grid)
+    int dec_max_a;  // bf16 calls with T*k <= dec_max_a take the small-batch path
+    int dec_split_gu, dec_split_dn;  // its K slices (gate/up, down)
 };
 
 namespace {
@@ -160,8 +163,15 @@ colibri_moe_status_t init_impl(colibri_moe* h, const colibri_moe_weights_t* w)
     const size_t o_ps = cv.take(A * sizeof(int32_t));
     const size_t o_inv = cv.take(A * sizeof(int32_t));
     const size_t o_h = cv.take(A * f * es);
-    const size_t n_ys = c.dtype == COLIBRI_MOE_BF16 ? (size_t)cmoe::kMaxSplit : 1;
-    const size_t o_ys = cv.take(n_ys * A * d * sizeof(float));
+    // Ys: the down GEMM's partial sums (kMaxSplit for bf16), and on the
+    // small-batch path also the gate/up slice partials before SiLU.
+    size_t ys_floats = (c.dtype == COLIBRI_MOE_BF16 ? (size_t)cmoe::kMaxSplit : 1) * A * d;
+    if (c.dtype == COLIBRI_MOE_BF16 && h->dec_max_a > 0) {
+        const size_t ad = (size_t)h->dec_max_a;
+        ys_floats = std::max(ys_floats, (size_t)h->dec_split_gu * ad * 2 * f);
+        ys_floats = std::max(ys_floats, (size_t)h->dec_split_dn * ad * d);
+    }
+    const size_t o_ys = cv.take(ys_floats * sizeof(float));
     h->arena_bytes = cv.off;
 
     if (hipMalloc(&h->arena, h->arena_bytes) != hipSuccess) {
@@ -242,6 +252,18 @@ colibri_moe_status_t colibri_moe_init(colibri_moe_t** out, const colibri_moe_con
         release(h);
         return COLIBRI_MOE_ERR_HIP;
     }
+    // Small-batch path (bf16): calls with at most CMOE_DECODE_MAX_A
+    // assignments (default 256; 0 turns the path off). Results do not depend
+    // on the path beyond fp32 summation order.
+    h->dec_max_a = 0;
+    h->dec_split_gu = h->dec_split_dn = 1;
+    if (cfg->dtype == COLIBRI_MOE_BF16) {
+        const int64_t amax = (int64_t)cfg->max_tokens * cfg->top_k;
+        h->dec_max_a = (int)std::min<int64_t>(amax, env_int("CMOE_DECODE_MAX_A", 256, 0, 1 << 16));
+        const int waves = cmoe::decode_waves(h->cus);
+        h->dec_split_gu = cmoe::decode_split(cfg->n_experts, 2 * cfg->d_ff, cfg->d_model, waves, 64);
+        h->dec_split_dn = cmoe::decode_split(cfg->n_experts, cfg->d_model, cfg->d_ff, waves, 64);
+    }
     st = init_impl(h, w);
     if (st != COLIBRI_MOE_OK) {
         release(h);
@@ -303,15 +325,28 @@ colibri_moe_status_t colibri_moe_forward(colibri_moe_t* h, const void* x, int32_
         CMOE_HIP(hipEventRecord(h->ev[2], s));
 
     const int A = T * c.top_k;
-    GemmArgs gu{x, h->w_gu, h->H, offsets, perm, A, c.n_experts, c.top_k, c.d_model, c.d_ff, h->group_n, 1, h->cus};
-    CMOE_HIP(bf ? launch_gate_up_bf16(gu, s) : launch_gate_up_f32(gu, s));
-    if (tm)
-        CMOE_HIP(hipEventRecord(h->ev[3], s));
-
-    const int split = bf ? down_split_bf16(A, c.n_experts, c.d_model, c.d_ff, h->cus) : 1;
-    GemmArgs dn{h->H, h->w_d, h->Ys, offsets, perm, A, c.n_experts, c.top_k, c.d_model, c.d_ff, h->group_n, split,
-                h->cus};
-    CMOE_HIP(bf ? launch_down_bf16(dn, s) : launch_down_f32(dn, s));
+    int split = 1;
+    if (bf && A <= h->dec_max_a) {
+        // small-batch path: weight streaming with K slices
+        DecodeArgs gu{x, h->w_gu, h->Ys, offsets, perm, A, c.n_experts, c.d_model, c.d_ff, h->dec_split_gu};
+        CMOE_HIP(launch_decode_gemm(gu, 1, h->cus, s));
+        CMOE_HIP(launch_decode_silu(h->Ys, h->H, A, c.d_ff, h->dec_split_gu, s));
+        if (tm)
+            CMOE_HIP(hipEventRecord(h->ev[3], s));
+        DecodeArgs dn{h->H, h->w_d, h->Ys, offsets, perm, A, c.n_experts, c.d_model, c.d_ff, h->dec_split_dn};
+        CMOE_HIP(launch_decode_gemm(dn, 0, h->cus, s));
+        split = h->dec_split_dn;
+    } else {
+        GemmArgs gu{x, h->w_gu, h->H, offsets, perm, A, c.n_experts, c.top_k, c.d_model, c.d_ff, h->group_n, 1,
+                    h->cus};
+        CMOE_HIP(bf ? launch_gate_up_bf16(gu, s) : launch_gate_up_f32(gu, s));
+        if (tm)
+            CMOE_HIP(hipEventRecord(h->ev[3], s));
+        split = bf ? down_split_bf16(A, c.n_experts, c.d_model, c.d_ff, h->cus) : 1;
+        GemmArgs dn{h->H, h->w_d, h->Ys, offsets, perm, A, c.n_experts, c.top_k, c.d_model, c.d_ff, h->group_n,
+                    split, h->cus};
+        CMOE_HIP(bf ? launch_down_bf16(dn, s) : launch_down_f32(dn, s));
+    }
     if (tm)
         CMOE_HIP(hipEventRecord(h->ev[4], s));
 

@@ -3,6 +3,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 namespace cmoe {
@@ -96,6 +98,25 @@ constexpr int kMaxSplit = 2;
 int down_split_bf16(int A, int E, int d, int f, int cus);
 hipError_t launch_gate_up_f32(const GemmArgs& a, hipStream_t s);
 hipError_t launch_down_f32(const GemmArgs& a, hipStream_t s);
+
+// Small-batch (decode) path of the bf16 expert GEMMs (decode_bf16.hip).
+struct DecodeArgs {
+    const void* a;            // gate/up: x [T][d] (rows through perm); down: H [A][f]
+    const void* b;            // blocked bf16 weights (as in the grouped GEMMs)
+    float* part;              // fp32 slice partials [split][A][N], N = 2f (gate/up) or d (down)
+    const int32_t* offsets;   // [E+1]
+    const int32_t* perm;      // [A]
+    int A;                    // T*k of this call
+    int E, d, f;
+    int split;                // K slices
+};
+// Waves a decode launch runs on `cus` compute units.
+int decode_waves(int cus);
+// K slices for an (E experts, N weight rows, K) decode GEMM on `waves` waves.
+int decode_split(int E, int N, int K, int waves, int max_split);
+hipError_t launch_decode_gemm(const DecodeArgs& a, int gate_up, int cus, hipStream_t s);
+// H = SiLU(sum of gate slices) * (sum of up slices), bf16.
+hipError_t launch_decode_silu(const float* part, void* H, int A, int f, int S, hipStream_t s);
 
 struct CombineArgs {
     const float* ys;    // split partials, each [A][d] fp32 by sorted position

@@ -1,0 +1,183 @@
+// decode_bf16.hip - expert GEMMs of bf16 layers for small token counts.
+//
+// The same two expert GEMMs as gemm_bf16.hip (the per-expert SwiGLU FFN of
+// «Colibri 是什么» (xxqk.cn) §2.3, batched over the active experts as in
+// «Colibri不是一只蜂鸟» (discosf.com) §3.2), for steps where every active expert
+// holds only a few tokens, as when generating one token per sequence. There the
+// work is reading each active expert's weights once: the MFMA work is tiny, and
+// a 256-row output tile would spend most of its matrix time on rows that do not
+// exist. So this path has no LDS and no barriers at all:
+//   - a work item is (expert e, 32-row weight block nb, K slice s); every wave
+//     takes items w, w + W, ... (W = waves in the grid) on its own;
+//   - for each 32-token group of the expert it multiplies the tokens' K slice
+//     (A fragments, through perm for gate/up) with the weight block (B
+//     fragments, fetched straight into registers from the blocked MFMA layout)
+//     with v_mfma_f32_32x32x16_bf16, P k-steps of loads in flight ahead of the
+//     MFMAs (plain loads, so the compiler's wait counts are exact);
+//   - it writes the fp32 partial sum of its slice: P[s][p][nb*32 + j].
+// K slices split every expert's weights into many equal, independent items,
+// which keeps all compute units streaming. For gate/up a second kernel sums
+// the slices and applies SiLU(g)*u into H; for down the slices are the Ys
+// partials that combine already sums.
+#include "common.hpp"
+
+namespace cmoe {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kP = 8;  // k-steps of loads in flight per wave
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_gemm_kernel(
+    DecodeArgs g, int gate_up)
+{
+    const int lane = threadIdx.x % kWave;
+    const int W = gridDim.x * (kThreads / kWave);
+    const int w0 = blockIdx.x * (kThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int N = gate_up ? 2 * g.f : g.d;
+    const int K = gate_up ? g.d : g.f;
+    const int NB = N / 32, KB = K / 16, S = g.split;
+    const int items = g.E * NB * S;
+    const Vec16* B = (const Vec16*)g.b;
+    const uint16_t* Abase = (const uint16_t*)g.a;
+
+    for (int it = w0; it < items; it += W) {
+        const int s = it % S;
+        const int rest = it / S;
+        const int nb = rest % NB;
+        const int e = rest / NB;
+        const int seg0 = g.offsets[e];
+        const int cnt = g.offsets[e + 1] - seg0;
+        if (cnt <= 0)
+            continue;
+        const int kb0 = (int)((int64_t)s * KB / S), kb1 = (int)((int64_t)(s + 1) * KB / S);
+        // Weight block (nb, kb) of expert e: 1 KiB, lane l's 16 bytes at l.
+        const Vec16* bp = B + ((int64_t)e * NB + nb) * KB * kWave + lane;
+        float* out = g.part + (int64_t)s * g.A * N + nb * 32 + (lane & 31);
+
+        for (int r0 = 0; r0 < cnt; r0 += 32) {
+            // A fragment rows: token row r0 + lane%32 of the segment (clamped;
+            // rows past the end repeat the last one and are not stored),
+            // k = kb*16 + 8*(lane/32) .. +8.
+            const int r = min(r0 + (lane & 31), cnt - 1);
+            const int src = gate_up ? g.perm[seg0 + r] : seg0 + r;
+            const Vec16* ap = (const Vec16*)(Abase + (int64_t)src * K) + (lane >> 5);
+
+            floatx16 acc;
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                acc[q] = 0.f;
+            Vec16 a0[kP], b0[kP], a1[kP], b1[kP];
+            // Loads past the slice end are clamped to its last k-step (valid
+            // addresses); their MFMAs are skipped.
+#pragma unroll
+            for (int i = 0; i < kP; ++i) {
+                const int kb = min(kb0 + i, kb1 - 1);
+                a0[i] = ap[kb * 2];
+                b0[i] = bp[(int64_t)kb * kWave];
+            }
+            for (int kb = kb0; kb < kb1; kb += 2 * kP) {
+#pragma unroll
+                for (int i = 0; i < kP; ++i) {
+                    const int kk = min(kb + kP + i, kb1 - 1);
+                    a1[i] = ap[kk * 2];
+                    b1[i] = bp[(int64_t)kk * kWave];
+                }
+#pragma unroll
+                for (int i = 0; i < kP; ++i)
+                    if (kb + i < kb1)
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0[i]), as_bf16x8(b0[i]), acc, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < kP; ++i) {
+                    const int kk = min(kb + 2 * kP + i, kb1 - 1);
+                    a0[i] = ap[kk * 2];
+                    b0[i] = bp[(int64_t)kk * kWave];
+                }
+#pragma unroll
+                for (int i = 0; i < kP; ++i)
+                    if (kb + kP + i < kb1)
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1[i]), as_bf16x8(b1[i]), acc, 0, 0, 0);
+            }
+            // Accumulator layout: lane holds weight row nb*32 + lane%32 and,
+            // for q = 0..15, token row 8*(q/4) + 4*(lane/32) + q%4 of the group.
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int row = r0 + 8 * (q / 4) + 4 * (lane >> 5) + (q % 4);
+                if (row < cnt)
+                    out[(int64_t)(seg0 + row) * N] = acc[q];
+            }
+        }
+    }
+}
+
+// H[p][c] = bf16(SiLU(sum_s P[s][p][gate row of c]) * sum_s P[s][p][up row of c]),
+// with gate/up interleaved by 32 rows: h column c is gate row (c/32)*64 + c%32
+// and up row (c/32)*64 + 32 + c%32 of the combined [2f] weight rows. Four
+// consecutive columns per thread, slices summed in order.
+__global__ __launch_bounds__(256) void decode_silu_kernel(const float* part, uint16_t* H, int A, int f, int S)
+{
+    const int64_t groups = (int64_t)A * (f / 4);
+    const int64_t sstride = (int64_t)A * 2 * f;
+    for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < groups;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t p = idx / (f / 4);
+        const int c = (int)(idx % (f / 4)) * 4;
+        const int n = (c / 32) * 64 + (c % 32);
+        const float* gp = part + p * 2 * f + n;
+        float4 gs = *(const float4*)gp;
+        float4 us = *(const float4*)(gp + 32);
+        for (int s = 1; s < S; ++s) {
+            const float4 a = *(const float4*)(gp + s * sstride);
+            const float4 b = *(const float4*)(gp + s * sstride + 32);
+            gs.x += a.x;
+            gs.y += a.y;
+            gs.z += a.z;
+            gs.w += a.w;
+            us.x += b.x;
+            us.y += b.y;
+            us.z += b.z;
+            us.w += b.w;
+        }
+        uint2 packed;
+        packed.x = (uint32_t)f32_to_bf16_bits(silu(gs.x) * us.x) | ((uint32_t)f32_to_bf16_bits(silu(gs.y) * us.y) << 16);
+        packed.y = (uint32_t)f32_to_bf16_bits(silu(gs.z) * us.z) | ((uint32_t)f32_to_bf16_bits(silu(gs.w) * us.w) << 16);
+        *(uint2*)(H + p * f + c) = packed;
+    }
+}
+
+}  // namespace
+
+int decode_waves(int cus)
+{
+    return cus * 2 * (kThreads / kWave);
+}
+
+int decode_split(int E, int N, int K, int waves, int max_split)
+{
+    // Enough K slices for about eight items per wave, at least four k-steps each.
+    const int64_t blocks = (int64_t)E * (N / 32);
+    int64_t s = (8 * (int64_t)waves + blocks - 1) / blocks;
+    const int64_t cap = std::min<int64_t>(max_split, std::max(1, K / 16 / 4));
+    s = std::max<int64_t>(1, std::min(s, cap));
+    return (int)s;
+}
+
+hipError_t launch_decode_gemm(const DecodeArgs& a, int gate_up, int cus, hipStream_t s)
+{
+    hipLaunchKernelGGL(decode_gemm_kernel, dim3(cus * 2), dim3(kThreads), 0, s, a, gate_up);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_silu(const float* part, void* H, int A, int f, int S, hipStream_t s)
+{
+    const int64_t groups = (int64_t)A * (f / 4);
+    int64_t blocks = (groups + 255) / 256;
+    if (blocks > 4096)
+        blocks = 4096;
+    if (blocks < 1)
+        return hipSuccess;
+    hipLaunchKernelGGL(decode_silu_kernel, dim3((unsigned)blocks), dim3(256), 0, s, part, (uint16_t*)H, A, f, S);
+    return hipGetLastError();
+}
+
+}  // namespace cmoe

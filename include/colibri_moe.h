@@ -124,8 +124,10 @@ const char* colibri_moe_status_string(colibri_moe_status_t s);
 
 /* Stage names and GPU times (ms) of the last forward when the handle was
  * created with COLIBRI_MOE_FLAG_STAGE_TIMING (waits for that forward to
- * finish). Stages: 0 router, 1 dispatch, 2 gate/up GEMM, 3 down GEMM,
- * 4 combine. Writes min(n, 5) values; returns the number of stages. */
+ * finish). Stages: 0 router, 1 dispatch, 2 gate/up GEMM, 3 gate/up reduce
+ * (the K-slice sum and SiLU of the small-batch path; empty otherwise),
+ * 4 down GEMM, 5 combine. Writes min(n, 6) values; returns the number of
+ * stages. */
 int32_t colibri_moe_stage_times(colibri_moe_t* h, float* ms, int32_t n);
 const char* colibri_moe_stage_name(int32_t stage);
 

@@ -18,7 +18,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_OUT_OF_MEMORY, ERR_HIP 
 F32, BF16 = 0, 1
 FLAG_ASYNC = 1 << 0
 FLAG_STAGE_TIMING = 1 << 1
-STAGES = ("router", "dispatch", "gate_up_gemm", "down_gemm", "combine")
+STAGES = ("router", "dispatch", "gate_up_gemm", "gate_up_reduce", "down_gemm", "combine")
 
 
 class Config(ctypes.Structure):

@@ -23,10 +23,11 @@ using namespace cmoe;
 namespace {
 
 constexpr uint32_t kMagic = 0xC011B41Eu;
-constexpr int kStages = 5;
+constexpr int kStages = 6;
 constexpr int32_t kMaxTokensLimit = 1 << 24;
 
-const char* const kStageNames[kStages] = {"router", "dispatch", "gate_up_gemm", "down_gemm", "combine"};
+const char* const kStageNames[kStages] = {"router",         "dispatch",  "gate_up_gemm",
+                                          "gate_up_reduce", "down_gemm", "combine"};
 
 }  // namespace
 
@@ -327,12 +328,15 @@ colibri_moe_status_t colibri_moe_forward(colibri_moe_t* h, const void* x, int32_
     const int A = T * c.top_k;
     int split = 1;
     if (bf && A <= h->dec_max_a) {
-        // small-batch path: weight streaming with K slices
+        // small-batch path: weight streaming with K slices, then the slice sum
+        // and SiLU(g)*u
         DecodeArgs gu{x, h->w_gu, h->Ys, offsets, perm, A, c.n_experts, c.d_model, c.d_ff, h->dec_split_gu};
         CMOE_HIP(launch_decode_gemm(gu, 1, h->cus, s));
-        CMOE_HIP(launch_decode_silu(h->Ys, h->H, A, c.d_ff, h->dec_split_gu, s));
         if (tm)
             CMOE_HIP(hipEventRecord(h->ev[3], s));
+        CMOE_HIP(launch_decode_silu(h->Ys, h->H, A, c.d_ff, h->dec_split_gu, s));
+        if (tm)
+            CMOE_HIP(hipEventRecord(h->ev[4], s));
         DecodeArgs dn{h->H, h->w_d, h->Ys, offsets, perm, A, c.n_experts, c.d_model, c.d_ff, h->dec_split_dn};
         CMOE_HIP(launch_decode_gemm(dn, 0, h->cus, s));
         split = h->dec_split_dn;
@@ -340,20 +344,22 @@ colibri_moe_status_t colibri_moe_forward(colibri_moe_t* h, const void* x, int32_
         GemmArgs gu{x, h->w_gu, h->H, offsets, perm, A, c.n_experts, c.top_k, c.d_model, c.d_ff, h->group_n, 1,
                     h->cus};
         CMOE_HIP(bf ? launch_gate_up_bf16(gu, s) : launch_gate_up_f32(gu, s));
-        if (tm)
+        if (tm) {
             CMOE_HIP(hipEventRecord(h->ev[3], s));
+            CMOE_HIP(hipEventRecord(h->ev[4], s));  // no separate reduce on this path
+        }
         split = bf ? down_split_bf16(A, c.n_experts, c.d_model, c.d_ff, h->cus) : 1;
         GemmArgs dn{h->H, h->w_d, h->Ys, offsets, perm, A, c.n_experts, c.top_k, c.d_model, c.d_ff, h->group_n,
                     split, h->cus};
         CMOE_HIP(bf ? launch_down_bf16(dn, s) : launch_down_f32(dn, s));
     }
     if (tm)
-        CMOE_HIP(hipEventRecord(h->ev[4], s));
+        CMOE_HIP(hipEventRecord(h->ev[5], s));
 
     CombineArgs ca{h->Ys, inv, topw, y, T, c.top_k, c.d_model, split, bf ? 1 : 0};
     CMOE_HIP(launch_combine(ca, s));
     if (tm)
-        CMOE_HIP(hipEventRecord(h->ev[5], s));
+        CMOE_HIP(hipEventRecord(h->ev[6], s));
 
     if (!(c.flags & COLIBRI_MOE_FLAG_ASYNC))
         CMOE_HIP(hipStreamSynchronize(s));

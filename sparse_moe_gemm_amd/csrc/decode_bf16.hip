@@ -7,14 +7,16 @@
 // work is reading each active expert's weights once: the MFMA work is tiny, and
 // a 256-row output tile would spend most of its matrix time on rows that do not
 // exist. So this path has no LDS and no barriers at all:
-//   - a work item is (expert e, 32-row weight block nb, K slice s); every wave
-//     takes items w, w + W, ... (W = waves in the grid) on its own;
+//   - a work item is (expert e, two 32-row weight blocks nb and nb+1, K
+//     slice s); every wave takes items w, w + W, ... (W = waves in the grid)
+//     on its own;
 //   - for each 32-token group of the expert it multiplies the tokens' K slice
-//     (A fragments, through perm for gate/up) with the weight block (B
-//     fragments, fetched straight into registers from the blocked MFMA layout)
-//     with v_mfma_f32_32x32x16_bf16, P k-steps of loads in flight ahead of the
-//     MFMAs (plain loads, so the compiler's wait counts are exact);
-//   - it writes the fp32 partial sum of its slice: P[s][p][nb*32 + j].
+//     (A fragments, through perm for gate/up; each one feeds both blocks)
+//     with the two weight blocks (B fragments, fetched straight into
+//     registers from the blocked MFMA layout) with v_mfma_f32_32x32x16_bf16,
+//     P k-steps of loads in flight ahead of the MFMAs (plain loads, so the
+//     compiler's wait counts are exact);
+//   - it writes the fp32 partial sums of its slice: P[s][p][nb*32 + j].
 // K slices split every expert's weights into many equal, independent items,
 // which keeps all compute units streaming. For gate/up a second kernel sums
 // the slices and applies SiLU(g)*u into H; for down the slices are the Ys
@@ -26,55 +28,52 @@ namespace cmoe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kP = 8;  // k-steps of loads in flight per wave
+constexpr int kP = 6;  // k-steps of loads in flight per wave
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_gemm_kernel(
-    DecodeArgs g, int gate_up)
+template <bool GATE_UP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_gemm_kernel(DecodeArgs g)
 {
+    constexpr bool gate_up = GATE_UP;
     const int lane = threadIdx.x % kWave;
     const int W = gridDim.x * (kThreads / kWave);
     const int w0 = blockIdx.x * (kThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int N = gate_up ? 2 * g.f : g.d;
     const int K = gate_up ? g.d : g.f;
     const int NB = N / 32, KB = K / 16, S = g.split;
-    const int items = g.E * NB * S;
+    const int NB2 = NB / 2;  // items cover two weight blocks
+    const int items = g.E * NB2 * S;
     const Vec16* B = (const Vec16*)g.b;
     const uint16_t* Abase = (const uint16_t*)g.a;
 
     for (int it = w0; it < items; it += W) {
         const int s = it % S;
         const int rest = it / S;
-        const int nb = rest % NB;
-        const int e = rest / NB;
+        const int nb = (rest % NB2) * 2;
+        const int e = rest / NB2;
         const int seg0 = g.offsets[e];
         const int cnt = g.offsets[e + 1] - seg0;
         if (cnt <= 0)
             continue;
         const int kb0 = (int)((int64_t)s * KB / S), kb1 = (int)((int64_t)(s + 1) * KB / S);
-        // Weight block (nb, kb) of expert e: 1 KiB, lane l's 16 bytes at l.
         const Vec16* bp = B + ((int64_t)e * NB + nb) * KB * kWave + lane;
+        const int64_t bst = (int64_t)KB * kWave;  // next weight block
         float* out = g.part + (int64_t)s * g.A * N + nb * 32 + (lane & 31);
 
         for (int r0 = 0; r0 < cnt; r0 += 32) {
-            // A fragment rows: token row r0 + lane%32 of the segment (clamped;
-            // rows past the end repeat the last one and are not stored),
-            // k = kb*16 + 8*(lane/32) .. +8.
             const int r = min(r0 + (lane & 31), cnt - 1);
             const int src = gate_up ? g.perm[seg0 + r] : seg0 + r;
             const Vec16* ap = (const Vec16*)(Abase + (int64_t)src * K) + (lane >> 5);
-
-            floatx16 acc;
+            floatx16 acc0, acc1;
 #pragma unroll
             for (int q = 0; q < 16; ++q)
-                acc[q] = 0.f;
-            Vec16 a0[kP], b0[kP], a1[kP], b1[kP];
-            // Loads past the slice end are clamped to its last k-step (valid
-            // addresses); their MFMAs are skipped.
+                acc0[q] = acc1[q] = 0.f;
+            Vec16 a0[kP], b0[kP], c0[kP], a1[kP], b1[kP], c1[kP];
 #pragma unroll
             for (int i = 0; i < kP; ++i) {
                 const int kb = min(kb0 + i, kb1 - 1);
                 a0[i] = ap[kb * 2];
                 b0[i] = bp[(int64_t)kb * kWave];
+                c0[i] = bp[bst + (int64_t)kb * kWave];
             }
             for (int kb = kb0; kb < kb1; kb += 2 * kP) {
 #pragma unroll
@@ -82,29 +81,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                     const int kk = min(kb + kP + i, kb1 - 1);
                     a1[i] = ap[kk * 2];
                     b1[i] = bp[(int64_t)kk * kWave];
+                    c1[i] = bp[bst + (int64_t)kk * kWave];
                 }
 #pragma unroll
                 for (int i = 0; i < kP; ++i)
-                    if (kb + i < kb1)
-                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0[i]), as_bf16x8(b0[i]), acc, 0, 0, 0);
+                    if (kb + i < kb1) {
+                        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0[i]), as_bf16x8(b0[i]), acc0, 0, 0, 0);
+                        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0[i]), as_bf16x8(c0[i]), acc1, 0, 0, 0);
+                    }
 #pragma unroll
                 for (int i = 0; i < kP; ++i) {
                     const int kk = min(kb + 2 * kP + i, kb1 - 1);
                     a0[i] = ap[kk * 2];
                     b0[i] = bp[(int64_t)kk * kWave];
+                    c0[i] = bp[bst + (int64_t)kk * kWave];
                 }
 #pragma unroll
                 for (int i = 0; i < kP; ++i)
-                    if (kb + kP + i < kb1)
-                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1[i]), as_bf16x8(b1[i]), acc, 0, 0, 0);
+                    if (kb + kP + i < kb1) {
+                        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1[i]), as_bf16x8(b1[i]), acc0, 0, 0, 0);
+                        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1[i]), as_bf16x8(c1[i]), acc1, 0, 0, 0);
+                    }
             }
-            // Accumulator layout: lane holds weight row nb*32 + lane%32 and,
-            // for q = 0..15, token row 8*(q/4) + 4*(lane/32) + q%4 of the group.
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
                 const int row = r0 + 8 * (q / 4) + 4 * (lane >> 5) + (q % 4);
-                if (row < cnt)
-                    out[(int64_t)(seg0 + row) * N] = acc[q];
+                if (row < cnt) {
+                    out[(int64_t)(seg0 + row) * N] = acc0[q];
+                    out[(int64_t)(seg0 + row) * N + 32] = acc1[q];
+                }
             }
         }
     }
@@ -154,8 +159,9 @@ int decode_waves(int cus)
 
 int decode_split(int E, int N, int K, int waves, int max_split)
 {
-    // Enough K slices for about eight items per wave, at least four k-steps each.
-    const int64_t blocks = (int64_t)E * (N / 32);
+    // Enough K slices for about eight items (of two 32-row blocks) per wave, at
+    // least four k-steps each.
+    const int64_t blocks = (int64_t)E * (N / 64);
     int64_t s = (8 * (int64_t)waves + blocks - 1) / blocks;
     const int64_t cap = std::min<int64_t>(max_split, std::max(1, K / 16 / 4));
     s = std::max<int64_t>(1, std::min(s, cap));
@@ -164,7 +170,10 @@ int decode_split(int E, int N, int K, int waves, int max_split)
 
 hipError_t launch_decode_gemm(const DecodeArgs& a, int gate_up, int cus, hipStream_t s)
 {
-    hipLaunchKernelGGL(decode_gemm_kernel, dim3(cus * 2), dim3(kThreads), 0, s, a, gate_up);
+    if (gate_up)
+        hipLaunchKernelGGL(decode_gemm_kernel<true>, dim3(cus * 2), dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL(decode_gemm_kernel<false>, dim3(cus * 2), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -36,8 +36,8 @@ def test_status_strings_and_stage_names():
     texts = {cm.colibri_moe_status_string(s) for s in range(6)}
     assert len(texts) == 6
     assert cm.colibri_moe_status_string(99) == "unknown status"
-    assert [cm.colibri_moe_stage_name(i) for i in range(5)] == list(cm.STAGES)
-    assert cm.colibri_moe_stage_name(5) is None
+    assert [cm.colibri_moe_stage_name(i) for i in range(6)] == list(cm.STAGES)
+    assert cm.colibri_moe_stage_name(6) is None
 
 
 def _cfg(**kw):

@@ -61,11 +61,15 @@ def lib():
             "moe_oracle_dispatch": [P, i32, i32, i32, P, P, P, P, P],
             "moe_oracle_expert_ffn": [LP, i32, P, P, P],
             "moe_oracle_forward": [LP, P, i32, P, P, i32, P, P],
+            "moe_oracle_quantize_fp8": [P, ctypes.c_int, i64, i64, P, P],
+            "moe_oracle_dequantize_fp8": [P, P, i64, i64, P],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
             fn.restype = ctypes.c_int
             fn.argtypes = args
+        L.moe_oracle_fp8_value.restype = ctypes.c_double
+        L.moe_oracle_fp8_value.argtypes = [ctypes.c_uint8]
         _lib = L
     return _lib
 
@@ -213,3 +217,42 @@ def boundary_tie_tokens(logits, k: int, rel: float = 1e-5) -> np.ndarray:
     s = -np.sort(-lg, axis=1).astype(np.float64)
     a, b = s[:, k - 1], s[:, k]
     return (a - b) < rel * np.maximum(np.abs(a), np.abs(b))
+
+
+def quantize_fp8(w) -> tuple:
+    """8-bit expert weights (reading in moe_oracle.h): w [rows][cols] (bf16 bits
+    as uint16, or float32) -> (codes uint8 [rows][cols], scales float32 [rows])."""
+    w = np.ascontiguousarray(w)
+    rows, cols = w.shape[0], int(np.prod(w.shape[1:]))
+    codes = np.empty((rows, cols), dtype=np.uint8)
+    scales = np.empty(rows, dtype=np.float32)
+    _check(lib().moe_oracle_quantize_fp8(_ptr(w), _dtype_code(w), rows, cols, _ptr(codes), _ptr(scales)),
+           "quantize_fp8")
+    return codes.reshape(w.shape), scales
+
+
+def dequantize_fp8(codes, scales) -> np.ndarray:
+    """codes [rows][...] uint8, scales [rows] -> bf16 bit patterns (uint16), exact."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    rows, cols = codes.shape[0], int(np.prod(codes.shape[1:]))
+    out = np.empty(codes.shape, dtype=np.uint16)
+    _check(lib().moe_oracle_dequantize_fp8(_ptr(codes), _ptr(scales), rows, cols, _ptr(out)), "dequantize_fp8")
+    return out
+
+
+def fp8_value(code: int) -> float:
+    return float(lib().moe_oracle_fp8_value(code))
+
+
+def quantized_expert_weights(inp: dict) -> dict:
+    """The layer's inputs with every expert weight matrix replaced by its 8-bit
+    quantized-and-dequantized value (per expert, per output row); router and x
+    unchanged. Running the ordinary layer on these is the 8-bit layer."""
+    out = dict(inp)
+    for name in ("w_gate", "w_up", "w_down"):
+        w = inp[name]
+        E, rows, cols = w.shape
+        codes, scales = quantize_fp8(w.reshape(E * rows, cols))
+        out[name] = dequantize_fp8(codes, scales).reshape(E, rows, cols)
+    return out

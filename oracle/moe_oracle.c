@@ -298,3 +298,105 @@ int moe_oracle_forward(const moe_oracle_layer_t* L, const void* x, int32_t T,
     }
     return err;
 }
+
+/* ------------------------------------------------------------------------ */
+/* 8-bit expert weights: OCP FP8 E4M3 codes with one power-of-two scale per
+ * weight row (the reading stated in moe_oracle.h). Written from the format's
+ * definition: value = (-1)^s * 2^(E-7) * (1 + m/8) for E > 0, and
+ * (-1)^s * 2^-6 * (m/8) for E = 0. */
+
+double moe_oracle_fp8_value(uint8_t code)
+{
+    const int s = code >> 7, E = (code >> 3) & 15, m = code & 7;
+    if (E == 15 && m == 7)
+        return NAN;
+    const double v = (E == 0) ? ldexp((double)m, -9) : ldexp(8.0 + m, E - 10);
+    return s ? -v : v;
+}
+
+/* Nearest integer to x >= 0, ties to even. */
+static double round_half_even(double x)
+{
+    const double f = floor(x);
+    const double r = x - f;
+    if (r > 0.5)
+        return f + 1.0;
+    if (r < 0.5)
+        return f;
+    return (fmod(f, 2.0) == 0.0) ? f : f + 1.0;
+}
+
+/* E4M3 code of v, |v| <= 448, ties to even. */
+static uint8_t fp8_encode(double v)
+{
+    const int neg = signbit(v) ? 1 : 0;
+    const double a = fabs(v);
+    int E, m;
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal range: steps of 2^-9; a count of 8 is the smallest normal */
+        const int q = (int)round_half_even(ldexp(a, 9));
+        E = q >> 3;
+        m = q & 7;
+    } else {
+        int x;
+        (void)frexp(a, &x); /* a = f * 2^x, f in [0.5, 1): exponent of a is x-1 */
+        E = x - 1 + 7;
+        const double frac = ldexp(a, -(x - 1)) - 1.0; /* in [0, 1) */
+        m = (int)round_half_even(frac * 8.0);
+        if (m == 8) {
+            m = 0;
+            E += 1;
+        }
+    }
+    return (uint8_t)((neg << 7) | (E << 3) | m);
+}
+
+int moe_oracle_quantize_fp8(const void* w, int dtype, int64_t rows, int64_t cols,
+                            uint8_t* codes, float* scales)
+{
+    if (!w || !codes || !scales || rows <= 0 || cols <= 0)
+        return -1;
+    if (dtype != MOE_ORACLE_F32 && dtype != MOE_ORACLE_BF16)
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        double amax = 0.0;
+        for (int64_t i = 0; i < cols; ++i) {
+            const double a = fabs(elem(w, dtype, r * cols + i));
+            if (a > amax)
+                amax = a;
+        }
+        int e = 0;
+        if (amax > 0.0) {
+            int x;
+            const double f = frexp(amax, &x); /* amax = f * 2^x, f in [0.5, 1) */
+            /* 448 = 0.875 * 2^9: amax <= 448 * 2^e  <=>  f * 2^(x-9-e) <= 0.875 */
+            e = (f <= 0.875) ? x - 9 : x - 8;
+            if (e < -126)
+                e = -126;
+        }
+        scales[r] = (float)ldexp(1.0, e);
+        for (int64_t i = 0; i < cols; ++i)
+            codes[r * cols + i] = fp8_encode(ldexp(elem(w, dtype, r * cols + i), -e));
+    }
+    return 0;
+}
+
+int moe_oracle_dequantize_fp8(const uint8_t* codes, const float* scales, int64_t rows,
+                              int64_t cols, uint16_t* bf16_out)
+{
+    if (!codes || !scales || !bf16_out || rows <= 0 || cols <= 0)
+        return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t i = 0; i < cols; ++i) {
+            const double v = moe_oracle_fp8_value(codes[r * cols + i]) * (double)scales[r];
+            const float f = (float)v;
+            uint32_t u;
+            memcpy(&u, &f, 4);
+            if ((double)f != v || (u & 0xFFFFu) != 0)
+                return -2;
+            bf16_out[r * cols + i] = (uint16_t)(u >> 16);
+        }
+    }
+    return 0;
+}

@@ -96,6 +96,30 @@ int moe_oracle_forward(const moe_oracle_layer_t* L, const void* x, int32_t T,
                        const int32_t* forced_ids, const int32_t* token_list, int32_t n,
                        double* y, double* Y_slots);
 
+/* 8-bit expert weights («Colibri 是什么» (xxqk.cn) §4.2: the model converter can
+ * quantize only the expert FFN weights, with 8 bits, keeping the router in full
+ * precision). The pages fix neither the 8-bit format nor the scaling; the
+ * reading implemented here:
+ *   - format: OCP FP8 E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa
+ *     bits; largest finite 448; 0x7f/0xff are NaN and never produced);
+ *   - one scale per weight row (per output unit), a power of two 2^e with the
+ *     smallest integer e such that max_i |w[r][i]| <= 448 * 2^e (e = 0 for an
+ *     all-zero row; never below -126), so w * 2^-e is exact;
+ *   - code = w * 2^-e rounded to the nearest E4M3 value, ties to the even
+ *     mantissa; values below half the smallest subnormal (2^-10) give a
+ *     signed zero (the sign bit follows the sign of w, -0 included).
+ * The quantized layer is the same layer with every expert weight replaced by
+ * its dequantized value code * 2^e, which a bf16 tensor holds exactly.
+ * quantize: w [rows][cols] (dtype) -> codes [rows][cols], scales [rows] (2^e).
+ * dequantize: codes, scales -> bf16 bit patterns; fails (returns -2) if a value
+ * is not exactly representable in bf16. */
+int moe_oracle_quantize_fp8(const void* w, int dtype, int64_t rows, int64_t cols,
+                            uint8_t* codes, float* scales);
+int moe_oracle_dequantize_fp8(const uint8_t* codes, const float* scales, int64_t rows,
+                              int64_t cols, uint16_t* bf16_out);
+/* Value of one E4M3 code (NaN for 0x7f/0xff). */
+double moe_oracle_fp8_value(uint8_t code);
+
 #ifdef __cplusplus
 }
 #endif

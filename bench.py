@@ -9,7 +9,11 @@ Prints one JSON line with the throughput (tokens/s), the roofline position of
 the dominant kernel (measured live with HIP events on the layer's stream), and
 the CPU oracle timed on a bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--fp8-weights] [--no-cpu-baseline]
+
+--fp8-weights builds the layer with 8-bit expert weights (E4M3 codes, one
+power-of-two scale per weight row, converted to bf16 in registers): same bf16
+arithmetic, half the expert weight bytes.
 """
 from __future__ import annotations
 
@@ -45,6 +49,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--fp8-weights", action="store_true",
+                    help="8-bit expert weights (bf16 workloads only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens of the oracle sample (0 = sized to ~15 s of CPU work)")
@@ -81,10 +87,15 @@ def gemm_flops_per_assignment(cfg):
     return {"gate_up_gemm": 4.0 * cfg.d * cfg.f, "down_gemm": 2.0 * cfg.d * cfg.f}
 
 
-def active_weight_bytes(cfg, counts, stage):
-    es = cfg.elem_bytes()
+def active_weight_bytes(cfg, counts, stage, fp8=False):
+    """Bytes of the active experts' weights of one GEMM (fp8: codes plus one
+    fp32 scale per weight row)."""
     n_active = int((counts > 0).sum())
-    per = {"gate_up_gemm": 2 * cfg.d * cfg.f * es, "down_gemm": cfg.d * cfg.f * es}[stage]
+    if fp8:
+        per = {"gate_up_gemm": 2 * cfg.f * (cfg.d + 4), "down_gemm": cfg.d * (cfg.f + 4)}[stage]
+    else:
+        es = cfg.elem_bytes()
+        per = {"gate_up_gemm": 2 * cfg.d * cfg.f * es, "down_gemm": cfg.d * cfg.f * es}[stage]
     return n_active * per
 
 
@@ -114,12 +125,14 @@ def profiled_traffic(workload: str, kernel: str):
         return None
 
 
-def cpu_baseline(cfg, inp, sample_tokens: int):
+def cpu_baseline(cfg, inp, sample_tokens: int, fp8: bool = False):
     import oracle
 
     gomp = ctypes.CDLL("libgomp.so.1")
     threads = int(gomp.omp_get_max_threads())
-    L = oracle.Layer.from_inputs(inp, cfg.k)
+    # fp8: the oracle's 8-bit layer is its ordinary layer on the dequantized
+    # weights (quantized here, outside the timed part, as the library does at init)
+    L = oracle.Layer.from_inputs(oracle.quantized_expert_weights(inp) if fp8 else inp, cfg.k)
     x = inp["x"]
     per_tok_macs = cfg.d * cfg.E + 3 * cfg.d * cfg.f * cfg.k
     if sample_tokens <= 0:
@@ -158,13 +171,17 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     cfg = synth.CONFIGS[args.workload]
+    if args.fp8_weights and cfg.dtype != "bf16":
+        print("--fp8-weights needs a bf16 workload", file=sys.stderr)
+        sys.exit(2)
+    fp8 = bool(args.fp8_weights)
     t_gen = time.perf_counter()
     inp = synth.make_inputs(cfg)
     t_gen = time.perf_counter() - t_gen
 
     layer = cm.MoELayer(to_dev(inp["w_router"]), to_dev(inp["b_router"]), to_dev(inp["w_gate"]),
                         to_dev(inp["w_up"]), to_dev(inp["w_down"]), cfg.k, max_tokens=cfg.T,
-                        flags=cm.FLAG_ASYNC | cm.FLAG_STAGE_TIMING)
+                        flags=cm.FLAG_ASYNC | cm.FLAG_STAGE_TIMING | (cm.FLAG_FP8_WEIGHTS if fp8 else 0))
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     x = to_dev(inp["x"])
@@ -212,18 +229,19 @@ def main():
     # The library takes its small-batch (weight streaming) path for bf16 calls
     # with at most CMOE_DECODE_MAX_A (default 256) assignments.
     small_batch = cfg.dtype == "bf16" and A <= int(os.environ.get("CMOE_DECODE_MAX_A", "256"))
+    prof_key = args.workload + ("-fp8" if fp8 else "")
     if small_batch:
         # weight streaming bound: algorithmic bytes = the active experts' gate
         # and up weights, read once
-        achieved = active_weight_bytes(cfg, counts, dom) / (stage_ms[dom] * 1e-3) / 1e9
+        achieved = active_weight_bytes(cfg, counts, dom, fp8) / (stage_ms[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "traffic": profiled_traffic(args.workload, dom),
-                "kernel": "decode_gemm_kernel<true> (gate/up)"}
+                "frac": achieved / PEAK_HBM_GBS, "traffic": profiled_traffic(prof_key, dom),
+                "kernel": "decode_gemm_f8_kernel<true> (gate/up)" if fp8 else "decode_gemm_kernel<true> (gate/up)"}
     else:
         achieved = fpa[dom] * A / (stage_ms[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak_mm, "unit": "TFLOP/s",
-                "frac": achieved / peak_mm, "traffic": profiled_traffic(args.workload, dom),
-                "kernel": "grouped_gemm_kernel<256,256,128,128,true> (gate/up)"}
+                "frac": achieved / peak_mm, "traffic": profiled_traffic(prof_key, dom),
+                "kernel": f"grouped_gemm_kernel<256,256,128,128,true,{str(fp8).lower()}> (gate/up)"}
 
     out = {
         "metric": METRIC,
@@ -238,8 +256,10 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic (seeded SplitMix64 + Box-Muller, bf16 RNE; no trained weights)",
-        "config": {"workload": WORKLOAD_NAMES[args.workload], "T": cfg.T, "d_model": cfg.d,
-                   "n_experts": cfg.E, "top_k": cfg.k, "d_ff": cfg.f, "router_bias": cfg.bias or None},
+        "config": {"workload": WORKLOAD_NAMES[args.workload] + ("-fp8-weights" if fp8 else ""), "T": cfg.T,
+                   "d_model": cfg.d, "n_experts": cfg.E, "top_k": cfg.k, "d_ff": cfg.f,
+                   "router_bias": cfg.bias or None,
+                   "expert_weights": "fp8-e4m3, per-row power-of-two scale" if fp8 else cfg.dtype},
         "roofline": roof,
         "layer_tflops": layer_tflops,
         "layer_mfma_frac": layer_tflops / peak_mm,
@@ -249,7 +269,7 @@ def main():
         "input_gen_s": t_gen,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens)
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens, fp8)
     print(json.dumps(out), flush=True)
 
 

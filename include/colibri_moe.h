@@ -38,6 +38,19 @@
  *    is set, in which case it returns after enqueueing. A handle serves one
  *    stream; calls on one handle must not overlap.
  *  - On a non-OK return, outputs are undefined.
+ *
+ * 8-bit expert weights (COLIBRI_MOE_FLAG_FP8_WEIGHTS, bf16 layers only): the
+ * pages' converter may store the expert FFN weights alone in 8 bits while the
+ * router keeps full precision («Colibri 是什么» (xxqk.cn) §4.2). The pages fix
+ * no format; this library uses OCP FP8 E4M3 codes with one power-of-two scale
+ * per weight row (per output unit of the gate, up and down projections):
+ * scale = 2^e with the smallest integer e (>= -126) such that the row's
+ * largest magnitude is at most 448 * 2^e (e = 0 for an all-zero row), code =
+ * w / scale rounded to the nearest E4M3 value, ties to even mantissa, zero
+ * keeping the sign. Init quantizes the bf16 weights it is given; forward then
+ * computes the layer of the dequantized weights (code value * scale, exact in
+ * bf16) with bf16 activations and fp32 accumulation, reading half the weight
+ * bytes of the bf16 layer.
  */
 #ifndef COLIBRI_MOE_H
 #define COLIBRI_MOE_H
@@ -53,8 +66,9 @@ typedef enum {
     COLIBRI_MOE_ERR_INVALID_ARG = 1,  /* null where required, T < 0 or > max_tokens, k < 1 or > E, bad dtype */
     COLIBRI_MOE_ERR_UNSUPPORTED = 2,  /* d_model not a multiple of 128, d_ff not a multiple of 128
                                          (bf16) or 64 (f32), E > 256, k > 8, max_tokens > 2^24,
-                                         or max_tokens*k*d_ff, max_tokens*d_model or
-                                         2*d_ff*d_model reaching 2^31 */
+                                         max_tokens*k*d_ff, max_tokens*d_model or
+                                         2*d_ff*d_model reaching 2^31, or FP8_WEIGHTS with
+                                         dtype F32 */
     COLIBRI_MOE_ERR_ALIGNMENT = 3,    /* a tensor pointer not 16-byte aligned */
     COLIBRI_MOE_ERR_OUT_OF_MEMORY = 4,/* init could not allocate its memory */
     COLIBRI_MOE_ERR_HIP = 5           /* a HIP launch, copy or sync failed */
@@ -64,7 +78,9 @@ typedef enum { COLIBRI_MOE_F32 = 0, COLIBRI_MOE_BF16 = 1 } colibri_moe_dtype_t;
 
 enum {
     COLIBRI_MOE_FLAG_ASYNC = 1u << 0,       /* forward returns after enqueueing */
-    COLIBRI_MOE_FLAG_STAGE_TIMING = 1u << 1 /* record per-stage GPU times (hipEvents) */
+    COLIBRI_MOE_FLAG_STAGE_TIMING = 1u << 1, /* record per-stage GPU times (hipEvents) */
+    COLIBRI_MOE_FLAG_FP8_WEIGHTS = 1u << 2   /* bf16 only: keep expert weights as 8-bit codes
+                                                (format above) */
 };
 
 typedef struct {
@@ -118,6 +134,18 @@ colibri_moe_status_t colibri_moe_forward(colibri_moe_t* h, const void* x, int32_
  * free reject a pointer that is not a live handle (never created, or already
  * freed) with INVALID_ARG instead of touching it. */
 colibri_moe_status_t colibri_moe_free(colibri_moe_t* h);
+
+/* The 8-bit codes init stores for bf16 weight rows under
+ * COLIBRI_MOE_FLAG_FP8_WEIGHTS (format in the header comment; «Colibri 是什么»
+ * (xxqk.cn) §4.2), row-major: for w [rows][cols] bf16, codes [rows][cols]
+ * E4M3 bytes and scales [rows] fp32 (powers of two), so that w[r][c] is
+ * approximated by value(codes[r][c]) * scales[r]. All three are caller-owned
+ * DEVICE buffers; w must be 16-byte and codes 8-byte aligned. rows >= 1,
+ * cols >= 8 and a multiple of 8, rows * cols < 2^40; otherwise INVALID_ARG.
+ * Runs on hip_stream (NULL = default stream) and returns when it is done.
+ * Needs no handle. */
+colibri_moe_status_t colibri_moe_quantize_fp8(const void* w, int64_t rows, int64_t cols, uint8_t* codes,
+                                              float* scales, void* hip_stream);
 
 /* Static text for a status value. */
 const char* colibri_moe_status_string(colibri_moe_status_t s);

@@ -18,6 +18,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_OUT_OF_MEMORY, ERR_HIP 
 F32, BF16 = 0, 1
 FLAG_ASYNC = 1 << 0
 FLAG_STAGE_TIMING = 1 << 1
+FLAG_FP8_WEIGHTS = 1 << 2
 STAGES = ("router", "dispatch", "gate_up_gemm", "gate_up_reduce", "down_gemm", "combine")
 
 
@@ -39,7 +40,7 @@ class Routing(ctypes.Structure):
 
 
 EXPORTS = ("colibri_moe_init", "colibri_moe_forward", "colibri_moe_free", "colibri_moe_status_string",
-           "colibri_moe_stage_times", "colibri_moe_stage_name")
+           "colibri_moe_stage_times", "colibri_moe_stage_name", "colibri_moe_quantize_fp8")
 
 _lib = None
 
@@ -65,6 +66,8 @@ def lib() -> ctypes.CDLL:
         L.colibri_moe_stage_times.argtypes = [P, ctypes.POINTER(ctypes.c_float), i32]
         L.colibri_moe_stage_name.restype = ctypes.c_char_p
         L.colibri_moe_stage_name.argtypes = [i32]
+        L.colibri_moe_quantize_fp8.restype = ctypes.c_int
+        L.colibri_moe_quantize_fp8.argtypes = [P, ctypes.c_int64, ctypes.c_int64, P, P, P]
         _lib = L
     return _lib
 
@@ -103,6 +106,30 @@ def colibri_moe_stage_times(handle) -> list:
 def colibri_moe_stage_name(stage: int):
     s = lib().colibri_moe_stage_name(stage)
     return None if s is None else s.decode()
+
+
+def colibri_moe_quantize_fp8(w_ptr: int, rows: int, cols: int, codes_ptr: int, scales_ptr: int,
+                             hip_stream: int = 0) -> int:
+    return lib().colibri_moe_quantize_fp8(ctypes.c_void_p(w_ptr), rows, cols, ctypes.c_void_p(codes_ptr),
+                                          ctypes.c_void_p(scales_ptr), ctypes.c_void_p(hip_stream))
+
+
+def quantize_fp8(w, stream=None):
+    """(codes uint8 [rows][cols], scales fp32 [rows]) of a contiguous bf16
+    device tensor [rows][cols]: the 8-bit codes a layer built with
+    FLAG_FP8_WEIGHTS keeps."""
+    import torch
+
+    if w.dtype != torch.bfloat16 or w.dim() != 2 or not w.is_cuda or not w.is_contiguous():
+        raise TypeError("w must be a contiguous 2-D bfloat16 device tensor")
+    rows, cols = w.shape
+    codes = torch.empty(rows, cols, dtype=torch.uint8, device=w.device)
+    scales = torch.empty(rows, dtype=torch.float32, device=w.device)
+    s = stream if stream is not None else torch.cuda.current_stream()
+    st = colibri_moe_quantize_fp8(w.data_ptr(), rows, cols, codes.data_ptr(), scales.data_ptr(), s.cuda_stream)
+    if st != OK:
+        raise ColibriError("colibri_moe_quantize_fp8", st)
+    return codes, scales
 
 
 class ColibriError(RuntimeError):

@@ -42,8 +42,12 @@ struct colibri_moe {
     // weights (library copies, repacked)
     void* w_rt;   // [E][d]
     float* b_r;   // [E]
-    void* w_gu;   // [E][2f][d], gate/up interleaved by 32 rows (bf16: blocked MFMA layout)
-    void* w_d;    // [E][d][f] (bf16: blocked MFMA layout)
+    void* w_gu;   // [E][2f][d], gate/up interleaved by 32 rows (bf16: blocked MFMA layout;
+                  // fp8: E4M3 codes in the fp8 blocked layout)
+    void* w_d;    // [E][d][f] (bf16: blocked MFMA layout; fp8: as w_gu)
+    float* s_gu;  // fp8 row scales [E][2f] (interleaved rows), else null
+    float* s_d;   // fp8 row scales [E][d], else null
+    bool fp8;
     // workspace, sized for max_tokens
     float* topw;
     int32_t* ids;
@@ -119,6 +123,8 @@ colibri_moe_status_t validate_config(const colibri_moe_config_t* c)
         return COLIBRI_MOE_ERR_UNSUPPORTED;
     if (c->max_tokens > kMaxTokensLimit)
         return COLIBRI_MOE_ERR_UNSUPPORTED;
+    if ((c->flags & COLIBRI_MOE_FLAG_FP8_WEIGHTS) && c->dtype != COLIBRI_MOE_BF16)
+        return COLIBRI_MOE_ERR_UNSUPPORTED;
     // GEMM source offsets are 32-bit element offsets.
     const int64_t lim = (int64_t)1 << 31;
     if ((int64_t)c->max_tokens * c->d_model >= lim || (int64_t)c->max_tokens * c->top_k * c->d_ff >= lim ||
@@ -154,8 +160,11 @@ colibri_moe_status_t init_impl(colibri_moe* h, const colibri_moe_weights_t* w)
     Carver cv;
     const size_t o_wrt = cv.take(E * d * es);
     const size_t o_br = cv.take(E * sizeof(float));
-    const size_t o_wgu = cv.take(E * 2 * f * d * es);
-    const size_t o_wd = cv.take(E * d * f * es);
+    const size_t wes = h->fp8 ? 1 : es;  // bytes per stored expert weight
+    const size_t o_wgu = cv.take(E * 2 * f * d * wes);
+    const size_t o_wd = cv.take(E * d * f * wes);
+    const size_t o_sgu = h->fp8 ? cv.take(E * 2 * f * sizeof(float)) : 0;
+    const size_t o_sd = h->fp8 ? cv.take(E * d * sizeof(float)) : 0;
     const size_t o_topw = cv.take(A * sizeof(float));
     const size_t o_ids = cv.take(A * sizeof(int32_t));
     const size_t o_cnt = cv.take(E * sizeof(int32_t));
@@ -185,6 +194,8 @@ colibri_moe_status_t init_impl(colibri_moe* h, const colibri_moe_weights_t* w)
     h->b_r = (float*)(base + o_br);
     h->w_gu = base + o_wgu;
     h->w_d = base + o_wd;
+    h->s_gu = h->fp8 ? (float*)(base + o_sgu) : nullptr;
+    h->s_d = h->fp8 ? (float*)(base + o_sd) : nullptr;
     h->topw = (float*)(base + o_topw);
     h->ids = (int32_t*)(base + o_ids);
     h->counts = (int32_t*)(base + o_cnt);
@@ -201,7 +212,14 @@ colibri_moe_status_t init_impl(colibri_moe* h, const colibri_moe_weights_t* w)
         CMOE_HIP(hipMemcpyAsync(h->b_r, w->b_router, E * sizeof(float), hipMemcpyDeviceToDevice, s));
     else
         CMOE_HIP(hipMemsetAsync(h->b_r, 0, E * sizeof(float), s));
-    if (c.dtype == COLIBRI_MOE_BF16) {
+    if (h->fp8) {
+        // row scales, then E4M3 codes in the fp8 blocked layout (gate/up
+        // interleaved by 32 rows, scales in the interleaved row order)
+        CMOE_HIP(launch_fp8_row_scales(w->w_gate, w->w_up, h->s_gu, (int64_t)E * 2 * f, (int)(2 * f), (int)d, s));
+        CMOE_HIP(launch_fp8_row_scales(w->w_down, nullptr, h->s_d, (int64_t)E * d, (int)d, (int)f, s));
+        CMOE_HIP(launch_fp8_pack_blocked(w->w_gate, w->w_up, h->s_gu, h->w_gu, (int)E, (int)(2 * f), (int)d, s));
+        CMOE_HIP(launch_fp8_pack_blocked(w->w_down, nullptr, h->s_d, h->w_d, (int)E, (int)d, (int)f, s));
+    } else if (c.dtype == COLIBRI_MOE_BF16) {
         // blocked MFMA operand layout (gate/up interleaved by 32 rows)
         CMOE_HIP(launch_pack_blocked(w->w_gate, w->w_up, h->w_gu, (int)E, (int)(2 * f), (int)d, 1, s));
         CMOE_HIP(launch_pack_blocked(w->w_down, nullptr, h->w_d, (int)E, (int)d, (int)f, 0, s));
@@ -243,6 +261,7 @@ colibri_moe_status_t colibri_moe_init(colibri_moe_t** out, const colibri_moe_con
     h->stream = (hipStream_t)hip_stream;
     h->esize = cfg->dtype == COLIBRI_MOE_BF16 ? 2 : 4;
     h->timing = (cfg->flags & COLIBRI_MOE_FLAG_STAGE_TIMING) != 0;
+    h->fp8 = (cfg->flags & COLIBRI_MOE_FLAG_FP8_WEIGHTS) != 0;
     // Tile order of the grouped GEMMs (tuning only; results do not depend
     // on it): CMOE_GROUP_N n-tiles per group.
     h->group_n = env_int("CMOE_GROUP_N", 64, 1, 1 << 20);
@@ -262,8 +281,9 @@ colibri_moe_status_t colibri_moe_init(colibri_moe_t** out, const colibri_moe_con
         const int64_t amax = (int64_t)cfg->max_tokens * cfg->top_k;
         h->dec_max_a = (int)std::min<int64_t>(amax, env_int("CMOE_DECODE_MAX_A", 256, 0, 1 << 16));
         const int waves = cmoe::decode_waves(h->cus);
-        h->dec_split_gu = cmoe::decode_split(cfg->n_experts, 2 * cfg->d_ff, cfg->d_model, waves, 64);
-        h->dec_split_dn = cmoe::decode_split(cfg->n_experts, cfg->d_model, cfg->d_ff, waves, 64);
+        const int kstep = h->fp8 ? 32 : 16;
+        h->dec_split_gu = cmoe::decode_split(cfg->n_experts, 2 * cfg->d_ff, cfg->d_model, kstep, waves, 64);
+        h->dec_split_dn = cmoe::decode_split(cfg->n_experts, cfg->d_model, cfg->d_ff, kstep, waves, 64);
     }
     st = init_impl(h, w);
     if (st != COLIBRI_MOE_OK) {
@@ -330,27 +350,29 @@ colibri_moe_status_t colibri_moe_forward(colibri_moe_t* h, const void* x, int32_
     if (bf && A <= h->dec_max_a) {
         // small-batch path: weight streaming with K slices, then the slice sum
         // and SiLU(g)*u
-        DecodeArgs gu{x, h->w_gu, h->Ys, offsets, perm, A, c.n_experts, c.d_model, c.d_ff, h->dec_split_gu};
+        DecodeArgs gu{x, h->w_gu, h->s_gu, h->Ys, offsets, perm, A, c.n_experts, c.d_model, c.d_ff,
+                      h->dec_split_gu};
         CMOE_HIP(launch_decode_gemm(gu, 1, h->cus, s));
         if (tm)
             CMOE_HIP(hipEventRecord(h->ev[3], s));
         CMOE_HIP(launch_decode_silu(h->Ys, h->H, A, c.d_ff, h->dec_split_gu, s));
         if (tm)
             CMOE_HIP(hipEventRecord(h->ev[4], s));
-        DecodeArgs dn{h->H, h->w_d, h->Ys, offsets, perm, A, c.n_experts, c.d_model, c.d_ff, h->dec_split_dn};
+        DecodeArgs dn{h->H, h->w_d, h->s_d, h->Ys, offsets, perm, A, c.n_experts, c.d_model, c.d_ff,
+                      h->dec_split_dn};
         CMOE_HIP(launch_decode_gemm(dn, 0, h->cus, s));
         split = h->dec_split_dn;
     } else {
-        GemmArgs gu{x, h->w_gu, h->H, offsets, perm, A, c.n_experts, c.top_k, c.d_model, c.d_ff, h->group_n, 1,
-                    h->cus};
+        GemmArgs gu{x,         h->w_gu,   h->s_gu, h->H,      offsets,   perm, A, c.n_experts,
+                    c.top_k,   c.d_model, c.d_ff,  h->group_n, 1,       h->cus};
         CMOE_HIP(bf ? launch_gate_up_bf16(gu, s) : launch_gate_up_f32(gu, s));
         if (tm) {
             CMOE_HIP(hipEventRecord(h->ev[3], s));
             CMOE_HIP(hipEventRecord(h->ev[4], s));  // no separate reduce on this path
         }
         split = bf ? down_split_bf16(A, c.n_experts, c.d_model, c.d_ff, h->cus) : 1;
-        GemmArgs dn{h->H, h->w_d, h->Ys, offsets, perm, A, c.n_experts, c.top_k, c.d_model, c.d_ff, h->group_n,
-                    split, h->cus};
+        GemmArgs dn{h->H,      h->w_d,    h->s_d, h->Ys,      offsets, perm, A, c.n_experts,
+                    c.top_k,   c.d_model, c.d_ff, h->group_n, split,   h->cus};
         CMOE_HIP(bf ? launch_down_bf16(dn, s) : launch_down_f32(dn, s));
     }
     if (tm)
@@ -378,6 +400,21 @@ colibri_moe_status_t colibri_moe_free(colibri_moe_t* h)
     const bool ok = hipStreamSynchronize(h->stream) == hipSuccess;
     release(h);
     return ok ? COLIBRI_MOE_OK : COLIBRI_MOE_ERR_HIP;
+}
+
+colibri_moe_status_t colibri_moe_quantize_fp8(const void* w, int64_t rows, int64_t cols, uint8_t* codes,
+                                              float* scales, void* hip_stream)
+{
+    if (!w || !codes || !scales || rows < 1 || cols < 8 || cols % 8 != 0 || cols > INT32_MAX ||
+        rows > ((int64_t)1 << 40) / cols)
+        return COLIBRI_MOE_ERR_INVALID_ARG;
+    if (!aligned16(w) || ((uintptr_t)codes & 7u) || ((uintptr_t)scales & 3u))
+        return COLIBRI_MOE_ERR_ALIGNMENT;
+    hipStream_t s = (hipStream_t)hip_stream;
+    CMOE_HIP(launch_fp8_row_scales(w, nullptr, scales, rows, 0, (int)cols, s));
+    CMOE_HIP(launch_fp8_encode_rows(w, scales, codes, rows, (int)cols, s));
+    CMOE_HIP(hipStreamSynchronize(s));
+    return COLIBRI_MOE_OK;
 }
 
 const char* colibri_moe_status_string(colibri_moe_status_t s)

@@ -27,6 +27,19 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const Vec16& v)
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// Eight OCP E4M3 codes (little-endian in two words) to bf16, each multiplied
+// by sc (a power of two here, so exact): v_cvt_scalef32_pk_bf16_fp8, two codes
+// per instruction.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi, float sc)
+{
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, false);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, true);
+    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, false);
+    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, true);
+    return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b)
 {
     return __uint_as_float((uint32_t)b << 16);
@@ -78,9 +91,12 @@ struct GemmArgs {
     //   out = Ys: split partial sums over K, partial s at Ys + s*A*d, each
     //   [A][d] fp32 with row p = sorted position p (combine gathers them
     //   through inv).
-    // bf16 weights are in the blocked MFMA layout, fp32 weights row-major.
+    // bf16 weights are in the blocked MFMA layout, fp32 weights row-major;
+    // 8-bit weights (scales != null) are E4M3 codes in the fp8 blocked layout
+    // with one fp32 scale per weight row, scales[e*N + n].
     const void* a;
     const void* b;
+    const float* scales;
     void* out;
     const int32_t* offsets;   // [E+1]
     const int32_t* perm;      // [A]
@@ -102,7 +118,8 @@ hipError_t launch_down_f32(const GemmArgs& a, hipStream_t s);
 // Small-batch (decode) path of the bf16 expert GEMMs (decode_bf16.hip).
 struct DecodeArgs {
     const void* a;            // gate/up: x [T][d] (rows through perm); down: H [A][f]
-    const void* b;            // blocked bf16 weights (as in the grouped GEMMs)
+    const void* b;            // blocked bf16 or fp8 weights (as in the grouped GEMMs)
+    const float* scales;      // fp8 row scales [E][N], or null for bf16 weights
     float* part;              // fp32 slice partials [split][A][N], N = 2f (gate/up) or d (down)
     const int32_t* offsets;   // [E+1]
     const int32_t* perm;      // [A]
@@ -112,11 +129,25 @@ struct DecodeArgs {
 };
 // Waves a decode launch runs on `cus` compute units.
 int decode_waves(int cus);
-// K slices for an (E experts, N weight rows, K) decode GEMM on `waves` waves.
-int decode_split(int E, int N, int K, int waves, int max_split);
+// K slices for an (E experts, N weight rows, K) decode GEMM on `waves` waves
+// that steps through K in kstep-wide steps (16 for bf16 weights, 32 for fp8).
+int decode_split(int E, int N, int K, int kstep, int waves, int max_split);
 hipError_t launch_decode_gemm(const DecodeArgs& a, int gate_up, int cus, hipStream_t s);
 // H = SiLU(sum of gate slices) * (sum of up slices), bf16.
 hipError_t launch_decode_silu(const float* part, void* H, int A, int f, int S, hipStream_t s);
+
+// 8-bit expert weights (quant_fp8.hip). Row scales of bf16 weight rows: rows
+// of [rows][cols], or with w1 != null the interleaved gate/up rows of
+// [E][rows_per_e] (rows_per_e = 2f) built from w0 (gate) and w1 (up).
+hipError_t launch_fp8_row_scales(const void* w0, const void* w1, float* scales, int64_t rows, int rows_per_e,
+                                 int cols, hipStream_t s);
+// E4M3 codes in the fp8 blocked GEMM layout ([E][N][K] weights, gate/up
+// interleaved when w1 != null), scaled by the row scales.
+hipError_t launch_fp8_pack_blocked(const void* w0, const void* w1, const float* scales, void* out, int E, int N,
+                                   int K, hipStream_t s);
+// Row-major E4M3 codes of [rows][cols] bf16 with the given row scales.
+hipError_t launch_fp8_encode_rows(const void* w, const float* scales, uint8_t* codes, int64_t rows, int cols,
+                                  hipStream_t s);
 
 struct CombineArgs {
     const float* ys;    // split partials, each [A][d] fp32 by sorted position

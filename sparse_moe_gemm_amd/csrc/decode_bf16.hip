@@ -21,6 +21,12 @@
 // which keeps all compute units streaming. For gate/up a second kernel sums
 // the slices and applies SiLU(g)*u into H; for down the slices are the Ys
 // partials that combine already sums.
+// With 8-bit expert weights (E4M3 codes in the fp8 blocked layout, one scale
+// per weight row) the same items step through K 32 at a time: per step and
+// weight block one 1 KiB block of codes (one 16-byte load per lane: its B
+// fragments of the step's two 16-wide MFMA k steps), turned into exact bf16
+// (code times the row scale) in registers; the bytes read per weight are
+// halved, the arithmetic is the bf16 path's.
 #include "common.hpp"
 
 namespace cmoe {
@@ -115,6 +121,115 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
 }
 
+template <bool GATE_UP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_gemm_f8_kernel(DecodeArgs g)
+{
+    constexpr bool gate_up = GATE_UP;
+    constexpr int kQ = 4;  // 32-wide k steps of loads in flight per wave (two sets)
+    const int lane = threadIdx.x % kWave;
+    const int W = gridDim.x * (kThreads / kWave);
+    const int w0 = blockIdx.x * (kThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int N = gate_up ? 2 * g.f : g.d;
+    const int K = gate_up ? g.d : g.f;
+    const int NB = N / 32, KB = K / 32, S = g.split;
+    const int NB2 = NB / 2;
+    const int items = g.E * NB2 * S;
+    const Vec16* B = (const Vec16*)g.b;
+    const uint16_t* Abase = (const uint16_t*)g.a;
+
+    for (int it = w0; it < items; it += W) {
+        const int s = it % S;
+        const int rest = it / S;
+        const int nb = (rest % NB2) * 2;
+        const int e = rest / NB2;
+        const int seg0 = g.offsets[e];
+        const int cnt = g.offsets[e + 1] - seg0;
+        if (cnt <= 0)
+            continue;
+        const int kb0 = (int)((int64_t)s * KB / S), kb1 = (int)((int64_t)(s + 1) * KB / S);
+        // lane's 16 bytes of k step kb of row block nb: both halves' codes
+        const Vec16* bp = B + ((int64_t)e * NB + nb) * KB * kWave + lane;
+        const int64_t bst = (int64_t)KB * kWave;  // next weight block
+        const float s0 = g.scales[(int64_t)e * N + nb * 32 + (lane & 31)];
+        const float s1 = g.scales[(int64_t)e * N + nb * 32 + 32 + (lane & 31)];
+        float* out = g.part + (int64_t)s * g.A * N + nb * 32 + (lane & 31);
+
+        for (int r0 = 0; r0 < cnt; r0 += 32) {
+            const int r = min(r0 + (lane & 31), cnt - 1);
+            const int src = gate_up ? g.perm[seg0 + r] : seg0 + r;
+            // A fragment of 16-wide k step t: Vec16 index 2*t (+ lane/32 via the base)
+            const Vec16* ap = (const Vec16*)(Abase + (int64_t)src * K) + (lane >> 5);
+            floatx16 acc0, acc1;
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                acc0[q] = acc1[q] = 0.f;
+            Vec16 a0[kQ][2], a1[kQ][2];
+            Vec16 b0[kQ], c0[kQ], b1[kQ], c1[kQ];
+#pragma unroll
+            for (int i = 0; i < kQ; ++i) {
+                const int kb = min(kb0 + i, kb1 - 1);
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    a0[i][h] = ap[kb * 4 + 2 * h];
+                b0[i] = bp[(int64_t)kb * kWave];
+                c0[i] = bp[bst + (int64_t)kb * kWave];
+            }
+            for (int kb = kb0; kb < kb1; kb += 2 * kQ) {
+#pragma unroll
+                for (int i = 0; i < kQ; ++i) {
+                    const int kk = min(kb + kQ + i, kb1 - 1);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        a1[i][h] = ap[kk * 4 + 2 * h];
+                    b1[i] = bp[(int64_t)kk * kWave];
+                    c1[i] = bp[bst + (int64_t)kk * kWave];
+                }
+#pragma unroll
+                for (int i = 0; i < kQ; ++i)
+                    if (kb + i < kb1) {
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const bf16x8 fa = as_bf16x8(a0[i][h]);
+                            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fp8x8_to_bf16(b0[i][2 * h], b0[i][2 * h + 1], s0),
+                                                                           acc0, 0, 0, 0);
+                            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fp8x8_to_bf16(c0[i][2 * h], c0[i][2 * h + 1], s1),
+                                                                           acc1, 0, 0, 0);
+                        }
+                    }
+#pragma unroll
+                for (int i = 0; i < kQ; ++i) {
+                    const int kk = min(kb + 2 * kQ + i, kb1 - 1);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        a0[i][h] = ap[kk * 4 + 2 * h];
+                    b0[i] = bp[(int64_t)kk * kWave];
+                    c0[i] = bp[bst + (int64_t)kk * kWave];
+                }
+#pragma unroll
+                for (int i = 0; i < kQ; ++i)
+                    if (kb + kQ + i < kb1) {
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const bf16x8 fa = as_bf16x8(a1[i][h]);
+                            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fp8x8_to_bf16(b1[i][2 * h], b1[i][2 * h + 1], s0),
+                                                                           acc0, 0, 0, 0);
+                            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fp8x8_to_bf16(c1[i][2 * h], c1[i][2 * h + 1], s1),
+                                                                           acc1, 0, 0, 0);
+                        }
+                    }
+            }
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int row = r0 + 8 * (q / 4) + 4 * (lane >> 5) + (q % 4);
+                if (row < cnt) {
+                    out[(int64_t)(seg0 + row) * N] = acc0[q];
+                    out[(int64_t)(seg0 + row) * N + 32] = acc1[q];
+                }
+            }
+        }
+    }
+}
+
 // H[p][c] = bf16(SiLU(sum_s P[s][p][gate row of c]) * sum_s P[s][p][up row of c]),
 // with gate/up interleaved by 32 rows: h column c is gate row (c/32)*64 + c%32
 // and up row (c/32)*64 + 32 + c%32 of the combined [2f] weight rows. Four
@@ -157,20 +272,26 @@ int decode_waves(int cus)
     return cus * 2 * (kThreads / kWave);
 }
 
-int decode_split(int E, int N, int K, int waves, int max_split)
+int decode_split(int E, int N, int K, int kstep, int waves, int max_split)
 {
-    // Enough K slices for about eight items (of two 32-row blocks) per wave, at
-    // least four k-steps each.
+    // Enough K slices for about two items (of two 32-row blocks) per wave, at
+    // least four k-steps each. (Fewer, longer items stream better than many
+    // short ones; two per wave leave room to balance the last round.)
     const int64_t blocks = (int64_t)E * (N / 64);
-    int64_t s = (8 * (int64_t)waves + blocks - 1) / blocks;
-    const int64_t cap = std::min<int64_t>(max_split, std::max(1, K / 16 / 4));
+    int64_t s = (2 * (int64_t)waves + blocks - 1) / blocks;
+    const int64_t cap = std::min<int64_t>(max_split, std::max(1, K / kstep / 4));
     s = std::max<int64_t>(1, std::min(s, cap));
     return (int)s;
 }
 
 hipError_t launch_decode_gemm(const DecodeArgs& a, int gate_up, int cus, hipStream_t s)
 {
-    if (gate_up)
+    if (a.scales) {
+        if (gate_up)
+            hipLaunchKernelGGL(decode_gemm_f8_kernel<true>, dim3(cus * 2), dim3(kThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL(decode_gemm_f8_kernel<false>, dim3(cus * 2), dim3(kThreads), 0, s, a);
+    } else if (gate_up)
         hipLaunchKernelGGL(decode_gemm_kernel<true>, dim3(cus * 2), dim3(kThreads), 0, s, a);
     else
         hipLaunchKernelGGL(decode_gemm_kernel<false>, dim3(cus * 2), dim3(kThreads), 0, s, a);

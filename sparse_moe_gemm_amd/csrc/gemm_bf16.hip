@@ -68,18 +68,48 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p)
 
 // LDS stage layout (one 32-wide K stage of a BM x BN tile):
 //   A: BM rows x 4 chunks of 16 B (8 bf16), chunk index swizzled per row;
-//   B: BN/32 x 2 blocks of 1 KiB, each a 32-row x 16-k weight block in MFMA
-//      operand order (lane l's 8 values at l*16 B), copied whole from the
-//      blocked weight layout.
-template <int BM, int BN>
+//   B: bf16 weights: BN/32 x 2 blocks of 1 KiB, each a 32-row x 16-k weight
+//      block in MFMA operand order (lane l's 8 values at l*16 B); fp8 weights
+//      (F8): BN/32 blocks of 1 KiB, each 32 rows x 32 k (lane l's 16 codes
+//      at l*16 B: the 8 of the first 16-wide k step, then the 8 of the
+//      second); either way copied whole from the blocked weight layout.
+template <int BM, int BN, bool F8>
 struct Stage {
     Vec16 a[BM * kCH];
-    Vec16 b[(BN / 32) * 2 * 64];
+    Vec16 b[(BN / 32) * (F8 ? 1 : 2) * 64];
 };
-template <int BM, int BN>
+// The ring of stages; with fp8 weights the gate/up epilogue has a buffer of
+// its own (a 24 KiB slot is too small for it).
+template <int BM, int BN, bool F8, bool EPBUF>
 struct Ring {
-    Stage<BM, BN> st[kRing];
+    Stage<BM, BN, F8> st[kRing];
 };
+template <int BM, int BN, bool F8>
+struct Ring<BM, BN, F8, true> {
+    Stage<BM, BN, F8> st[kRing];
+    float ep[4 * 2048];
+};
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// B fragment as read from LDS (bf16x8 values, or 8 fp8 codes) and as the MFMA
+// takes it: fp8 codes become bf16 times the row's scale 2^e, which is exact.
+template <bool F8>
+struct BFrag {
+    typedef bf16x8 raw;
+};
+template <>
+struct BFrag<true> {
+    typedef u32x2 raw;
+};
+__device__ __forceinline__ bf16x8 to_bf16(bf16x8 r, float)
+{
+    return r;
+}
+__device__ __forceinline__ bf16x8 to_bf16(u32x2 r, float sc)
+{
+    return fp8x8_to_bf16(r[0], r[1], sc);
+}
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
@@ -121,27 +151,33 @@ struct LoadSrc {
 
 // Load q of this wave's share of one stage into the stage at LDS byte address
 // lds: A_INS instructions of 16 A rows each, then B_INS whole weight blocks.
-template <int BM, int BN, int A_INS, int B_INS>
+// KB is the number of 1 KiB blocks per 32 weight rows along K (K/16 for bf16
+// weights, K/32 for fp8).
+template <int BM, int BN, bool F8, int A_INS, int B_INS>
 __device__ __forceinline__ void issue_load(int q, const i32x4& ra, const LoadSrc<A_INS>& ls, int KB, int wv,
                                            uint32_t lane16, uint32_t lds)
 {
-    using St = Stage<BM, BN>;
+    using St = Stage<BM, BN, F8>;
     constexpr uint32_t kOffA = (uint32_t)offsetof(St, a);
     constexpr uint32_t kOffB = (uint32_t)offsetof(St, b);
     if (q < A_INS) {
         dma16(ra, ls.aoff[q], (uint32_t)ls.kt * (kBK * 2), lds + kOffA + (uint32_t)(wv * A_INS + q) * 1024u);
     } else {
-        const int blk = wv * B_INS + (q - A_INS);  // = row block * 2 + k block within the stage
-        const uint32_t soff = ((uint32_t)(blk >> 1) * (uint32_t)KB + (uint32_t)ls.kt * 2u + (uint32_t)(blk & 1)) * 1024u;
+        const int blk = wv * B_INS + (q - A_INS);
+        uint32_t soff;
+        if constexpr (F8)  // blk = row block
+            soff = ((uint32_t)blk * (uint32_t)KB + (uint32_t)ls.kt) * 1024u;
+        else  // blk = row block * 2 + k block within the stage
+            soff = ((uint32_t)(blk >> 1) * (uint32_t)KB + (uint32_t)ls.kt * 2u + (uint32_t)(blk & 1)) * 1024u;
         dma16(ls.rb, lane16, soff, lds + kOffB + (uint32_t)blk * 1024u);
     }
 }
 
 // Fragment readers of one LDS stage for wave (wm, wn): A fragment i (rows
 // wm*WM + i*32 ..) and B fragment j (weight rows wn*WN + j*32 ..) of k step ks.
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, bool F8>
 struct FragReader {
-    const Stage<BM, BN>* st;
+    const Stage<BM, BN, F8>* st;
     int wm, wn, lane;
     __device__ __forceinline__ bf16x8 a(int ks, int i) const
     {
@@ -149,9 +185,12 @@ struct FragReader {
         const int c = ks * 2 + (lane >> 5);
         return as_bf16x8(st->a[(wm * WM + i * 32 + lr) * kCH + (c ^ ((lr >> 2) & 3))]);
     }
-    __device__ __forceinline__ bf16x8 b(int ks, int j) const
+    __device__ __forceinline__ typename BFrag<F8>::raw b(int ks, int j) const
     {
-        return as_bf16x8(st->b[((wn * (WN / 32) + j) * 2 + ks) * 64 + lane]);
+        if constexpr (F8)
+            return ((const u32x2*)st->b)[((wn * (WN / 32) + j) * 64 + lane) * 2 + ks];
+        else
+            return as_bf16x8(st->b[((wn * (WN / 32) + j) * 2 + ks) * 64 + lane]);
     }
 };
 
@@ -177,11 +216,14 @@ struct FragReader {
 // The last m-tile of an expert runs the same code: its rows past the segment
 // end repeat the last valid row and their results are dropped. (A variant
 // that skips their MFMAs needs more registers than the persistent loop has.)
-template <int BM, int BN, int WM, int WN, int A_INS, int B_INS>
+// With fp8 weights (F8) the B fragments are read as 8 codes each and turned
+// into bf16 (row scale sc[j]) in the shadow of the MFMA before their first use.
+template <int BM, int BN, int WM, int WN, bool F8, int A_INS, int B_INS>
 __device__ __forceinline__ void stage(const i32x4& ra, const LoadSrc<A_INS>& ls, uint32_t ld_lds, int KB, int wv,
-                                      uint32_t lane16, const Stage<BM, BN>* st, const Stage<BM, BN>* st_next,
-                                      int wm, int wn, int lane, bf16x8 (&fa)[WM / 32],
-                                      bf16x8 (&fb)[WN / 32], floatx16 (&acc)[WM / 32][WN / 32])
+                                      uint32_t lane16, const Stage<BM, BN, F8>* st,
+                                      const Stage<BM, BN, F8>* st_next, int wm, int wn, int lane,
+                                      bf16x8 (&fa)[WM / 32], typename BFrag<F8>::raw (&fb)[WN / 32],
+                                      const float (&sc)[WN / 32], floatx16 (&acc)[WM / 32][WN / 32])
 {
     constexpr int MI = WM / 32, NI = WN / 32;
     constexpr int NLD = A_INS + B_INS;
@@ -190,14 +232,19 @@ __device__ __forceinline__ void stage(const i32x4& ra, const LoadSrc<A_INS>& ls,
     constexpr int RS = M / 2;    // reads are spread over the first RS MFMAs
     constexpr int L0 = NLD / 2;  // loads in the first half
     static_assert(kBK == 32, "two k steps per stage");
-    const FragReader<BM, BN, WM, WN> rd{st, wm, wn, lane}, rn{st_next, wm, wn, lane};
-    bf16x8 ga[MI], gb[NI];
+    const FragReader<BM, BN, WM, WN, F8> rd{st, wm, wn, lane}, rn{st_next, wm, wn, lane};
+    bf16x8 ga[MI];
+    typename BFrag<F8>::raw gb[NI];
+    bf16x8 cb[NI];
 
     int nread = 0, nld = 0;
+    cb[0] = to_bf16(fb[0], sc[0]);
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         const int i = m / NI, j = m % NI;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], cb[j], acc[i][j], 0, 0, 0);
+        if (i == 0 && j + 1 < NI)
+            cb[j + 1] = to_bf16(fb[j + 1], sc[j + 1]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (; nread < R && nread < ((m + 1) * R + RS - 1) / RS; ++nread) {
@@ -209,7 +256,7 @@ __device__ __forceinline__ void stage(const i32x4& ra, const LoadSrc<A_INS>& ls,
         }
 #pragma unroll
         for (; nld < ((m + 1) * L0) / M; ++nld) {
-            issue_load<BM, BN, A_INS, B_INS>(nld, ra, ls, KB, wv, lane16, ld_lds);
+            issue_load<BM, BN, F8, A_INS, B_INS>(nld, ra, ls, KB, wv, lane16, ld_lds);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -219,10 +266,13 @@ __device__ __forceinline__ void stage(const i32x4& ra, const LoadSrc<A_INS>& ls,
     __builtin_amdgcn_sched_barrier(0);
 
     nread = 0;
+    cb[0] = to_bf16(gb[0], sc[0]);
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         const int i = m / NI, j = m % NI;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[i], gb[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[i], cb[j], acc[i][j], 0, 0, 0);
+        if (i == 0 && j + 1 < NI)
+            cb[j + 1] = to_bf16(gb[j + 1], sc[j + 1]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (; nread < R && nread < ((m + 1) * R + RS - 1) / RS; ++nread) {
@@ -234,7 +284,7 @@ __device__ __forceinline__ void stage(const i32x4& ra, const LoadSrc<A_INS>& ls,
         }
 #pragma unroll
         for (; nld < L0 + ((m + 1) * (NLD - L0)) / M; ++nld) {
-            issue_load<BM, BN, A_INS, B_INS>(nld, ra, ls, KB, wv, lane16, ld_lds);
+            issue_load<BM, BN, F8, A_INS, B_INS>(nld, ra, ls, KB, wv, lane16, ld_lds);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -351,15 +401,16 @@ __device__ __forceinline__ i32x4 panel_rsrc(const void* b, const Tile& t, int N,
 // tile, or of the next tile (its A rows are `held`), or, past the last
 // tile, a reload of this tile's last stage that nobody reads (it keeps the
 // loads per stage, and so every wait count, the same).
-template <int BM, int BN, int WM, int WN, int A_INS, int B_INS>
+template <int BM, int BN, int WM, int WN, bool F8, bool EPBUF, int A_INS, int B_INS>
 __device__ __forceinline__ void tile_stages(const i32x4& ra, const LoadSrc<A_INS>& cs, int nkt, bool has_nxt,
                                             const i32x4& nrb, int nkt0, const uint32_t (&cpart)[A_INS],
-                                            uint32_t Kbytes, int KB, int wv, uint32_t lane16, Ring<BM, BN>& ring,
-                                            uint32_t ring0, int& b, int wm, int wn, int lane,
-                                            bf16x8 (&fa)[WM / 32], bf16x8 (&fb)[WN / 32],
-                                            const uint32_t (&held)[A_INS], floatx16 (&acc)[WM / 32][WN / 32])
+                                            uint32_t Kbytes, int KB, int wv, uint32_t lane16,
+                                            Ring<BM, BN, F8, EPBUF>& ring, uint32_t ring0, int& b, int wm, int wn,
+                                            int lane, bf16x8 (&fa)[WM / 32], typename BFrag<F8>::raw (&fb)[WN / 32],
+                                            const float (&sc)[WN / 32], const uint32_t (&held)[A_INS],
+                                            floatx16 (&acc)[WM / 32][WN / 32])
 {
-    constexpr uint32_t kStageBytes = sizeof(Stage<BM, BN>);
+    constexpr uint32_t kStageBytes = sizeof(Stage<BM, BN, F8>);
     int j = 0;
     do {  // a tile has at least kAhead stages
         const int ja = j + kAhead;
@@ -375,10 +426,12 @@ __device__ __forceinline__ void tile_stages(const i32x4& ra, const LoadSrc<A_INS
         } else {
             ls.kt = cs.kt + nkt - 1;
         }
+        if constexpr (F8)  // uniform, but the compiler may keep it in a VGPR
+            ls.kt = __builtin_amdgcn_readfirstlane(ls.kt);
         const int bl = b + kAhead >= kRing ? b + kAhead - kRing : b + kAhead;
         const int bn = b + 1 >= kRing ? 0 : b + 1;
-        stage<BM, BN, WM, WN, A_INS, B_INS>(ra, ls, ring0 + (uint32_t)bl * kStageBytes, KB, wv, lane16,
-                                            &ring.st[b], &ring.st[bn], wm, wn, lane, fa, fb, acc);
+        stage<BM, BN, WM, WN, F8, A_INS, B_INS>(ra, ls, ring0 + (uint32_t)bl * kStageBytes, KB, wv, lane16,
+                                                &ring.st[b], &ring.st[bn], wm, wn, lane, fa, fb, sc, acc);
         b = bn;
     } while (++j < nkt);
 }
@@ -393,25 +446,39 @@ __device__ __forceinline__ int row_src(const int32_t* perm, const Tile& t, int r
     return GATE_UP ? perm[p] : p;
 }
 
-template <int BM, int BN, int WM, int WN, bool GATE_UP>
+// Per-lane row scales of fp8 weights: the wave's column j*32 + lane%32 of
+// tile t (weight row n*BN + wn*WN + j*32 + lane%32 of expert e).
+template <int BN, int WN>
+__device__ __forceinline__ void load_scales(const float* scales, const Tile& t, int N, int wn, int lane,
+                                            float (&sc)[WN / 32])
+{
+    const float* p = scales + (int64_t)t.e * N + t.n * BN + wn * WN + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < WN / 32; ++j)
+        sc[j] = p[j * 32];
+}
+
+template <int BM, int BN, int WM, int WN, bool GATE_UP, bool F8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void grouped_gemm_kernel(GemmArgs g)
 {
     constexpr int WAVES_N = BN / WN;
     constexpr int MI = WM / 32, NI = WN / 32;
-    constexpr int A_INS = BM * kCH / 64 / 4;      // A loads per wave per stage
-    constexpr int B_INS = (BN / 32) * 2 / 4;      // weight blocks per wave per stage
+    constexpr int A_INS = BM * kCH / 64 / 4;             // A loads per wave per stage
+    constexpr int B_INS = (BN / 32) * (F8 ? 1 : 2) / 4;  // weight blocks per wave per stage
     constexpr int NLD = A_INS + B_INS;
+    constexpr bool EPBUF = GATE_UP && F8;                // gate/up epilogue outside the ring
     static_assert((BM / WM) * WAVES_N == kThreads / kWave, "4 waves");
-    static_assert(A_INS * 4 * 16 == BM && B_INS * 4 == (BN / 32) * 2, "stage split over 4 waves");
+    static_assert(A_INS * 4 * 16 == BM && B_INS * 4 == (BN / 32) * (F8 ? 1 : 2), "stage split over 4 waves");
     static_assert(!GATE_UP || (NI % 2 == 0 && WN % 64 == 0), "gate/up pairs per wave");
-    static_assert(sizeof(Ring<BM, BN>) <= 160 * 1024, "LDS");
+    static_assert(sizeof(Ring<BM, BN, F8, EPBUF>) <= 160 * 1024, "LDS");
+    static_assert(!GATE_UP || EPBUF || sizeof(Stage<BM, BN, F8>) >= 4 * 2048 * sizeof(float), "epilogue in a slot");
 
-    __shared__ Ring<BM, BN> ring;
+    __shared__ Ring<BM, BN, F8, EPBUF> ring;
 
     const int N = GATE_UP ? 2 * g.f : g.d;  // weight rows per expert
     const int K = GATE_UP ? g.d : g.f;
     const int NT = N / BN;
-    const int KB = K / 16;   // 16-wide k blocks per weight row block
+    const int KB = K / (F8 ? 32 : 16);  // 1 KiB weight blocks per weight row block
     const int KT = K / kBK;  // K stages (a multiple of 4, at least 4)
     const int S = GATE_UP ? 1 : g.split;
     const int lane = threadIdx.x % kWave;
@@ -460,6 +527,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             held[i] = (uint32_t)row_src<GATE_UP>(g.perm, nxt, slot[i]);
     }
 
+    float sc[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+        sc[j] = 1.0f;
+    if constexpr (F8) {
+        // Wait for them here, before any stream load is in flight: a load
+        // still pending when the tile loop is entered would make the
+        // compiler wait for it (and so for every stage load) in each stage.
+        load_scales<BN, WN>(g.scales, cur, N, wn, lane, sc);
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+            asm volatile("" : "+v"(sc[j]) : : "memory");
+    }
+
     floatx16 acc[MI][NI];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -473,21 +554,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // which has at least kAhead stages), then the k step 0 fragments of the
     // first one.
     const uint32_t ring0 = lds_addr(&ring);
-    constexpr uint32_t kStageBytes = sizeof(Stage<BM, BN>);
+    constexpr uint32_t kStageBytes = sizeof(Stage<BM, BN, F8>);
 #pragma unroll
     for (int p = 0; p < kAhead; ++p) {
         LoadSrc<A_INS> ls = cs;
         ls.kt = cs.kt + p;
 #pragma unroll
         for (int q = 0; q < NLD; ++q)
-            issue_load<BM, BN, A_INS, B_INS>(q, ra, ls, KB, wv, lane16, ring0 + (uint32_t)p * kStageBytes);
+            issue_load<BM, BN, F8, A_INS, B_INS>(q, ra, ls, KB, wv, lane16, ring0 + (uint32_t)p * kStageBytes);
     }
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kAhead - 1) * NLD) : "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    bf16x8 fa[MI], fb[NI];
+    bf16x8 fa[MI];
+    typename BFrag<F8>::raw fb[NI];
     {
-        const FragReader<BM, BN, WM, WN> r0{&ring.st[0], wm, wn, lane};
+        const FragReader<BM, BN, WM, WN, F8> r0{&ring.st[0], wm, wn, lane};
 #pragma unroll
         for (int j = 0; j < NI; ++j)
             fb[j] = r0.b(0, j);
@@ -498,8 +580,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     int b = 0;
 
     for (;;) {
-        tile_stages<BM, BN, WM, WN, A_INS, B_INS>(ra, cs, cur.nkt, has_nxt, nrb, nxt.kt0, cpart, Kbytes, KB, wv,
-                                                  lane16, ring, ring0, b, wm, wn, lane, fa, fb, held, acc);
+        tile_stages<BM, BN, WM, WN, F8, EPBUF, A_INS, B_INS>(ra, cs, cur.nkt, has_nxt, nrb, nxt.kt0, cpart, Kbytes,
+                                                             KB, wv, lane16, ring, ring0, b, wm, wn, lane, fa, fb,
+                                                             sc, held, acc);
 
         // The tile after next: decode it and fetch its token rows now, so the
         // fetch overlaps the epilogue. Its first use is pinned after the
@@ -520,6 +603,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             for (int i = 0; i < A_INS; ++i)
                 nheld[i] = (uint32_t)row_src<GATE_UP>(g.perm, nn, slot[i]);
         }
+        // The next tile's row scales, fetched the same way (first use pinned
+        // after the epilogue).
+        float nsc[NI];
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+            nsc[j] = sc[j];
+        if constexpr (F8)
+            if (has_nxt)
+                load_scales<BN, WN>(g.scales, nxt, N, wn, lane, nsc);
 
         // Epilogue of the tile. 32x32 accumulator layout: lane holds column
         // lane%32 and, for q = 0..15, row 8*(q/4) + 4*(lane/32) + q%4. Rows
@@ -534,14 +626,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             // Through LDS, one (32-row group, gate/up block pair) at a time:
             // the accumulators go from AGPRs straight into this wave's 8 KiB
             // of the ring slot the tile's last stage used (free until the
-            // next stage refills it, after the barrier below), as fp32 rows of
-            // 32 with the 16-byte chunk index XORed with row%8 (conflict-free
-            // writes and reads); each lane then reads back 16 consecutive
-            // gate and up values of one row, applies SiLU(g)*u and stores 16
-            // bf16 of H with two 16-byte stores.
+            // next stage refills it, after the barrier below; with fp8
+            // weights a slot is too small and the ring has an epilogue buffer
+            // of its own), as fp32 rows of 32 with the 16-byte chunk index
+            // XORed with row%8 (conflict-free writes and reads); each lane
+            // then reads back 16 consecutive gate and up values of one row,
+            // applies SiLU(g)*u and stores 16 bf16 of H with two 16-byte
+            // stores.
             static_assert(BN == 256 && WN == 128 && NI == 4, "gate/up epilogue layout");
-            const int bfree = b == 0 ? kRing - 1 : b - 1;
-            float* ep = (float*)&ring.st[bfree] + wv * 2048;
+            float* ep;
+            if constexpr (EPBUF) {
+                ep = ring.ep + wv * 2048;
+            } else {
+                const int bfree = b == 0 ? kRing - 1 : b - 1;
+                ep = (float*)&ring.st[bfree] + wv * 2048;
+            }
             const int wr = 8 * 0 + 4 * (lane >> 5);  // row of q = 0 inside the 32-row group
             const int wc = lane & 31;
             const int rr = lane >> 1;                  // row read back by this lane
@@ -576,9 +675,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                     dst[1] = Vec16{hv[4], hv[5], hv[6], hv[7]};
                 }
             }
-            // Every wave is done with the slot before the next stage loads it.
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
+            // Every wave is done with the slot before the next stage loads it
+            // (a wave's own epilogue buffer needs no barrier).
+            if constexpr (!EPBUF) {
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+            }
         } else {
             float* Ys = (float*)g.out + (int64_t)cur.s * g.A_max * g.d;
 #pragma unroll
@@ -602,6 +704,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                     acc[i][j][q] = 0.f;
         if constexpr (GATE_UP)
             asm volatile("" : "+v"(nheld[0]), "+v"(nheld[1]), "+v"(nheld[2]), "+v"(nheld[3]) : : "memory");
+        if constexpr (F8) {
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
+                asm volatile("" : "+v"(nsc[j]) : : "memory");
+        }
         if (!has_nxt)
             break;
 
@@ -619,6 +726,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
         for (int i = 0; i < A_INS; ++i)
             held[i] = nheld[i];
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+            sc[j] = nsc[j];
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the trailing reloads
 }
@@ -693,7 +803,7 @@ int down_split_bf16(int A, int E, int d, int f, int cus)
     return (KT >= 16 && tiles < 3 * (int64_t)cus) ? 2 : 1;
 }
 
-template <bool GATE_UP>
+template <bool GATE_UP, bool F8>
 hipError_t launch_grouped(const GemmArgs& a, hipStream_t s)
 {
     const int N = GATE_UP ? 2 * a.f : a.d;
@@ -705,24 +815,27 @@ hipError_t launch_grouped(const GemmArgs& a, hipStream_t s)
         return hipSuccess;
     if constexpr (GATE_UP) {
         // 2 * d_ff is a multiple of 256 (d_ff % 128 == 0 is checked at init)
-        hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 256, 128, 128, true>), dim3(grid), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 256, 128, 128, true, F8>), dim3(grid), dim3(kThreads), 0, s,
+                           a);
     } else {
         if (BN == 256)
-            hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 256, 128, 128, false>), dim3(grid), dim3(kThreads), 0, s, a);
+            hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 256, 128, 128, false, F8>), dim3(grid), dim3(kThreads), 0,
+                               s, a);
         else
-            hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 128, 128, 64, false>), dim3(grid), dim3(kThreads), 0, s, a);
+            hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 128, 128, 64, false, F8>), dim3(grid), dim3(kThreads), 0,
+                               s, a);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t s)
 {
-    return launch_grouped<true>(a, s);
+    return a.scales ? launch_grouped<true, true>(a, s) : launch_grouped<true, false>(a, s);
 }
 
 hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t s)
 {
-    return launch_grouped<false>(a, s);
+    return a.scales ? launch_grouped<false, true>(a, s) : launch_grouped<false, false>(a, s);
 }
 
 hipError_t launch_pack_blocked(const void* w0, const void* w1, void* out, int E, int N, int K, int gate_up,

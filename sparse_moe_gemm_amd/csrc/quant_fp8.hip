@@ -1,0 +1,206 @@
+// quant_fp8.hip - 8-bit expert weights: quantization at init.
+//
+// «Colibri 是什么» (xxqk.cn) §4.2: the model converter can quantize the expert
+// FFN weights alone to 8 bits, keeping the router in full precision. The
+// pages fix neither the 8-bit format nor the scaling; this library uses
+//   - OCP FP8 E4M3 codes (gfx950's native 8-bit float: bias 7, 3 mantissa
+//     bits, largest finite 448, no infinities);
+//   - one scale per weight row (output unit), the power of two 2^e with the
+//     smallest integer e such that max_i |w[r][i]| <= 448 * 2^e (e = 0 for an
+//     all-zero row, e >= -126), so w * 2^-e is exact;
+//   - code = w * 2^-e rounded to the nearest E4M3 value, ties to the even
+//     mantissa, values below 2^-10 to a zero that keeps the sign of w.
+// Dequantization, code * 2^e, is exact in bf16, so the GEMMs convert codes to
+// bf16 in registers (v_cvt_scalef32_pk_bf16_fp8, scale = 2^e) and multiply
+// on the bf16 MFMA path; only the bytes read from memory change.
+//
+// Layout written for the GEMMs (blocked, like the bf16 one but one 1 KiB block
+// per 32 rows x 32 k): block (e, nb, kb) holds rows nb*32 .. +32 and
+// k = kb*32 .. +32; lane l's 16 bytes at l*16 are row nb*32 + l%32: first the
+// 8 codes of k = kb*32 + 8*(l/32) .. +8 (the lane's MFMA B fragment of the
+// first 16-wide k step), then those of k = kb*32 + 16 + 8*(l/32) .. +8 (the
+// second step). The small-batch GEMM fetches a lane's 16 bytes with one
+// load; the tiled GEMM reads each 8-byte half from LDS.
+#include "common.hpp"
+
+namespace cmoe {
+
+namespace {
+
+// Exponent e of the row scale from the row's largest magnitude.
+__device__ __forceinline__ int fp8_scale_exp(float amax)
+{
+    if (!(amax > 0.f))
+        return 0;
+    int x;
+    const float f = frexpf(amax, &x);  // amax = f * 2^x, f in [0.5, 1)
+    // 448 = 0.875 * 2^9: amax <= 448 * 2^e  <=>  f * 2^(x - 9 - e) <= 0.875
+    const int e = (f <= 0.875f) ? x - 9 : x - 8;
+    return e < -126 ? -126 : e;
+}
+
+// E4M3 code of v = w * 2^-e (exact), |v| <= 448.
+__device__ __forceinline__ uint32_t fp8_encode(float v)
+{
+    const uint32_t bits = __float_as_uint(v);
+    const uint32_t sign = (bits >> 31) << 7;
+    const float a = fabsf(v);
+    uint32_t E, m;
+    if (a < 0.015625f) {  // below 2^-6: steps of 2^-9 (a count of 8 is the smallest normal)
+        const uint32_t q = (uint32_t)rintf(a * 512.0f);  // exact scaling, round half to even
+        E = q >> 3;
+        m = q & 7u;
+    } else {
+        const uint32_t ab = bits & 0x7FFFFFFFu;
+        const uint32_t mant = ab & 0x7FFFFFu;
+        E = (ab >> 23) - 127 + 7;
+        m = mant >> 20;
+        const uint32_t rem = mant & 0xFFFFFu;  // the 20 bits dropped
+        if (rem > 0x80000u || (rem == 0x80000u && (m & 1u)))
+            ++m;
+        if (m == 8u) {
+            m = 0;
+            ++E;
+        }
+    }
+    return sign | (E << 3) | m;
+}
+
+// Per-row scales. One wave per row of `cols` bf16 values (cols % 8 == 0);
+// with `two_src`, combined row n of a [E][2f] matrix comes from w0 (gate) when
+// n % 64 < 32, else from w1 (up), source row (n/64)*32 + n%32 of expert e.
+__global__ __launch_bounds__(256) void fp8_row_scale_kernel(const uint16_t* w0, const uint16_t* w1, float* scales,
+                                                            int64_t rows, int rows_per_e, int cols, int two_src)
+{
+    const int lane = threadIdx.x % kWave;
+    const int64_t nw = (int64_t)gridDim.x * (blockDim.x / kWave);
+    for (int64_t r = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; r < rows; r += nw) {
+        const uint16_t* src;
+        if (two_src) {
+            const int64_t e = r / rows_per_e;
+            const int n = (int)(r % rows_per_e);
+            const int w = n % 64;
+            src = (w < 32 ? w0 : w1) + (e * (rows_per_e / 2) + (n / 64) * 32 + (w % 32)) * (int64_t)cols;
+        } else {
+            src = w0 + r * (int64_t)cols;
+        }
+        float amax = 0.f;
+        for (int c = lane * 8; c < cols; c += kWave * 8) {
+            const Vec16 v = *(const Vec16*)(src + c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                amax = fmaxf(amax, fabsf(__uint_as_float(v[i] << 16)));
+                amax = fmaxf(amax, fabsf(__uint_as_float(v[i] & 0xFFFF0000u)));
+            }
+        }
+#pragma unroll
+        for (int o = kWave / 2; o > 0; o >>= 1)
+            amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+        if (lane == 0)
+            scales[r] = ldexpf(1.0f, fp8_scale_exp(amax));
+    }
+}
+
+// 1 / s for a power of two s = 2^e (-126 <= e <= 127): exact, from the exponent.
+__device__ __forceinline__ float inv_pow2(float s)
+{
+    int x;
+    (void)frexpf(s, &x);  // s = 0.5 * 2^x
+    return ldexpf(1.0f, 1 - x);
+}
+
+// Codes of 8 consecutive bf16 values (16 bytes) scaled by 1/scale, packed
+// little-endian into two words.
+__device__ __forceinline__ uint2 encode8(const Vec16 v, float inv_scale)
+{
+    uint32_t c[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        c[2 * i] = fp8_encode(__uint_as_float(v[i] << 16) * inv_scale);
+        c[2 * i + 1] = fp8_encode(__uint_as_float(v[i] & 0xFFFF0000u) * inv_scale);
+    }
+    return make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+}
+
+// Blocked fp8 layout (see the file comment), one 16-byte lane chunk per thread.
+__global__ __launch_bounds__(256) void fp8_pack_blocked_kernel(const uint16_t* w0, const uint16_t* w1,
+                                                               const float* scales, Vec16* out, int E, int N, int K,
+                                                               int two_src)
+{
+    const int NB = N / 32, KB = K / 32;
+    const int64_t total = (int64_t)E * NB * KB * kWave;
+    const int Nsrc = two_src ? N / 2 : N;
+    for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int l = (int)(idx % kWave);
+        const int64_t blk = idx / kWave;
+        const int kb = (int)(blk % KB);
+        const int64_t rb = blk / KB;
+        const int nb = (int)(rb % NB);
+        const int e = (int)(rb / NB);
+        const int n = nb * 32 + (l % 32);
+        const int k = kb * 32 + 8 * (l / 32);
+        const uint16_t* src;
+        int srow;
+        if (two_src) {
+            const int w = n % 64;
+            srow = (n / 64) * 32 + (w % 32);
+            src = w < 32 ? w0 : w1;
+        } else {
+            srow = n;
+            src = w0;
+        }
+        const uint16_t* rowp = src + ((int64_t)e * Nsrc + srow) * K;
+        // multiplying by the exact 2^-e is the exact w * 2^-e
+        const float inv = inv_pow2(scales[(int64_t)e * N + n]);
+        const uint2 lo = encode8(*(const Vec16*)(rowp + k), inv);
+        const uint2 hi = encode8(*(const Vec16*)(rowp + k + 16), inv);
+        out[idx] = Vec16{lo.x, lo.y, hi.x, hi.y};
+    }
+}
+
+// Row-major codes: codes[r][c] for c < cols (cols % 8 == 0).
+__global__ __launch_bounds__(256) void fp8_encode_rows_kernel(const uint16_t* w, const float* scales, uint8_t* codes,
+                                                              int64_t rows, int cols)
+{
+    const int64_t chunks = rows * (cols / 8);
+    for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < chunks;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = idx / (cols / 8);
+        const int c = (int)(idx % (cols / 8)) * 8;
+        *(uint2*)(codes + r * cols + c) = encode8(*(const Vec16*)(w + r * cols + c), inv_pow2(scales[r]));
+    }
+}
+
+}  // namespace
+
+hipError_t launch_fp8_row_scales(const void* w0, const void* w1, float* scales, int64_t rows, int rows_per_e, int cols,
+                                 hipStream_t s)
+{
+    const int64_t blocks = std::min<int64_t>((rows + 3) / 4, 8192);
+    hipLaunchKernelGGL(fp8_row_scale_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const uint16_t*)w0,
+                       (const uint16_t*)w1, scales, rows, rows_per_e, cols, w1 ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_fp8_pack_blocked(const void* w0, const void* w1, const float* scales, void* out, int E, int N, int K,
+                                   hipStream_t s)
+{
+    hipLaunchKernelGGL(fp8_pack_blocked_kernel, dim3(2048), dim3(256), 0, s, (const uint16_t*)w0, (const uint16_t*)w1,
+                       scales, (Vec16*)out, E, N, K, w1 ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_fp8_encode_rows(const void* w, const float* scales, uint8_t* codes, int64_t rows, int cols,
+                                  hipStream_t s)
+{
+    const int64_t chunks = rows * (cols / 8);
+    const int64_t blocks = std::min<int64_t>((chunks + 255) / 256, 8192);
+    if (blocks < 1)
+        return hipSuccess;
+    hipLaunchKernelGGL(fp8_encode_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const uint16_t*)w, scales,
+                       codes, rows, cols);
+    return hipGetLastError();
+}
+
+}  // namespace cmoe

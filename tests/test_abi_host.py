@@ -61,6 +61,7 @@ FAKE = 0x100000  # never dereferenced: validation fails before any use
     (dict(d_ff=100), cm.ERR_UNSUPPORTED),
     (dict(d_ff=192), cm.ERR_UNSUPPORTED),
     (dict(max_tokens=(1 << 24) + 1), cm.ERR_UNSUPPORTED),
+    (dict(dtype=cm.F32, flags=cm.FLAG_FP8_WEIGHTS), cm.ERR_UNSUPPORTED),
 ])
 def test_init_rejects_bad_configs(kw, status):
     w = cm.Weights(FAKE, None, FAKE, FAKE, FAKE)
@@ -95,3 +96,19 @@ def test_binding_is_marshalling_only():
                 text = open(os.path.join(dirpath, fn)).read()
                 assert "oracle" not in text.lower().replace("oracle-free", ""), fn
                 assert "import synth" not in text and "moe_oracle" not in text, fn
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, 4, 8, FAKE, FAKE), cm.ERR_INVALID_ARG),
+    ((FAKE, 4, 8, None, FAKE), cm.ERR_INVALID_ARG),
+    ((FAKE, 4, 8, FAKE, None), cm.ERR_INVALID_ARG),
+    ((FAKE, 0, 8, FAKE, FAKE), cm.ERR_INVALID_ARG),
+    ((FAKE, 4, 4, FAKE, FAKE), cm.ERR_INVALID_ARG),
+    ((FAKE, 4, 12, FAKE, FAKE), cm.ERR_INVALID_ARG),
+    ((FAKE, 1 << 35, 64, FAKE, FAKE), cm.ERR_INVALID_ARG),
+    ((FAKE + 8, 4, 8, FAKE, FAKE), cm.ERR_ALIGNMENT),
+    ((FAKE, 4, 8, FAKE + 4, FAKE), cm.ERR_ALIGNMENT),
+    ((FAKE, 4, 8, FAKE, FAKE + 2), cm.ERR_ALIGNMENT),
+])
+def test_quantize_fp8_rejects_bad_arguments(args, status):
+    assert cm.colibri_moe_quantize_fp8(*args) == status

@@ -1,0 +1,179 @@
+"""GPU parity of the 8-bit expert-weight layer (FLAG_FP8_WEIGHTS) with the
+oracle, through the C ABI.
+
+* Quantization: the codes and scales of colibri_moe_quantize_fp8 (the routine
+  init applies to every expert weight row) equal the oracle's bit for bit, on
+  synthetic weights and on rows built to hit every rounding tie between
+  neighbouring codes, the subnormal codes, the largest code, all-zero rows and
+  the clamp of the scale exponent.
+* Layer: the oracle layer run on the oracle's dequantized weights is the 8-bit
+  layer (the dequantized weights are exact in bf16, and everything after them
+  is the bf16 layer's arithmetic), so the bf16 rules apply: routing exactly,
+  y within a per-token norm-wise error of 2e-2. The quantization itself moves
+  y by about 5% on these inputs, so the same comparison against the
+  unquantized layer fails: both are checked, on both GEMM paths.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from moe_case import compare, make_layer, run_gpu, sample_tokens, to_dev
+
+pytestmark = pytest.mark.gpu
+
+C = synth.LayerConfig
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Exact for values representable in bf16 (asserted)."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    bits = a.view(np.uint32)
+    assert np.all(bits & 0xFFFF == 0), "value not representable in bf16"
+    return (bits >> 16).astype(np.uint16)
+
+
+def special_rows() -> np.ndarray:
+    """Rows of 16 values: a probe value and the row maximum 448 * 2^s, so the
+    row scale is 2^s and the probe's code is the nearest E4M3 value of
+    probe / 2^s (ties between neighbouring codes included)."""
+    vals = []
+    for c in range(0, 0x7E):  # midpoints between neighbouring codes, both signs
+        a, b = oracle.fp8_value(c), oracle.fp8_value(c + 1)
+        vals += [(a + b) / 2, -(a + b) / 2, a, -a]
+    vals += [0.0, -0.0, 2.0 ** -11, -2.0 ** -11, 2.0 ** -10, 1.5 * 2.0 ** -10, 448.0, -448.0, 440.0, 416.0]
+    rows = []
+    for s in (-20, 0, 5):
+        for v in vals:
+            r = np.zeros(16, dtype=np.float32)
+            r[3] = v * 2.0 ** s
+            r[11] = 448.0 * 2.0 ** s
+            rows.append(r)
+    rows.append(np.zeros(16, dtype=np.float32))  # all-zero row: scale 1, codes 0
+    r = np.zeros(16, dtype=np.float32)
+    r[0] = -0.0
+    rows.append(r)
+    # row maxima just above and at 448 * 2^s (scale exponent steps), and tiny
+    # maxima where the exponent clamps at -126
+    for amax in (448.0, 449.0, 224.0, 225.0, 1.0, 0.875, 2.0 ** -100, 2.0 ** -120, 2.0 ** -126):
+        r = np.linspace(-amax, amax, 16).astype(np.float32)
+        rows.append(f32_round_bf16(r))
+    return np.stack(rows)
+
+
+def f32_round_bf16(a: np.ndarray) -> np.ndarray:
+    """Round fp32 to the nearest bf16 value (ties to even), as fp32."""
+    bits = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    bits = (bits + 0x7FFF + ((bits >> 16) & 1)) >> 16 << 16
+    return bits.astype(np.uint32).view(np.float32)
+
+
+def gpu_quantize(w_bits: np.ndarray):
+    import torch
+
+    import sparse_moe_gemm_amd as cm
+
+    codes, scales = cm.quantize_fp8(to_dev(w_bits))
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), scales.cpu().numpy()
+
+
+def test_quantize_matches_oracle_on_special_rows():
+    w = f32_to_bf16_bits(special_rows())
+    print(f"special rows {w.shape}", flush=True)
+    codes, scales = gpu_quantize(w)
+    rc, rs = oracle.quantize_fp8(w)
+    bad = np.argwhere(codes != rc)
+    assert bad.size == 0, f"codes differ at {bad[:5].tolist()}: gpu {codes[tuple(bad[0])]} oracle {rc[tuple(bad[0])]}"
+    assert np.array_equal(scales.view(np.uint32), rs.view(np.uint32))
+
+
+@pytest.mark.parametrize("shape", [(8 * 2 * 256, 512), (3, 8), (1000, 136), (64, 14336)])
+def test_quantize_matches_oracle_on_weights(shape):
+    rows, cols = shape
+    print(f"quantize {shape}", flush=True)
+    rng = np.random.default_rng(rows * 7 + cols)
+    w = f32_round_bf16(rng.standard_normal(shape).astype(np.float32) * np.float32(0.02))
+    w[:: max(1, rows // 7)] *= np.float32(37.0)  # rows of other magnitudes
+    w = f32_to_bf16_bits(f32_round_bf16(w))
+    codes, scales = gpu_quantize(w)
+    rc, rs = oracle.quantize_fp8(w)
+    assert np.array_equal(scales.view(np.uint32), rs.view(np.uint32))
+    bad = np.argwhere(codes != rc)
+    assert bad.size == 0, f"codes differ at {bad[:5].tolist()}"
+
+
+def test_quantize_of_layer_weights_matches_oracle():
+    cfg = C("mixtral-small", 700, 256, 8, 2, 512, "bf16")
+    inp = synth.make_inputs(cfg)
+    for name in ("w_gate", "w_up", "w_down"):
+        E, rows, cols = inp[name].shape
+        w = inp[name].reshape(E * rows, cols)
+        codes, scales = gpu_quantize(w)
+        rc, rs = oracle.quantize_fp8(w)
+        assert np.array_equal(codes, rc) and np.array_equal(scales, rs), name
+
+
+def _layer_case(cfg, inp, tokens_of=None):
+    import sparse_moe_gemm_amd as cm
+
+    layer = make_layer(cfg, inp, flags=cm.FLAG_FP8_WEIGHTS)
+    g = run_gpu(layer, inp["x"])
+    layer.close()
+    toks = None if tokens_of is None else tokens_of(g)
+    q = oracle.quantized_expert_weights(inp)
+    rep = compare(cfg, inp, g, tokens=toks, ref_layer=oracle.Layer.from_inputs(q, cfg.k))
+    # against the unquantized layer the same rule fails: the GPU computed the
+    # 8-bit layer, not the bf16 one
+    t = np.arange(cfg.T) if toks is None else toks
+    y0 = oracle.Layer.from_inputs(inp, cfg.k).forward(inp["x"], tokens=t, forced_ids=g["topk_ids"])
+    den = np.max(np.abs(y0), axis=1)
+    e0 = np.max(np.abs(g["y"][t] - y0), axis=1) / np.where(den > 0, den, 1.0)
+    rep["err_vs_unquantized_mean"] = float(e0.mean())
+    assert e0.mean() > 4 * rep["max_err"], rep
+    return g, rep
+
+
+PATHS = {"tiled": "0", "small-batch": "65536"}
+CASES = [
+    C("decode-small", 32, 512, 8, 2, 1024, "bf16"),
+    C("one-token", 1, 128, 8, 2, 128, "bf16"),
+    C("ragged-17", 17, 384, 16, 3, 384, "bf16"),
+    C("single-expert", 130, 128, 1, 1, 128, "bf16"),
+    C("mixtral-small", 700, 256, 8, 2, 512, "bf16"),
+    C("fine-grained-small", 1000, 256, 128, 4, 256, "bf16"),
+    C("k8-E256", 64, 128, 256, 8, 128, "bf16"),
+    C("skewed-masked-small", 2000, 256, 64, 2, 128, "bf16",
+      {0: 4.0, 3: 4.0, **{e: -1.0e4 for e in range(44, 64)}}),
+]
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("cfg", CASES, ids=[c.name for c in CASES])
+def test_fp8_layer_parity(cfg, path, monkeypatch):
+    monkeypatch.setenv("CMOE_DECODE_MAX_A", PATHS[path])
+    print(f"fp8 case {cfg} path {path}", flush=True)
+    inp = synth.make_inputs(cfg)
+    g, rep = _layer_case(cfg, inp)
+    print(rep, flush=True)
+    if cfg.name == "skewed-masked-small":
+        assert np.all(g["expert_counts"][44:] == 0)
+
+
+@pytest.mark.parametrize("name", ["decode", "mixtral"])
+def test_fp8_full_size_workload(name):
+    cfg = synth.CONFIGS[name]
+    print(f"fp8 full-size case {cfg}", flush=True)
+    inp = synth.make_inputs(cfg)
+    g, rep = _layer_case(cfg, inp, None if cfg.T <= 64 else (lambda g: sample_tokens(g, cfg.T)))
+    print(name, rep, flush=True)
+
+
+def test_fp8_rejected_for_f32_layers():
+    import sparse_moe_gemm_amd as cm
+
+    cfg = synth.CONFIGS["tiny-f32"]
+    inp = synth.make_inputs(cfg)
+    with pytest.raises(cm.ColibriError) as ei:
+        make_layer(cfg, inp, flags=cm.FLAG_FP8_WEIGHTS)
+    assert ei.value.status == cm.ERR_UNSUPPORTED

@@ -157,8 +157,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         for (int r0 = 0; r0 < cnt; r0 += 32) {
             const int r = min(r0 + (lane & 31), cnt - 1);
             const int src = gate_up ? g.perm[seg0 + r] : seg0 + r;
-            // A fragment of 16-wide k step t: Vec16 index 2*t (+ lane/32 via the base)
-            const Vec16* ap = (const Vec16*)(Abase + (int64_t)src * K) + (lane >> 5);
+            // k order of the 8-bit weight layout: in 32-wide step kb, lane half
+            // lane/32 holds k kb*32 + 16*(lane/32) .. +16, 8 per 16-wide k step
+            // h; the activations are read in the same order (Vec16 kb*4 + h
+            // from the lane half's base)
+            const Vec16* ap = (const Vec16*)(Abase + (int64_t)src * K) + 2 * (lane >> 5);
             floatx16 acc0, acc1;
 #pragma unroll
             for (int q = 0; q < 16; ++q)
@@ -170,7 +173,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 const int kb = min(kb0 + i, kb1 - 1);
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
-                    a0[i][h] = ap[kb * 4 + 2 * h];
+                    a0[i][h] = ap[kb * 4 + h];
                 b0[i] = bp[(int64_t)kb * kWave];
                 c0[i] = bp[bst + (int64_t)kb * kWave];
             }
@@ -180,7 +183,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                     const int kk = min(kb + kQ + i, kb1 - 1);
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
-                        a1[i][h] = ap[kk * 4 + 2 * h];
+                        a1[i][h] = ap[kk * 4 + h];
                     b1[i] = bp[(int64_t)kk * kWave];
                     c1[i] = bp[bst + (int64_t)kk * kWave];
                 }
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                     const int kk = min(kb + 2 * kQ + i, kb1 - 1);
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
-                        a0[i][h] = ap[kk * 4 + 2 * h];
+                        a0[i][h] = ap[kk * 4 + h];
                     b0[i] = bp[(int64_t)kk * kWave];
                     c0[i] = bp[bst + (int64_t)kk * kWave];
                 }

@@ -71,8 +71,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p)
 //   B: bf16 weights: BN/32 x 2 blocks of 1 KiB, each a 32-row x 16-k weight
 //      block in MFMA operand order (lane l's 8 values at l*16 B); fp8 weights
 //      (F8): BN/32 blocks of 1 KiB, each 32 rows x 32 k (lane l's 16 codes
-//      at l*16 B: the 8 of the first 16-wide k step, then the 8 of the
-//      second); either way copied whole from the blocked weight layout.
+//      at l*16 B: k 16*(l/32) .. +16, 8 for each 16-wide k step); either way
+//      copied whole from the blocked weight layout.
 template <int BM, int BN, bool F8>
 struct Stage {
     Vec16 a[BM * kCH];
@@ -182,7 +182,11 @@ struct FragReader {
     __device__ __forceinline__ bf16x8 a(int ks, int i) const
     {
         const int lr = lane & 31;
-        const int c = ks * 2 + (lane >> 5);
+        // k order inside a 32-wide stage: bf16 weights step-major (k step ks,
+        // lane half lane/32 holds 8 k); 8-bit weights lane-half-major (lane
+        // half lane/32 holds 16 consecutive k, 8 per k step), the order of the
+        // 8-bit weight layout. Any order works if A and B agree.
+        const int c = F8 ? (lane >> 5) * 2 + ks : ks * 2 + (lane >> 5);
         return as_bf16x8(st->a[(wm * WM + i * 32 + lr) * kCH + (c ^ ((lr >> 2) & 3))]);
     }
     __device__ __forceinline__ typename BFrag<F8>::raw b(int ks, int j) const

@@ -16,11 +16,14 @@
 //
 // Layout written for the GEMMs (blocked, like the bf16 one but one 1 KiB block
 // per 32 rows x 32 k): block (e, nb, kb) holds rows nb*32 .. +32 and
-// k = kb*32 .. +32; lane l's 16 bytes at l*16 are row nb*32 + l%32: first the
-// 8 codes of k = kb*32 + 8*(l/32) .. +8 (the lane's MFMA B fragment of the
-// first 16-wide k step), then those of k = kb*32 + 16 + 8*(l/32) .. +8 (the
-// second step). The small-batch GEMM fetches a lane's 16 bytes with one
-// load; the tiled GEMM reads each 8-byte half from LDS.
+// k = kb*32 .. +32; lane l's 16 bytes at l*16 are the codes of row
+// nb*32 + l%32, k = kb*32 + 16*(l/32) .. +16. This k order serves both ways
+// the codes are multiplied: as bf16 on the 16-wide bf16 MFMA (the lane's
+// 8-byte halves are its B fragments of two k steps, the activations are read
+// in the same order), and on the 64-wide fp8 MFMA, whose lane l takes k
+// 16*(l/32) .. +16 of each 32-k half of its 64 (two consecutive blocks). The
+// small-batch GEMMs fetch a lane's 16 bytes with one load; the tiled GEMMs
+// read them from LDS.
 #include "common.hpp"
 
 namespace cmoe {
@@ -139,7 +142,7 @@ __global__ __launch_bounds__(256) void fp8_pack_blocked_kernel(const uint16_t* w
         const int nb = (int)(rb % NB);
         const int e = (int)(rb / NB);
         const int n = nb * 32 + (l % 32);
-        const int k = kb * 32 + 8 * (l / 32);
+        const int k = kb * 32 + 16 * (l / 32);
         const uint16_t* src;
         int srow;
         if (two_src) {
@@ -154,7 +157,7 @@ __global__ __launch_bounds__(256) void fp8_pack_blocked_kernel(const uint16_t* w
         // multiplying by the exact 2^-e is the exact w * 2^-e
         const float inv = inv_pow2(scales[(int64_t)e * N + n]);
         const uint2 lo = encode8(*(const Vec16*)(rowp + k), inv);
-        const uint2 hi = encode8(*(const Vec16*)(rowp + k + 16), inv);
+        const uint2 hi = encode8(*(const Vec16*)(rowp + k + 8), inv);
         out[idx] = Vec16{lo.x, lo.y, hi.x, hi.y};
     }
 }

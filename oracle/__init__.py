@@ -60,7 +60,9 @@ def lib():
             "moe_oracle_topk": [P, i32, i32, i32, P, P, P],
             "moe_oracle_dispatch": [P, i32, i32, i32, P, P, P, P, P],
             "moe_oracle_expert_ffn": [LP, i32, P, P, P],
+            "moe_oracle_expert_ffn_ex": [LP, i32, P, P, P, i32],
             "moe_oracle_forward": [LP, P, i32, P, P, i32, P, P],
+            "moe_oracle_forward_ex": [LP, P, i32, P, P, i32, P, P, i32],
             "moe_oracle_quantize_fp8": [P, ctypes.c_int, i64, i64, P, P],
             "moe_oracle_dequantize_fp8": [P, P, i64, i64, P],
         }
@@ -89,6 +91,9 @@ def _dtype_code(arr) -> int:
 def _check(rc, what):
     if rc != 0:
         raise ValueError(f"{what} failed with {rc}")
+
+
+ACT_FP8 = 1  # MOE_ORACLE_ACT_FP8
 
 
 class Layer:
@@ -134,17 +139,20 @@ class Layer:
         _check(lib().moe_oracle_router(ctypes.byref(self._s), _ptr(x), T, _ptr(out)), "router")
         return out
 
-    def expert_ffn(self, e: int, v, want_h: bool = False):
+    def expert_ffn(self, e: int, v, want_h: bool = False, act_fp8: bool = False):
+        """FFN of expert e on one row v; with act_fp8 the 8-bit activation
+        mode (h returned as the quantized values the down GEMM uses)."""
         v = np.ascontiguousarray(v)
         assert _dtype_code(v) == self.dtype and v.shape == (self.d,)
         out = np.empty(self.d, dtype=np.float64)
         h = np.empty(self.f, dtype=np.float64) if want_h else None
-        _check(lib().moe_oracle_expert_ffn(ctypes.byref(self._s), int(e), _ptr(v), _ptr(out), _ptr(h)),
-               "expert_ffn")
+        _check(lib().moe_oracle_expert_ffn_ex(ctypes.byref(self._s), int(e), _ptr(v), _ptr(out), _ptr(h),
+                                              ACT_FP8 if act_fp8 else 0), "expert_ffn")
         return (out, h) if want_h else out
 
-    def forward(self, x, tokens=None, forced_ids=None, want_slots: bool = False):
-        """y [n][d] double for the listed tokens (all tokens if None)."""
+    def forward(self, x, tokens=None, forced_ids=None, want_slots: bool = False, act_fp8: bool = False):
+        """y [n][d] double for the listed tokens (all tokens if None); act_fp8
+        selects the 8-bit activation mode of the expert FFN."""
         x = self._x(x)
         T = x.shape[0]
         tl = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int32)
@@ -154,8 +162,8 @@ class Layer:
             assert fi.shape == (T, self.k)
         y = np.empty((n, self.d), dtype=np.float64)
         ys = np.empty((n, self.k, self.d), dtype=np.float64) if want_slots else None
-        _check(lib().moe_oracle_forward(ctypes.byref(self._s), _ptr(x), T, _ptr(fi), _ptr(tl), n,
-                                        _ptr(y), _ptr(ys)), "forward")
+        _check(lib().moe_oracle_forward_ex(ctypes.byref(self._s), _ptr(x), T, _ptr(fi), _ptr(tl), n,
+                                           _ptr(y), _ptr(ys), ACT_FP8 if act_fp8 else 0), "forward")
         return (y, ys) if want_slots else y
 
 

@@ -189,21 +189,35 @@ int moe_oracle_dispatch(const int32_t* ids, int32_t T, int32_t k, int32_t E,
  *   g_i = sum_c v_c W_g[e][i][c];  u_i = sum_c v_c W_u[e][i][c]
  *   h_i = SiLU(g_i) * u_i = g_i / (1 + exp(-g_i)) * u_i
  *   out_o = sum_i h_i W_d[e][o][i] */
+static void quantize_row_values(double* v, int64_t n);
+static double bf16_round(double v);
+
+/* With act_fp8 (8-bit activations, reading in moe_oracle.h) the input row and
+ * h enter their GEMMs as their 8-bit row-quantized values: the input row v as
+ * given, h after rounding to bf16. xv is scratch of d doubles. */
 static void expert_ffn(const moe_oracle_layer_t* L, int32_t e, const void* xbase, int64_t xoff,
-                       double* h, double* out)
+                       double* h, double* out, int act_fp8, double* xv)
 {
     const int64_t d = L->d, f = L->f;
     const int dt = L->dtype;
     const int64_t wg0 = (int64_t)e * f * d;
     const int64_t wd0 = (int64_t)e * d * f;
+    for (int64_t c = 0; c < d; ++c)
+        xv[c] = elem(xbase, dt, xoff + c);
+    if (act_fp8)
+        quantize_row_values(xv, d);
     for (int64_t i = 0; i < f; ++i) {
         double g = 0.0, u = 0.0;
         for (int64_t c = 0; c < d; ++c) {
-            double v = elem(xbase, dt, xoff + c);
-            g += v * elem(L->w_gate, dt, wg0 + i * d + c);
-            u += v * elem(L->w_up, dt, wg0 + i * d + c);
+            g += xv[c] * elem(L->w_gate, dt, wg0 + i * d + c);
+            u += xv[c] * elem(L->w_up, dt, wg0 + i * d + c);
         }
         h[i] = g / (1.0 + exp(-g)) * u;
+    }
+    if (act_fp8) {
+        for (int64_t i = 0; i < f; ++i)
+            h[i] = bf16_round(h[i]);
+        quantize_row_values(h, f);
     }
     for (int64_t o = 0; o < d; ++o) {
         double acc = 0.0;
@@ -213,18 +227,30 @@ static void expert_ffn(const moe_oracle_layer_t* L, int32_t e, const void* xbase
     }
 }
 
+int moe_oracle_expert_ffn_ex(const moe_oracle_layer_t* L, int32_t e, const void* v,
+                             double* out, double* h_out, int32_t flags)
+{
+    if (!layer_ok(L) || !v || !out || e < 0 || e >= L->E || (flags & ~MOE_ORACLE_ACT_FP8))
+        return -1;
+    double* h = h_out ? h_out : (double*)malloc(sizeof(double) * (size_t)L->f);
+    double* xv = (double*)malloc(sizeof(double) * (size_t)L->d);
+    if (!h || !xv) {
+        if (!h_out)
+            free(h);
+        free(xv);
+        return -3;
+    }
+    expert_ffn(L, e, v, 0, h, out, flags & MOE_ORACLE_ACT_FP8, xv);
+    if (!h_out)
+        free(h);
+    free(xv);
+    return 0;
+}
+
 int moe_oracle_expert_ffn(const moe_oracle_layer_t* L, int32_t e, const void* v,
                           double* out, double* h_out)
 {
-    if (!layer_ok(L) || !v || !out || e < 0 || e >= L->E)
-        return -1;
-    double* h = h_out ? h_out : (double*)malloc(sizeof(double) * (size_t)L->f);
-    if (!h)
-        return -3;
-    expert_ffn(L, e, v, 0, h, out);
-    if (!h_out)
-        free(h);
-    return 0;
+    return moe_oracle_expert_ffn_ex(L, e, v, out, h_out, 0);
 }
 
 /* Whole layer per token: route, select, run the k experts, weighted sum.
@@ -236,8 +262,16 @@ int moe_oracle_forward(const moe_oracle_layer_t* L, const void* x, int32_t T,
                        const int32_t* forced_ids, const int32_t* token_list, int32_t n,
                        double* y, double* Y_slots)
 {
-    if (!layer_ok(L) || !x || !y || T < 0 || n < 0)
+    return moe_oracle_forward_ex(L, x, T, forced_ids, token_list, n, y, Y_slots, 0);
+}
+
+int moe_oracle_forward_ex(const moe_oracle_layer_t* L, const void* x, int32_t T,
+                          const int32_t* forced_ids, const int32_t* token_list, int32_t n,
+                          double* y, double* Y_slots, int32_t flags)
+{
+    if (!layer_ok(L) || !x || !y || T < 0 || n < 0 || (flags & ~MOE_ORACLE_ACT_FP8))
         return -1;
+    const int act_fp8 = (flags & MOE_ORACLE_ACT_FP8) != 0;
     if (!token_list && n != T)
         return -1;
     const int32_t E = L->E, k = L->k;
@@ -260,7 +294,8 @@ int moe_oracle_forward(const moe_oracle_layer_t* L, const void* x, int32_t T,
         double* wd = (double*)malloc(sizeof(double) * (size_t)k);
         double* h = (double*)malloc(sizeof(double) * (size_t)f);
         double* ye = (double*)malloc(sizeof(double) * (size_t)d);
-        if (!lg || !ids || !wd || !h || !ye) {
+        double* xv = (double*)malloc(sizeof(double) * (size_t)d);
+        if (!lg || !ids || !wd || !h || !ye || !xv) {
 #pragma omp atomic write
             err = -3;
         } else {
@@ -283,7 +318,7 @@ int moe_oracle_forward(const moe_oracle_layer_t* L, const void* x, int32_t T,
             for (int64_t o = 0; o < d; ++o)
                 yr[o] = 0.0;
             for (int32_t j = 0; j < k; ++j) {
-                expert_ffn(L, ids[j], x, (int64_t)t * d, h, ye);
+                expert_ffn(L, ids[j], x, (int64_t)t * d, h, ye, act_fp8, xv);
                 if (Y_slots)
                     memcpy(Y_slots + ((int64_t)r * k + j) * d, ye, sizeof(double) * (size_t)d);
                 for (int64_t o = 0; o < d; ++o)
@@ -295,6 +330,7 @@ int moe_oracle_forward(const moe_oracle_layer_t* L, const void* x, int32_t T,
         free(wd);
         free(h);
         free(ye);
+        free(xv);
     }
     return err;
 }
@@ -351,6 +387,45 @@ static uint8_t fp8_encode(double v)
     return (uint8_t)((neg << 7) | (E << 3) | m);
 }
 
+/* Exponent e of a row's power-of-two scale from its largest magnitude (the
+ * rule of the reading: smallest e with amax <= 448 * 2^e, 0 for a zero row,
+ * at least -126). */
+static int row_scale_exp(double amax)
+{
+    if (!(amax > 0.0))
+        return 0;
+    int x;
+    const double f = frexp(amax, &x); /* amax = f * 2^x, f in [0.5, 1) */
+    /* 448 = 0.875 * 2^9: amax <= 448 * 2^e  <=>  f * 2^(x-9-e) <= 0.875 */
+    const int e = (f <= 0.875) ? x - 9 : x - 8;
+    return e < -126 ? -126 : e;
+}
+
+/* v[0..n) replaced by its 8-bit row quantization, dequantized: code * 2^e. */
+static void quantize_row_values(double* v, int64_t n)
+{
+    double amax = 0.0;
+    for (int64_t i = 0; i < n; ++i)
+        if (fabs(v[i]) > amax)
+            amax = fabs(v[i]);
+    const int e = row_scale_exp(amax);
+    for (int64_t i = 0; i < n; ++i)
+        v[i] = ldexp(moe_oracle_fp8_value(fp8_encode(ldexp(v[i], -e))), e);
+}
+
+/* v rounded to bf16 (8 significant bits), to nearest, ties to even; values
+ * are far inside bf16's exponent range here. */
+static double bf16_round(double v)
+{
+    if (v == 0.0 || !isfinite(v))
+        return v;
+    int x;
+    (void)frexp(fabs(v), &x); /* |v| in [2^(x-1), 2^x) */
+    const double q = round_half_even(ldexp(fabs(v), 8 - x)); /* 8 significant bits */
+    const double r = ldexp(q, x - 8);
+    return v < 0 ? -r : r;
+}
+
 int moe_oracle_quantize_fp8(const void* w, int dtype, int64_t rows, int64_t cols,
                             uint8_t* codes, float* scales)
 {
@@ -366,15 +441,7 @@ int moe_oracle_quantize_fp8(const void* w, int dtype, int64_t rows, int64_t cols
             if (a > amax)
                 amax = a;
         }
-        int e = 0;
-        if (amax > 0.0) {
-            int x;
-            const double f = frexp(amax, &x); /* amax = f * 2^x, f in [0.5, 1) */
-            /* 448 = 0.875 * 2^9: amax <= 448 * 2^e  <=>  f * 2^(x-9-e) <= 0.875 */
-            e = (f <= 0.875) ? x - 9 : x - 8;
-            if (e < -126)
-                e = -126;
-        }
+        const int e = row_scale_exp(amax);
         scales[r] = (float)ldexp(1.0, e);
         for (int64_t i = 0; i < cols; ++i)
             codes[r * cols + i] = fp8_encode(ldexp(elem(w, dtype, r * cols + i), -e));

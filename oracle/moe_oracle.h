@@ -46,6 +46,10 @@ extern "C" {
 
 enum { MOE_ORACLE_F32 = 0, MOE_ORACLE_BF16 = 1 };
 
+/* Flags of the _ex entry points. MOE_ORACLE_ACT_FP8: 8-bit activations in the
+ * expert FFN (reading below, after the 8-bit weights). */
+enum { MOE_ORACLE_ACT_FP8 = 1 };
+
 /* Host description of one layer. Matrices are row-major:
  *   w_router [d][E], b_router [E] fp32 (NULL = zeros),
  *   w_gate, w_up [E][f][d], w_down [E][d][f].
@@ -82,6 +86,8 @@ int moe_oracle_dispatch(const int32_t* ids, int32_t T, int32_t k, int32_t E,
  * out [d]. If h_out is not NULL it receives the f values of h. */
 int moe_oracle_expert_ffn(const moe_oracle_layer_t* L, int32_t e, const void* v,
                           double* out, double* h_out);
+int moe_oracle_expert_ffn_ex(const moe_oracle_layer_t* L, int32_t e, const void* v,
+                             double* out, double* h_out, int32_t flags);
 
 /* Whole layer for the tokens in token_list (NULL = all T tokens, in order).
  * Routing uses the oracle's own logits unless forced_ids [T][k] is given, in
@@ -95,6 +101,9 @@ int moe_oracle_expert_ffn(const moe_oracle_layer_t* L, int32_t e, const void* v,
 int moe_oracle_forward(const moe_oracle_layer_t* L, const void* x, int32_t T,
                        const int32_t* forced_ids, const int32_t* token_list, int32_t n,
                        double* y, double* Y_slots);
+int moe_oracle_forward_ex(const moe_oracle_layer_t* L, const void* x, int32_t T,
+                          const int32_t* forced_ids, const int32_t* token_list, int32_t n,
+                          double* y, double* Y_slots, int32_t flags);
 
 /* 8-bit expert weights («Colibri 是什么» (xxqk.cn) §4.2: the model converter can
  * quantize only the expert FFN weights, with 8 bits, keeping the router in full
@@ -119,6 +128,16 @@ int moe_oracle_dequantize_fp8(const uint8_t* codes, const float* scales, int64_t
                               int64_t cols, uint16_t* bf16_out);
 /* Value of one E4M3 code (NaN for 0x7f/0xff). */
 double moe_oracle_fp8_value(uint8_t code);
+
+/* 8-bit activations (MOE_ORACLE_ACT_FP8): the pages store the expert weights
+ * in 8 bits and say nothing of the activations; this optional mode reads the
+ * roadmap's FP8 as FP8 matrix products, which need 8-bit inputs on both
+ * sides. Reading: each expert GEMM input row is quantized by the rule above
+ * (E4M3, one power-of-two scale per row): the token row x[t] (as given, per
+ * token; the router still sees the full-precision x) before gate/up, and the
+ * row h of each (token, expert) assignment before down, after rounding h to
+ * bf16 (the activation storage type), nearest, ties to even. The products
+ * and sums are then those of the dequantized values, in double as always. */
 
 #ifdef __cplusplus
 }

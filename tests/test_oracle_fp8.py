@@ -2,7 +2,9 @@
 one power-of-two scale per weight row; the reading is stated in
 oracle/moe_oracle.h). Each check uses something other than the encoder's own
 formula: values the E4M3 format fixes, a brute-force nearest-code search over
-all 256 codes, the minimality of the scale, and exactness of dequantization."""
+all 256 codes, the minimality of the scale, and exactness of dequantization.
+The optional 8-bit activation mode is pinned by recomputing an expert FFN with
+those brute-force pieces and numpy, and by its routing on full-precision x."""
 import math
 
 import numpy as np
@@ -121,3 +123,96 @@ def test_quantized_layer_is_the_layer_on_dequantized_weights():
 def test_invalid_arguments():
     with pytest.raises(Exception):
         oracle.quantize_fp8(np.zeros((0, 4), dtype=np.float32))
+
+
+# --- 8-bit activations (the oracle's MOE_ORACLE_ACT_FP8 mode) -----------------
+
+def brute_force_row(vals):
+    """8-bit row quantization by search: the smallest power of two 2^e
+    (e >= -126) with max|v| <= 448 * 2^e, then every value's nearest code by
+    brute force. Returns the dequantized values."""
+    amax = max(abs(v) for v in vals)
+    e = -126
+    while amax > 448.0 * 2.0 ** e:
+        e += 1
+    if amax == 0.0:
+        e = 0
+    return [oracle.fp8_value(brute_force_code(v / 2.0 ** e)) * 2.0 ** e for v in vals]
+
+
+def bf16_nearest(v: float) -> float:
+    """Nearest value with 8 significant bits, ties to even (Python's round is
+    exact and ties to even on the scaled mantissa)."""
+    if v == 0.0:
+        return v
+    m, ex = math.frexp(v)  # v = m * 2^ex, 0.5 <= |m| < 1
+    return round(m * 256.0) / 256.0 * 2.0 ** ex
+
+
+def test_act_fp8_expert_ffn_by_brute_force():
+    cfg = synth.LayerConfig("q8", 6, 32, 3, 2, 16, "bf16")
+    inp = oracle.quantized_expert_weights(synth.make_inputs(cfg))
+    L = oracle.Layer.from_inputs(inp, cfg.k)
+    wg = synth.bf16_bits_to_f32(inp["w_gate"]).astype(np.float64)
+    wu = synth.bf16_bits_to_f32(inp["w_up"]).astype(np.float64)
+    wd = synth.bf16_bits_to_f32(inp["w_down"]).astype(np.float64)
+    for t in range(cfg.T):
+        xrow = inp["x"][t]
+        xq = np.array(brute_force_row(list(synth.bf16_bits_to_f32(xrow).astype(np.float64))))
+        for e in range(cfg.E):
+            g, u = wg[e] @ xq, wu[e] @ xq
+            h = g / (1.0 + np.exp(-g)) * u
+            hq = np.array(brute_force_row([bf16_nearest(float(v)) for v in h]))
+            want = wd[e] @ hq
+            out, h_or = L.expert_ffn(e, xrow, want_h=True, act_fp8=True)
+            assert np.allclose(h_or, hq, rtol=0, atol=0), (t, e)
+            assert np.allclose(out, want, rtol=1e-12, atol=1e-14), (t, e)
+            # the mode changes the result (else this pin would be vacuous)
+            assert not np.allclose(out, L.expert_ffn(e, xrow), rtol=1e-6, atol=0)
+
+
+def test_act_fp8_routes_on_full_precision_x():
+    cfg = synth.LayerConfig("q8r", 40, 64, 8, 2, 32, "bf16")
+    inp = oracle.quantized_expert_weights(synth.make_inputs(cfg))
+    L = oracle.Layer.from_inputs(inp, cfg.k)
+    x = inp["x"]
+    y = L.forward(x, act_fp8=True)
+    ids, _, w64 = oracle.topk(L.router(x), cfg.k)
+    for t in range(cfg.T):
+        ref = sum(w64[t, j] * L.expert_ffn(int(ids[t, j]), x[t], act_fp8=True) for j in range(cfg.k))
+        assert np.allclose(y[t], ref, rtol=1e-13, atol=1e-15), t
+    y0 = L.forward(x)
+    rel = np.max(np.abs(y - y0)) / np.max(np.abs(y0))
+    assert 1e-3 < rel < 0.2, rel
+
+
+def test_act_fp8_constructed_rounding_order():
+    """h is rounded to bf16 before it is quantized; x is quantized as given.
+    fp32 layer, one expert, d = f = 2, identity down projection. Gate
+    pre-activations of 64 make SiLU exact (SiLU(64) = 64 in double), so h is
+    64 * up exactly."""
+    f32 = np.float32
+    small = 1.0625 + 2.0 ** -12  # just above the midpoint of codes 1.0 and 1.125
+    wr = np.ones((2, 1), f32)
+    wd = np.eye(2, dtype=f32)[None]
+    # 1) x = [1, 0] -> xq = x; h = [64*7, 64*small/64] = [448, small]: row scale
+    #    1; bf16 rounds small to the tie 1.0625, which goes to the even code
+    #    1.0 (quantized unrounded it would give 1.125).
+    L = oracle.Layer(wr, None, np.array([[[64.0, 0.0], [64.0, 0.0]]], f32),
+                     np.array([[[7.0, 0.0], [small / 64.0, 0.0]]], f32), wd, 1)
+    x = np.array([1.0, 0.0], f32)
+    out, h = L.expert_ffn(0, x, want_h=True, act_fp8=True)
+    assert list(h) == [448.0, 1.0] and list(out) == [448.0, 1.0]
+    out0, h0 = L.expert_ffn(0, x, want_h=True)
+    assert list(h0) == [448.0, small] and list(out0) == [448.0, small]
+    # 2) x = [small, 256]: row scale 1, quantized directly: xq = [1.125, 256].
+    #    g = 0.25 * x_1 = 64 for both units; u_0 = x_0 / 64, u_1 = 7/256 * x_1
+    #    = 7, so h = [xq_0, 448] = [1.125, 448] (already codes of scale 1).
+    L2 = oracle.Layer(wr, None, np.array([[[0.0, 0.25], [0.0, 0.25]]], f32),
+                      np.array([[[1.0 / 64.0, 0.0], [0.0, 7.0 / 256.0]]], f32), wd, 1)
+    x2 = np.array([small, 256.0], f32)
+    assert float(x2[0]) == small
+    out2, h2 = L2.expert_ffn(0, x2, want_h=True, act_fp8=True)
+    assert list(h2) == [1.125, 448.0] and list(out2) == [1.125, 448.0]
+    _, h2raw = L2.expert_ffn(0, x2, want_h=True)
+    assert list(h2raw) == [small, 448.0]

@@ -9,11 +9,14 @@ Prints one JSON line with the throughput (tokens/s), the roofline position of
 the dominant kernel (measured live with HIP events on the layer's stream), and
 the CPU oracle timed on a bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--fp8-weights] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--fp8-weights] [--fp8-activations]
+                    [--no-cpu-baseline]
 
 --fp8-weights builds the layer with 8-bit expert weights (E4M3 codes, one
 power-of-two scale per weight row, converted to bf16 in registers): same bf16
-arithmetic, half the expert weight bytes.
+arithmetic, half the expert weight bytes. --fp8-activations (implies
+--fp8-weights) also quantizes the expert GEMM inputs per row and runs both
+expert GEMMs on the fp8 MFMA; the roofline peak is then the fp8 one.
 """
 from __future__ import annotations
 
@@ -31,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/sec at 1 GPU; % of peak MFMA (prefill) / HBM GB/s (decode)"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (vector and matrix)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 WORKLOAD_NAMES = {
@@ -51,6 +55,8 @@ def parse():
     ap.add_argument("--workload", default="mixtral", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--fp8-weights", action="store_true",
                     help="8-bit expert weights (bf16 workloads only)")
+    ap.add_argument("--fp8-activations", action="store_true",
+                    help="8-bit expert weights and GEMM inputs, fp8 MFMA (bf16 workloads only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens of the oracle sample (0 = sized to ~15 s of CPU work)")
@@ -125,13 +131,14 @@ def profiled_traffic(workload: str, kernel: str):
         return None
 
 
-def cpu_baseline(cfg, inp, sample_tokens: int, fp8: bool = False):
+def cpu_baseline(cfg, inp, sample_tokens: int, fp8: bool = False, q8: bool = False):
     import oracle
 
     gomp = ctypes.CDLL("libgomp.so.1")
     threads = int(gomp.omp_get_max_threads())
     # fp8: the oracle's 8-bit layer is its ordinary layer on the dequantized
-    # weights (quantized here, outside the timed part, as the library does at init)
+    # weights (quantized here, outside the timed part, as the library does at
+    # init); q8 adds its 8-bit activation mode
     L = oracle.Layer.from_inputs(oracle.quantized_expert_weights(inp) if fp8 else inp, cfg.k)
     x = inp["x"]
     per_tok_macs = cfg.d * cfg.E + 3 * cfg.d * cfg.f * cfg.k
@@ -145,7 +152,7 @@ def cpu_baseline(cfg, inp, sample_tokens: int, fp8: bool = False):
     reps, dt = 0, 0.0
     while reps == 0 or (sample_tokens == cfg.T and dt < 10.0 and reps < 1000):
         t0 = time.perf_counter()
-        L.forward(x, tokens=toks)
+        L.forward(x, tokens=toks, act_fp8=q8)
         dt += time.perf_counter() - t0
         reps += 1
     what = f"first {sample_tokens} tokens of the workload" if reps == 1 else \
@@ -171,17 +178,19 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     cfg = synth.CONFIGS[args.workload]
-    if args.fp8_weights and cfg.dtype != "bf16":
-        print("--fp8-weights needs a bf16 workload", file=sys.stderr)
+    q8 = bool(args.fp8_activations)
+    fp8 = bool(args.fp8_weights) or q8
+    if fp8 and cfg.dtype != "bf16":
+        print("--fp8-weights / --fp8-activations need a bf16 workload", file=sys.stderr)
         sys.exit(2)
-    fp8 = bool(args.fp8_weights)
     t_gen = time.perf_counter()
     inp = synth.make_inputs(cfg)
     t_gen = time.perf_counter() - t_gen
 
     layer = cm.MoELayer(to_dev(inp["w_router"]), to_dev(inp["b_router"]), to_dev(inp["w_gate"]),
                         to_dev(inp["w_up"]), to_dev(inp["w_down"]), cfg.k, max_tokens=cfg.T,
-                        flags=cm.FLAG_ASYNC | cm.FLAG_STAGE_TIMING | (cm.FLAG_FP8_WEIGHTS if fp8 else 0))
+                        flags=cm.FLAG_ASYNC | cm.FLAG_STAGE_TIMING | (cm.FLAG_FP8_WEIGHTS if fp8 else 0)
+                        | (cm.FLAG_FP8_ACTIVATIONS if q8 else 0))
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     x = to_dev(inp["x"])
@@ -222,26 +231,28 @@ def main():
     tokens_per_s = cfg.T / (ms_per_step * 1e-3)
     A = cfg.T * cfg.k
     layer_tflops = cfg.flops() / (ms_per_step * 1e-3) / 1e12
-    peak_mm = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
+    peak_mm = PEAK_FP8_TFLOPS if q8 else PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
 
     fpa = gemm_flops_per_assignment(cfg)
     dom = "gate_up_gemm"  # carries 2/3 of the flops and of the weight bytes
     # The library takes its small-batch (weight streaming) path for bf16 calls
     # with at most CMOE_DECODE_MAX_A (default 256) assignments.
     small_batch = cfg.dtype == "bf16" and A <= int(os.environ.get("CMOE_DECODE_MAX_A", "256"))
-    prof_key = args.workload + ("-fp8" if fp8 else "")
+    prof_key = args.workload + ("-w8a8" if q8 else "-fp8" if fp8 else "")
     if small_batch:
         # weight streaming bound: algorithmic bytes = the active experts' gate
         # and up weights, read once
         achieved = active_weight_bytes(cfg, counts, dom, fp8) / (stage_ms[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS, "traffic": profiled_traffic(prof_key, dom),
-                "kernel": "decode_gemm_f8_kernel<true> (gate/up)" if fp8 else "decode_gemm_kernel<true> (gate/up)"}
+                "kernel": ("decode_gemm_q8_kernel<true>" if q8 else "decode_gemm_f8_kernel<true>" if fp8
+                           else "decode_gemm_kernel<true>") + " (gate/up)"}
     else:
         achieved = fpa[dom] * A / (stage_ms[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak_mm, "unit": "TFLOP/s",
                 "frac": achieved / peak_mm, "traffic": profiled_traffic(prof_key, dom),
-                "kernel": f"grouped_gemm_kernel<256,256,128,128,true,{str(fp8).lower()}> (gate/up)"}
+                "kernel": "grouped_gemm_kernel<256,256,128,128,true,"
+                          f"{str(fp8 and not q8).lower()},{str(q8).lower()}> (gate/up)"}
 
     out = {
         "metric": METRIC,
@@ -254,12 +265,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg.dtype,
+        "dtype": "fp8" if q8 else cfg.dtype,
         "data": "synthetic (seeded SplitMix64 + Box-Muller, bf16 RNE; no trained weights)",
-        "config": {"workload": WORKLOAD_NAMES[args.workload] + ("-fp8-weights" if fp8 else ""), "T": cfg.T,
+        "config": {"workload": WORKLOAD_NAMES[args.workload] + ("-w8a8" if q8 else "-fp8-weights" if fp8 else ""),
+                   "T": cfg.T,
                    "d_model": cfg.d, "n_experts": cfg.E, "top_k": cfg.k, "d_ff": cfg.f,
                    "router_bias": cfg.bias or None,
-                   "expert_weights": "fp8-e4m3, per-row power-of-two scale" if fp8 else cfg.dtype},
+                   "expert_weights": "fp8-e4m3, per-row power-of-two scale" if fp8 else cfg.dtype,
+                   "expert_gemm_inputs": "fp8-e4m3, per-row power-of-two scale" if q8 else cfg.dtype},
         "roofline": roof,
         "layer_tflops": layer_tflops,
         "layer_mfma_frac": layer_tflops / peak_mm,
@@ -269,7 +282,7 @@ def main():
         "input_gen_s": t_gen,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens, fp8)
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens, fp8, q8)
     print(json.dumps(out), flush=True)
 
 

@@ -51,6 +51,16 @@
  * computes the layer of the dequantized weights (code value * scale, exact in
  * bf16) with bf16 activations and fp32 accumulation, reading half the weight
  * bytes of the bf16 layer.
+ *
+ * 8-bit activations (COLIBRI_MOE_FLAG_FP8_ACTIVATIONS, on top of FP8_WEIGHTS):
+ * the roadmap's FP8 read as FP8 matrix products. Each expert GEMM input row is
+ * quantized by the same rule (E4M3, one power-of-two scale per row): the token
+ * row x[t] before the gate/up GEMM (the router still sees the full x), and
+ * each assignment's h row, after it is stored as bf16, before the down GEMM.
+ * Both GEMMs then multiply E4M3 by E4M3 on gfx950's fp8 MFMA
+ * (v_mfma_scale_f32_32x32x64_f8f6f4, the scales applied as E8M0 exponents),
+ * exact products summed in fp32. With stage timing, stage 1 includes the x
+ * quantization and stage 3 the h quantization.
  */
 #ifndef COLIBRI_MOE_H
 #define COLIBRI_MOE_H
@@ -67,8 +77,9 @@ typedef enum {
     COLIBRI_MOE_ERR_UNSUPPORTED = 2,  /* d_model not a multiple of 128, d_ff not a multiple of 128
                                          (bf16) or 64 (f32), E > 256, k > 8, max_tokens > 2^24,
                                          max_tokens*k*d_ff, max_tokens*d_model or
-                                         2*d_ff*d_model reaching 2^31, or FP8_WEIGHTS with
-                                         dtype F32 */
+                                         2*d_ff*d_model reaching 2^31, FP8_WEIGHTS with
+                                         dtype F32, FP8_ACTIVATIONS without FP8_WEIGHTS
+                                         or with d_model or d_ff below 256 */
     COLIBRI_MOE_ERR_ALIGNMENT = 3,    /* a tensor pointer not 16-byte aligned */
     COLIBRI_MOE_ERR_OUT_OF_MEMORY = 4,/* init could not allocate its memory */
     COLIBRI_MOE_ERR_HIP = 5           /* a HIP launch, copy or sync failed */
@@ -79,8 +90,10 @@ typedef enum { COLIBRI_MOE_F32 = 0, COLIBRI_MOE_BF16 = 1 } colibri_moe_dtype_t;
 enum {
     COLIBRI_MOE_FLAG_ASYNC = 1u << 0,       /* forward returns after enqueueing */
     COLIBRI_MOE_FLAG_STAGE_TIMING = 1u << 1, /* record per-stage GPU times (hipEvents) */
-    COLIBRI_MOE_FLAG_FP8_WEIGHTS = 1u << 2   /* bf16 only: keep expert weights as 8-bit codes
+    COLIBRI_MOE_FLAG_FP8_WEIGHTS = 1u << 2,  /* bf16 only: keep expert weights as 8-bit codes
                                                 (format above) */
+    COLIBRI_MOE_FLAG_FP8_ACTIVATIONS = 1u << 3 /* with FP8_WEIGHTS, d_model and d_ff >= 256:
+                                                  8-bit expert GEMM inputs, fp8 MFMAs (above) */
 };
 
 typedef struct {

@@ -19,6 +19,7 @@ F32, BF16 = 0, 1
 FLAG_ASYNC = 1 << 0
 FLAG_STAGE_TIMING = 1 << 1
 FLAG_FP8_WEIGHTS = 1 << 2
+FLAG_FP8_ACTIVATIONS = 1 << 3
 STAGES = ("router", "dispatch", "gate_up_gemm", "gate_up_reduce", "down_gemm", "combine")
 
 

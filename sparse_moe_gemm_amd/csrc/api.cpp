@@ -48,6 +48,11 @@ struct colibri_moe {
     float* s_gu;  // fp8 row scales [E][2f] (interleaved rows), else null
     float* s_d;   // fp8 row scales [E][d], else null
     bool fp8;
+    bool q8;      // 8-bit activations too (fp8 MFMA)
+    uint8_t* xq;  // q8: token rows as E4M3 codes [max_tokens][d]
+    float* xsc;   // q8: their scales by sorted position [A]
+    uint8_t* hq;  // q8: h rows as E4M3 codes [A][f]
+    float* hsc;   // q8: their scales [A]
     // workspace, sized for max_tokens
     float* topw;
     int32_t* ids;
@@ -125,6 +130,11 @@ colibri_moe_status_t validate_config(const colibri_moe_config_t* c)
         return COLIBRI_MOE_ERR_UNSUPPORTED;
     if ((c->flags & COLIBRI_MOE_FLAG_FP8_WEIGHTS) && c->dtype != COLIBRI_MOE_BF16)
         return COLIBRI_MOE_ERR_UNSUPPORTED;
+    // 8-bit activations: on top of 8-bit weights; the tiled fp8 GEMMs stream
+    // K in 64-wide stages, at least four.
+    if ((c->flags & COLIBRI_MOE_FLAG_FP8_ACTIVATIONS) &&
+        (!(c->flags & COLIBRI_MOE_FLAG_FP8_WEIGHTS) || c->d_model < 256 || c->d_ff < 256))
+        return COLIBRI_MOE_ERR_UNSUPPORTED;
     // GEMM source offsets are 32-bit element offsets.
     const int64_t lim = (int64_t)1 << 31;
     if ((int64_t)c->max_tokens * c->d_model >= lim || (int64_t)c->max_tokens * c->top_k * c->d_ff >= lim ||
@@ -165,6 +175,10 @@ colibri_moe_status_t init_impl(colibri_moe* h, const colibri_moe_weights_t* w)
     const size_t o_wd = cv.take(E * d * f * wes);
     const size_t o_sgu = h->fp8 ? cv.take(E * 2 * f * sizeof(float)) : 0;
     const size_t o_sd = h->fp8 ? cv.take(E * d * sizeof(float)) : 0;
+    const size_t o_xq = h->q8 ? cv.take((size_t)c.max_tokens * d) : 0;
+    const size_t o_xsc = h->q8 ? cv.take(A * sizeof(float)) : 0;
+    const size_t o_hq = h->q8 ? cv.take(A * f) : 0;
+    const size_t o_hsc = h->q8 ? cv.take(A * sizeof(float)) : 0;
     const size_t o_topw = cv.take(A * sizeof(float));
     const size_t o_ids = cv.take(A * sizeof(int32_t));
     const size_t o_cnt = cv.take(E * sizeof(int32_t));
@@ -196,6 +210,10 @@ colibri_moe_status_t init_impl(colibri_moe* h, const colibri_moe_weights_t* w)
     h->w_d = base + o_wd;
     h->s_gu = h->fp8 ? (float*)(base + o_sgu) : nullptr;
     h->s_d = h->fp8 ? (float*)(base + o_sd) : nullptr;
+    h->xq = h->q8 ? base + o_xq : nullptr;
+    h->xsc = h->q8 ? (float*)(base + o_xsc) : nullptr;
+    h->hq = h->q8 ? base + o_hq : nullptr;
+    h->hsc = h->q8 ? (float*)(base + o_hsc) : nullptr;
     h->topw = (float*)(base + o_topw);
     h->ids = (int32_t*)(base + o_ids);
     h->counts = (int32_t*)(base + o_cnt);
@@ -262,6 +280,7 @@ colibri_moe_status_t colibri_moe_init(colibri_moe_t** out, const colibri_moe_con
     h->esize = cfg->dtype == COLIBRI_MOE_BF16 ? 2 : 4;
     h->timing = (cfg->flags & COLIBRI_MOE_FLAG_STAGE_TIMING) != 0;
     h->fp8 = (cfg->flags & COLIBRI_MOE_FLAG_FP8_WEIGHTS) != 0;
+    h->q8 = (cfg->flags & COLIBRI_MOE_FLAG_FP8_ACTIVATIONS) != 0;
     // Tile order of the grouped GEMMs (tuning only; results do not depend
     // on it): CMOE_GROUP_N n-tiles per group.
     h->group_n = env_int("CMOE_GROUP_N", 64, 1, 1 << 20);
@@ -281,7 +300,7 @@ colibri_moe_status_t colibri_moe_init(colibri_moe_t** out, const colibri_moe_con
         const int64_t amax = (int64_t)cfg->max_tokens * cfg->top_k;
         h->dec_max_a = (int)std::min<int64_t>(amax, env_int("CMOE_DECODE_MAX_A", 256, 0, 1 << 16));
         const int waves = cmoe::decode_waves(h->cus);
-        const int kstep = h->fp8 ? 32 : 16;
+        const int kstep = h->q8 ? 64 : h->fp8 ? 32 : 16;
         h->dec_split_gu = cmoe::decode_split(cfg->n_experts, 2 * cfg->d_ff, cfg->d_model, kstep, waves, 64);
         h->dec_split_dn = cmoe::decode_split(cfg->n_experts, cfg->d_model, cfg->d_ff, kstep, waves, 64);
     }
@@ -342,6 +361,9 @@ colibri_moe_status_t colibri_moe_forward(colibri_moe_t* h, const void* x, int32_
 
     DispatchArgs da{ids, T, c.top_k, c.n_experts, counts, offsets, perm, perm_slot, inv};
     CMOE_HIP(launch_dispatch(da, s));
+    const bool q8 = h->q8;
+    if (q8)  // token rows to 8 bits, scales by sorted position
+        CMOE_HIP(launch_act_quant(x, T, c.d_model, c.top_k, inv, h->xq, h->xsc, s));
     if (tm)
         CMOE_HIP(hipEventRecord(h->ev[2], s));
 
@@ -350,29 +372,33 @@ colibri_moe_status_t colibri_moe_forward(colibri_moe_t* h, const void* x, int32_
     if (bf && A <= h->dec_max_a) {
         // small-batch path: weight streaming with K slices, then the slice sum
         // and SiLU(g)*u
-        DecodeArgs gu{x, h->w_gu, h->s_gu, h->Ys, offsets, perm, A, c.n_experts, c.d_model, c.d_ff,
-                      h->dec_split_gu};
+        DecodeArgs gu{q8 ? (const void*)h->xq : x, h->w_gu, h->s_gu, q8 ? h->xsc : nullptr, h->Ys, offsets, perm,
+                      A, c.n_experts, c.d_model, c.d_ff, h->dec_split_gu};
         CMOE_HIP(launch_decode_gemm(gu, 1, h->cus, s));
         if (tm)
             CMOE_HIP(hipEventRecord(h->ev[3], s));
         CMOE_HIP(launch_decode_silu(h->Ys, h->H, A, c.d_ff, h->dec_split_gu, s));
+        if (q8)
+            CMOE_HIP(launch_act_quant(h->H, A, c.d_ff, 0, nullptr, h->hq, h->hsc, s));
         if (tm)
             CMOE_HIP(hipEventRecord(h->ev[4], s));
-        DecodeArgs dn{h->H, h->w_d, h->s_d, h->Ys, offsets, perm, A, c.n_experts, c.d_model, c.d_ff,
-                      h->dec_split_dn};
+        DecodeArgs dn{q8 ? (const void*)h->hq : h->H, h->w_d, h->s_d, q8 ? h->hsc : nullptr, h->Ys, offsets, perm,
+                      A, c.n_experts, c.d_model, c.d_ff, h->dec_split_dn};
         CMOE_HIP(launch_decode_gemm(dn, 0, h->cus, s));
         split = h->dec_split_dn;
     } else {
-        GemmArgs gu{x,         h->w_gu,   h->s_gu, h->H,      offsets,   perm, A, c.n_experts,
-                    c.top_k,   c.d_model, c.d_ff,  h->group_n, 1,       h->cus};
+        GemmArgs gu{q8 ? (const void*)h->xq : x, h->w_gu, h->s_gu, q8 ? h->xsc : nullptr, h->H, offsets, perm, A,
+                    c.n_experts, c.top_k, c.d_model, c.d_ff, h->group_n, 1, h->cus};
         CMOE_HIP(bf ? launch_gate_up_bf16(gu, s) : launch_gate_up_f32(gu, s));
-        if (tm) {
+        if (tm)
             CMOE_HIP(hipEventRecord(h->ev[3], s));
-            CMOE_HIP(hipEventRecord(h->ev[4], s));  // no separate reduce on this path
-        }
-        split = bf ? down_split_bf16(A, c.n_experts, c.d_model, c.d_ff, h->cus) : 1;
-        GemmArgs dn{h->H,      h->w_d,    h->s_d, h->Ys,      offsets, perm, A, c.n_experts,
-                    c.top_k,   c.d_model, c.d_ff, h->group_n, split,   h->cus};
+        if (q8)  // h rows to 8 bits (the only reduce step on this path)
+            CMOE_HIP(launch_act_quant(h->H, A, c.d_ff, 0, nullptr, h->hq, h->hsc, s));
+        if (tm)
+            CMOE_HIP(hipEventRecord(h->ev[4], s));
+        split = bf ? down_split_bf16(A, c.n_experts, c.d_model, c.d_ff, h->cus, q8 ? 1 : 0) : 1;
+        GemmArgs dn{q8 ? (const void*)h->hq : h->H, h->w_d, h->s_d, q8 ? h->hsc : nullptr, h->Ys, offsets, perm, A,
+                    c.n_experts, c.top_k, c.d_model, c.d_ff, h->group_n, split, h->cus};
         CMOE_HIP(bf ? launch_down_bf16(dn, s) : launch_down_f32(dn, s));
     }
     if (tm)

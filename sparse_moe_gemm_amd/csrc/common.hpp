@@ -93,10 +93,13 @@ struct GemmArgs {
     //   through inv).
     // bf16 weights are in the blocked MFMA layout, fp32 weights row-major;
     // 8-bit weights (scales != null) are E4M3 codes in the fp8 blocked layout
-    // with one fp32 scale per weight row, scales[e*N + n].
+    // with one fp32 scale per weight row, scales[e*N + n]. With a_scales the
+    // A rows are 8-bit too (E4M3 codes, one power-of-two scale per A row,
+    // indexed by sorted position p) and the fp8 MFMA runs (W8A8).
     const void* a;
     const void* b;
     const float* scales;
+    const float* a_scales;
     void* out;
     const int32_t* offsets;   // [E+1]
     const int32_t* perm;      // [A]
@@ -111,7 +114,7 @@ hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t s);
 // K splits the bf16 down GEMM uses for a call with A = T*k assignments on
 // `cus` compute units (1 or 2; the Ys workspace holds kMaxSplit partials).
 constexpr int kMaxSplit = 2;
-int down_split_bf16(int A, int E, int d, int f, int cus);
+int down_split_bf16(int A, int E, int d, int f, int cus, int q8);
 hipError_t launch_gate_up_f32(const GemmArgs& a, hipStream_t s);
 hipError_t launch_down_f32(const GemmArgs& a, hipStream_t s);
 
@@ -120,6 +123,7 @@ struct DecodeArgs {
     const void* a;            // gate/up: x [T][d] (rows through perm); down: H [A][f]
     const void* b;            // blocked bf16 or fp8 weights (as in the grouped GEMMs)
     const float* scales;      // fp8 row scales [E][N], or null for bf16 weights
+    const float* a_scales;    // W8A8: A is E4M3 codes, row scales by sorted position; else null
     float* part;              // fp32 slice partials [split][A][N], N = 2f (gate/up) or d (down)
     const int32_t* offsets;   // [E+1]
     const int32_t* perm;      // [A]
@@ -145,6 +149,11 @@ hipError_t launch_fp8_row_scales(const void* w0, const void* w1, float* scales, 
 // interleaved when w1 != null), scaled by the row scales.
 hipError_t launch_fp8_pack_blocked(const void* w0, const void* w1, const float* scales, void* out, int E, int N,
                                    int K, hipStream_t s);
+// 8-bit activation rows: codes [rows][cols] of a bf16 [rows][cols] matrix and
+// the rows' power-of-two scales, at scales[row], or with inv at
+// scales[inv[row*k + j]] for j < k.
+hipError_t launch_act_quant(const void* x, int64_t rows, int cols, int k, const int32_t* inv, uint8_t* codes,
+                            float* scales, hipStream_t s);
 // Row-major E4M3 codes of [rows][cols] bf16 with the given row scales.
 hipError_t launch_fp8_encode_rows(const void* w, const float* scales, uint8_t* codes, int64_t rows, int cols,
                                   hipStream_t s);

@@ -233,6 +233,129 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
 }
 
+// 8-bit weights and activations (W8A8): the same items in 64-wide k steps on
+// v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, per-lane E8M0 scales). A lane
+// takes, of each step, k 16*(l/32) .. +16 of both 32-k halves: activation
+// chunks l/32 and 2 + l/32 of the row's 64 codes, and its 16 bytes of the two
+// 1 KiB weight blocks of the step.
+__device__ __forceinline__ int e8m0_byte(float s)
+{
+    return (int)((__float_as_uint(s) >> 23) & 0xFFu);
+}
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ v8i cat16(const Vec16& lo, const Vec16& hi)
+{
+    return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+template <bool GATE_UP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_gemm_q8_kernel(DecodeArgs g)
+{
+    constexpr bool gate_up = GATE_UP;
+    constexpr int kQ = 3;  // 64-wide k steps of loads in flight per wave (two sets)
+    const int lane = threadIdx.x % kWave;
+    const int W = gridDim.x * (kThreads / kWave);
+    const int w0 = blockIdx.x * (kThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int N = gate_up ? 2 * g.f : g.d;
+    const int K = gate_up ? g.d : g.f;
+    const int NB = N / 32, KB = K / 64, KB32 = K / 32, S = g.split;
+    const int NB2 = NB / 2;
+    const int items = g.E * NB2 * S;
+    const Vec16* B = (const Vec16*)g.b;
+    const uint8_t* Abase = (const uint8_t*)g.a;
+
+    for (int it = w0; it < items; it += W) {
+        const int s = it % S;
+        const int rest = it / S;
+        const int nb = (rest % NB2) * 2;
+        const int e = rest / NB2;
+        const int seg0 = g.offsets[e];
+        const int cnt = g.offsets[e + 1] - seg0;
+        if (cnt <= 0)
+            continue;
+        const int kb0 = (int)((int64_t)s * KB / S), kb1 = (int)((int64_t)(s + 1) * KB / S);
+        // lane's 16 bytes of 1 KiB block q of row block nb: bp[q * 64]
+        const Vec16* bp = B + ((int64_t)e * NB + nb) * KB32 * kWave + lane;
+        const int64_t bst = (int64_t)KB32 * kWave;  // next weight block
+        const int sb0 = e8m0_byte(g.scales[(int64_t)e * N + nb * 32 + (lane & 31)]);
+        const int sb1 = e8m0_byte(g.scales[(int64_t)e * N + nb * 32 + 32 + (lane & 31)]);
+        float* out = g.part + (int64_t)s * g.A * N + nb * 32 + (lane & 31);
+
+        for (int r0 = 0; r0 < cnt; r0 += 32) {
+            const int r = min(r0 + (lane & 31), cnt - 1);
+            const int src = gate_up ? g.perm[seg0 + r] : seg0 + r;
+            const int sa = e8m0_byte(g.a_scales[seg0 + r]);
+            // 16-byte chunk c of step kb of the row: ap[kb * 4 + c]
+            const Vec16* ap = (const Vec16*)(Abase + (int64_t)src * K) + (lane >> 5);
+            floatx16 acc0, acc1;
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                acc0[q] = acc1[q] = 0.f;
+            Vec16 a0[kQ][2], b0[kQ][2], c0[kQ][2], a1[kQ][2], b1[kQ][2], c1[kQ][2];
+#pragma unroll
+            for (int i = 0; i < kQ; ++i) {
+                const int kb = min(kb0 + i, kb1 - 1);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    a0[i][h] = ap[kb * 4 + 2 * h];
+                    b0[i][h] = bp[(int64_t)(2 * kb + h) * kWave];
+                    c0[i][h] = bp[bst + (int64_t)(2 * kb + h) * kWave];
+                }
+            }
+            for (int kb = kb0; kb < kb1; kb += 2 * kQ) {
+#pragma unroll
+                for (int i = 0; i < kQ; ++i) {
+                    const int kk = min(kb + kQ + i, kb1 - 1);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        a1[i][h] = ap[kk * 4 + 2 * h];
+                        b1[i][h] = bp[(int64_t)(2 * kk + h) * kWave];
+                        c1[i][h] = bp[bst + (int64_t)(2 * kk + h) * kWave];
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < kQ; ++i)
+                    if (kb + i < kb1) {
+                        const v8i fa = cat16(a0[i][0], a0[i][1]);
+                        acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, cat16(b0[i][0], b0[i][1]), acc0, 0, 0,
+                                                                               0, sa, 0, sb0);
+                        acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, cat16(c0[i][0], c0[i][1]), acc1, 0, 0,
+                                                                               0, sa, 0, sb1);
+                    }
+#pragma unroll
+                for (int i = 0; i < kQ; ++i) {
+                    const int kk = min(kb + 2 * kQ + i, kb1 - 1);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        a0[i][h] = ap[kk * 4 + 2 * h];
+                        b0[i][h] = bp[(int64_t)(2 * kk + h) * kWave];
+                        c0[i][h] = bp[bst + (int64_t)(2 * kk + h) * kWave];
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < kQ; ++i)
+                    if (kb + kQ + i < kb1) {
+                        const v8i fa = cat16(a1[i][0], a1[i][1]);
+                        acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, cat16(b1[i][0], b1[i][1]), acc0, 0, 0,
+                                                                               0, sa, 0, sb0);
+                        acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, cat16(c1[i][0], c1[i][1]), acc1, 0, 0,
+                                                                               0, sa, 0, sb1);
+                    }
+            }
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int row = r0 + 8 * (q / 4) + 4 * (lane >> 5) + (q % 4);
+                if (row < cnt) {
+                    out[(int64_t)(seg0 + row) * N] = acc0[q];
+                    out[(int64_t)(seg0 + row) * N + 32] = acc1[q];
+                }
+            }
+        }
+    }
+}
+
 // H[p][c] = bf16(SiLU(sum_s P[s][p][gate row of c]) * sum_s P[s][p][up row of c]),
 // with gate/up interleaved by 32 rows: h column c is gate row (c/32)*64 + c%32
 // and up row (c/32)*64 + 32 + c%32 of the combined [2f] weight rows. Four
@@ -289,7 +412,12 @@ int decode_split(int E, int N, int K, int kstep, int waves, int max_split)
 
 hipError_t launch_decode_gemm(const DecodeArgs& a, int gate_up, int cus, hipStream_t s)
 {
-    if (a.scales) {
+    if (a.a_scales) {
+        if (gate_up)
+            hipLaunchKernelGGL(decode_gemm_q8_kernel<true>, dim3(cus * 2), dim3(kThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL(decode_gemm_q8_kernel<false>, dim3(cus * 2), dim3(kThreads), 0, s, a);
+    } else if (a.scales) {
         if (gate_up)
             hipLaunchKernelGGL(decode_gemm_f8_kernel<true>, dim3(cus * 2), dim3(kThreads), 0, s, a);
         else

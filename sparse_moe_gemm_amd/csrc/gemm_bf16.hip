@@ -294,6 +294,112 @@ __device__ __forceinline__ void stage(const i32x4& ra, const LoadSrc<A_INS>& ls,
     }
 }
 
+// ---------------------------------------------------------------------------
+// 8-bit activations and weights (Q8): v_mfma_scale_f32_32x32x64_f8f6f4, E4M3 x
+// E4M3, one 64-wide k step per stage. A stage has the bf16 stage's shape in
+// bytes: A rows of 64 codes (four 16-byte chunks, swizzled as for bf16), and
+// per 32 weight rows two 1 KiB blocks (k 0..31 and 32..63 of the stage in the
+// 8-bit weight layout). The MFMA's lane l takes row l%32 and, in its 32
+// bytes, k 16*(l/32) .. +16 of the first 32-k half and the same of the second:
+// A chunks l/32 and 2 + l/32, and the lane's 16 bytes of both weight blocks.
+// Each lane's operands are scaled by 2^(byte - 127) per operand (the rows'
+// power-of-two scales, E8M0); products and sums are exact fp8 products summed
+// in fp32.
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ v8i cat16(const Vec16& lo, const Vec16& hi)
+{
+    return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+// E8M0 byte of a power-of-two fp32 scale (its biased exponent).
+__device__ __forceinline__ int e8m0(float s)
+{
+    return (int)((__float_as_uint(s) >> 23) & 0xFFu);
+}
+
+template <int BM, int BN, int WM, int WN>
+struct FragReaderQ8 {
+    const Stage<BM, BN, false>* st;
+    int wm, wn, lane;
+    __device__ __forceinline__ v8i a(int i) const
+    {
+        const int lr = lane & 31, h = lane >> 5, sw = (lr >> 2) & 3;
+        const Vec16* row = st->a + (wm * WM + i * 32 + lr) * kCH;
+        return cat16(row[h ^ sw], row[(2 + h) ^ sw]);
+    }
+    __device__ __forceinline__ v8i b(int j) const
+    {
+        const int rb = wn * (WN / 32) + j;
+        return cat16(st->b[(rb * 2) * 64 + lane], st->b[(rb * 2 + 1) * 64 + lane]);
+    }
+};
+
+// One Q8 stage, pipelined like the bf16 one: first half = the MFMAs of the
+// wave's first two 32-row groups (fragments read during the previous stage)
+// while the other two groups' A fragments of this stage are read; middle =
+// the same wait and barrier; second half = the last two row groups' MFMAs,
+// ordered by weight block, each block's fragment re-read for the next stage
+// as soon as its last MFMA is issued, then the next stage's first A
+// fragments. Half of the loads in each half.
+template <int BM, int BN, int WM, int WN, int A_INS, int B_INS>
+__device__ __forceinline__ void stage_q8(const i32x4& ra, const LoadSrc<A_INS>& ls, uint32_t ld_lds, int KB, int wv,
+                                         uint32_t lane16, const Stage<BM, BN, false>* st,
+                                         const Stage<BM, BN, false>* st_next, int wm, int wn, int lane,
+                                         v8i (&fa)[2], v8i (&fb)[WN / 32], const int (&sa)[WM / 32],
+                                         const int (&sb)[WN / 32], floatx16 (&acc)[WM / 32][WN / 32])
+{
+    constexpr int MI = WM / 32, NI = WN / 32;
+    constexpr int NLD = A_INS + B_INS;
+    constexpr int M = 2 * NI;    // MFMAs per half
+    constexpr int L0 = NLD / 2;  // loads in the first half
+    static_assert(MI == 4, "two row groups per half");
+    const FragReaderQ8<BM, BN, WM, WN> rd{st, wm, wn, lane}, rn{st_next, wm, wn, lane};
+    v8i ga[2];
+
+    int nld = 0;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const int i = m / NI, j = m % NI;
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, sa[i], 0, sb[j]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (m == 0 || m == NI / 2) {
+            ga[m == 0 ? 0 : 1] = rd.a(m == 0 ? 2 : 3);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (; nld < ((m + 1) * L0) / M; ++nld) {
+            issue_load<BM, BN, false, A_INS, B_INS>(nld, ra, ls, KB, wv, lane16, ld_lds);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(%0)" ::"n"(2 * NLD + L0) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const int j = m / 2, ii = m % 2;
+        acc[2 + ii][j] =
+            __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ga[ii], fb[j], acc[2 + ii][j], 0, 0, 0, sa[2 + ii], 0, sb[j]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (ii == 1) {
+            fb[j] = rn.b(j);
+            __builtin_amdgcn_sched_barrier(0);
+            if (j >= NI - 2) {
+                fa[j - (NI - 2)] = rn.a(j - (NI - 2));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (; nld < L0 + ((m + 1) * (NLD - L0)) / M; ++nld) {
+            issue_load<BM, BN, false, A_INS, B_INS>(nld, ra, ls, KB, wv, lane16, ld_lds);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
 // Per-lane view of the m-tiles: lane l holds experts 4l .. 4l+3 (E <= 256).
 struct TileTable {
     int off[4];  // segment start offsets[e]
@@ -440,6 +546,59 @@ __device__ __forceinline__ void tile_stages(const i32x4& ra, const LoadSrc<A_INS
     } while (++j < nkt);
 }
 
+// tile_stages for Q8 (same stream, stage_q8 per stage).
+template <int BM, int BN, int WM, int WN, int A_INS, int B_INS>
+__device__ __forceinline__ void tile_stages_q8(const i32x4& ra, const LoadSrc<A_INS>& cs, int nkt, bool has_nxt,
+                                               const i32x4& nrb, int nkt0, const uint32_t (&cpart)[A_INS],
+                                               uint32_t Kbytes, int KB, int wv, uint32_t lane16,
+                                               Ring<BM, BN, false, false>& ring, uint32_t ring0, int& b, int wm,
+                                               int wn, int lane, v8i (&fa)[2], v8i (&fb)[WN / 32],
+                                               const int (&sa)[WM / 32], const int (&sb)[WN / 32],
+                                               const uint32_t (&held)[A_INS], floatx16 (&acc)[WM / 32][WN / 32])
+{
+    constexpr uint32_t kStageBytes = sizeof(Stage<BM, BN, false>);
+    int j = 0;
+    do {
+        const int ja = j + kAhead;
+        LoadSrc<A_INS> ls = cs;
+        if (ja < nkt) {
+            ls.kt = cs.kt + ja;
+        } else if (has_nxt) {
+            ls.rb = nrb;
+#pragma unroll
+            for (int i = 0; i < A_INS; ++i)
+                ls.aoff[i] = held[i] * Kbytes + cpart[i];
+            ls.kt = nkt0 + (ja - nkt);
+        } else {
+            ls.kt = cs.kt + nkt - 1;
+        }
+        ls.kt = __builtin_amdgcn_readfirstlane(ls.kt);
+        const int bl = b + kAhead >= kRing ? b + kAhead - kRing : b + kAhead;
+        const int bn = b + 1 >= kRing ? 0 : b + 1;
+        stage_q8<BM, BN, WM, WN, A_INS, B_INS>(ra, ls, ring0 + (uint32_t)bl * kStageBytes, KB, wv, lane16,
+                                               &ring.st[b], &ring.st[bn], wm, wn, lane, fa, fb, sa, sb, acc);
+        b = bn;
+    } while (++j < nkt);
+}
+
+// Per-lane scales of a Q8 tile: A rows wm*WM + i*32 + lane%32 (clamped to the
+// tile's valid rows, as the rows themselves) from a_scales by sorted
+// position, weight rows as load_scales. Raw fp32 values: they become E8M0
+// bytes (e8m0) only after the loads are pinned, so that no use waits for
+// them early.
+template <int BN, int WM, int WN>
+__device__ __forceinline__ void load_scales_q8(const float* a_scales, const float* b_scales, const Tile& t, int N,
+                                               int wm, int wn, int lane, float (&sa)[WM / 32], float (&sb)[WN / 32])
+{
+#pragma unroll
+    for (int i = 0; i < WM / 32; ++i)
+        sa[i] = a_scales[t.row0 + min(wm * WM + i * 32 + (lane & 31), t.rows - 1)];
+    const float* p = b_scales + (int64_t)t.e * N + t.n * BN + wn * WN + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < WN / 32; ++j)
+        sb[j] = p[j * 32];
+}
+
 // Source row of slot r of a tile's A rows: token perm[p] (gate/up) or the
 // sorted position p itself (down); rows past the segment end are clamped to
 // its last row (their results are never stored).
@@ -462,9 +621,13 @@ __device__ __forceinline__ void load_scales(const float* scales, const Tile& t, 
         sc[j] = p[j * 32];
 }
 
-template <int BM, int BN, int WM, int WN, bool GATE_UP, bool F8>
+// F8: 8-bit weights multiplied as bf16 (W8A16); Q8: 8-bit weights and
+// activations on the fp8 MFMA (W8A8; F8 is false then: the stage has the
+// bf16 layout's shape).
+template <int BM, int BN, int WM, int WN, bool GATE_UP, bool F8, bool Q8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void grouped_gemm_kernel(GemmArgs g)
 {
+    static_assert(!(F8 && Q8), "one weight mode");
     constexpr int WAVES_N = BN / WN;
     constexpr int MI = WM / 32, NI = WN / 32;
     constexpr int A_INS = BM * kCH / 64 / 4;             // A loads per wave per stage
@@ -482,8 +645,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int N = GATE_UP ? 2 * g.f : g.d;  // weight rows per expert
     const int K = GATE_UP ? g.d : g.f;
     const int NT = N / BN;
-    const int KB = K / (F8 ? 32 : 16);  // 1 KiB weight blocks per weight row block
-    const int KT = K / kBK;  // K stages (a multiple of 4, at least 4)
+    const int KB = K / (F8 || Q8 ? 32 : 16);  // 1 KiB weight blocks per weight row block
+    const int KT = K / (Q8 ? 64 : kBK);       // K stages (at least kAhead)
     const int S = GATE_UP ? 1 : g.split;
     const int lane = threadIdx.x % kWave;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -497,7 +660,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int G = gridDim.x;
 
     // Per-lane slot rows and swizzled chunk byte offsets of this wave's A loads.
-    const uint32_t Kbytes = (uint32_t)K * 2u;
+    const uint32_t Kbytes = (uint32_t)K * (Q8 ? 1u : 2u);
     int slot[A_INS];
     uint32_t cpart[A_INS];
 #pragma unroll
@@ -544,6 +707,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         for (int j = 0; j < NI; ++j)
             asm volatile("" : "+v"(sc[j]) : : "memory");
     }
+    int sa[MI], sb[NI];  // Q8: E8M0 row scales of the current tile
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+        sa[i] = 127;
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+        sb[j] = 127;
+    if constexpr (Q8) {
+        float fa_s[MI], fb_s[NI];
+        load_scales_q8<BN, WM, WN>(g.a_scales, g.scales, cur, N, wm, wn, lane, fa_s, fb_s);
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            asm volatile("" : "+v"(fa_s[i]) : : "memory");
+            sa[i] = e8m0(fa_s[i]);
+        }
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            asm volatile("" : "+v"(fb_s[j]) : : "memory");
+            sb[j] = e8m0(fb_s[j]);
+        }
+    }
 
     floatx16 acc[MI][NI];
 #pragma unroll
@@ -572,7 +756,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     asm volatile("" ::: "memory");
     bf16x8 fa[MI];
     typename BFrag<F8>::raw fb[NI];
-    {
+    v8i qa[2], qb[NI];  // Q8 fragments
+    if constexpr (Q8) {
+        const FragReaderQ8<BM, BN, WM, WN> r0{&ring.st[0], wm, wn, lane};
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+            qb[j] = r0.b(j);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            qa[i] = r0.a(i);
+    } else {
         const FragReader<BM, BN, WM, WN, F8> r0{&ring.st[0], wm, wn, lane};
 #pragma unroll
         for (int j = 0; j < NI; ++j)
@@ -584,9 +777,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     int b = 0;
 
     for (;;) {
-        tile_stages<BM, BN, WM, WN, F8, EPBUF, A_INS, B_INS>(ra, cs, cur.nkt, has_nxt, nrb, nxt.kt0, cpart, Kbytes,
-                                                             KB, wv, lane16, ring, ring0, b, wm, wn, lane, fa, fb,
-                                                             sc, held, acc);
+        if constexpr (Q8)
+            tile_stages_q8<BM, BN, WM, WN, A_INS, B_INS>(ra, cs, cur.nkt, has_nxt, nrb, nxt.kt0, cpart, Kbytes, KB,
+                                                         wv, lane16, ring, ring0, b, wm, wn, lane, qa, qb, sa, sb,
+                                                         held, acc);
+        else
+            tile_stages<BM, BN, WM, WN, F8, EPBUF, A_INS, B_INS>(ra, cs, cur.nkt, has_nxt, nrb, nxt.kt0, cpart,
+                                                                 Kbytes, KB, wv, lane16, ring, ring0, b, wm, wn, lane,
+                                                                 fa, fb, sc, held, acc);
 
         // The tile after next: decode it and fetch its token rows now, so the
         // fetch overlaps the epilogue. Its first use is pinned after the
@@ -616,6 +814,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         if constexpr (F8)
             if (has_nxt)
                 load_scales<BN, WN>(g.scales, nxt, N, wn, lane, nsc);
+        float nsa[MI], nsb[NI];
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+            nsa[i] = 1.0f;
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+            nsb[j] = 1.0f;
+        if constexpr (Q8)
+            if (has_nxt)
+                load_scales_q8<BN, WM, WN>(g.a_scales, g.scales, nxt, N, wm, wn, lane, nsa, nsb);
 
         // Epilogue of the tile. 32x32 accumulator layout: lane holds column
         // lane%32 and, for q = 0..15, row 8*(q/4) + 4*(lane/32) + q%4. Rows
@@ -713,6 +921,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             for (int j = 0; j < NI; ++j)
                 asm volatile("" : "+v"(nsc[j]) : : "memory");
         }
+        if constexpr (Q8) {
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+                asm volatile("" : "+v"(nsa[i]) : : "memory");
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
+                asm volatile("" : "+v"(nsb[j]) : : "memory");
+        }
         if (!has_nxt)
             break;
 
@@ -733,6 +949,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
         for (int j = 0; j < NI; ++j)
             sc[j] = nsc[j];
+        if constexpr (Q8) {
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+                sa[i] = e8m0(nsa[i]);
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
+                sb[j] = e8m0(nsb[j]);
+        }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the trailing reloads
 }
@@ -796,18 +1020,18 @@ __global__ void interleave_gate_up_kernel(const uint8_t* wg, const uint8_t* wu, 
 // 128), 256x128 tiles (waves of 128x64, 5 x 24 KiB stages).
 constexpr int kBM = 256;
 
-int down_split_bf16(int A, int E, int d, int f, int cus)
+int down_split_bf16(int A, int E, int d, int f, int cus, int q8)
 {
     // Split K in two when the down GEMM has fewer than three tiles per compute
     // unit: whole-tile rounds then waste much of the last round, and halves
     // fill it better at the price of one more fp32 partial for combine to read.
     const int BN = d % 256 == 0 ? 256 : 128;
     const int64_t tiles = ((int64_t)A / kBM + E) * (d / BN);
-    const int KT = f / kBK;
+    const int KT = f / (q8 ? 64 : kBK);
     return (KT >= 16 && tiles < 3 * (int64_t)cus) ? 2 : 1;
 }
 
-template <bool GATE_UP, bool F8>
+template <bool GATE_UP, bool F8, bool Q8>
 hipError_t launch_grouped(const GemmArgs& a, hipStream_t s)
 {
     const int N = GATE_UP ? 2 * a.f : a.d;
@@ -819,27 +1043,31 @@ hipError_t launch_grouped(const GemmArgs& a, hipStream_t s)
         return hipSuccess;
     if constexpr (GATE_UP) {
         // 2 * d_ff is a multiple of 256 (d_ff % 128 == 0 is checked at init)
-        hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 256, 128, 128, true, F8>), dim3(grid), dim3(kThreads), 0, s,
-                           a);
+        hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 256, 128, 128, true, F8, Q8>), dim3(grid), dim3(kThreads), 0,
+                           s, a);
     } else {
         if (BN == 256)
-            hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 256, 128, 128, false, F8>), dim3(grid), dim3(kThreads), 0,
-                               s, a);
+            hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 256, 128, 128, false, F8, Q8>), dim3(grid), dim3(kThreads),
+                               0, s, a);
         else
-            hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 128, 128, 64, false, F8>), dim3(grid), dim3(kThreads), 0,
-                               s, a);
+            hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 128, 128, 64, false, F8, Q8>), dim3(grid), dim3(kThreads),
+                               0, s, a);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t s)
 {
-    return a.scales ? launch_grouped<true, true>(a, s) : launch_grouped<true, false>(a, s);
+    if (a.a_scales)
+        return launch_grouped<true, false, true>(a, s);
+    return a.scales ? launch_grouped<true, true, false>(a, s) : launch_grouped<true, false, false>(a, s);
 }
 
 hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t s)
 {
-    return a.scales ? launch_grouped<false, true>(a, s) : launch_grouped<false, false>(a, s);
+    if (a.a_scales)
+        return launch_grouped<false, false, true>(a, s);
+    return a.scales ? launch_grouped<false, true, false>(a, s) : launch_grouped<false, false, false>(a, s);
 }
 
 hipError_t launch_pack_blocked(const void* w0, const void* w1, void* out, int E, int N, int K, int gate_up,

@@ -175,7 +175,55 @@ __global__ __launch_bounds__(256) void fp8_encode_rows_kernel(const uint16_t* w,
     }
 }
 
+// 8-bit activation rows (the layer's optional W8A8 mode): row t of a [rows][cols]
+// bf16 matrix becomes codes [rows][cols] with its power-of-two scale (the
+// weights' rule), one wave per row. The scale goes to scales[t], or, with
+// inv, to scales[inv[t*k + j]] for each of token t's k assignments (the
+// sorted positions the GEMMs index their A rows by).
+__global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* x, int64_t rows, int cols, int k,
+                                                        const int32_t* inv, uint8_t* codes, float* scales)
+{
+    const int lane = threadIdx.x % kWave;
+    const int64_t nw = (int64_t)gridDim.x * (blockDim.x / kWave);
+    for (int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; t < rows; t += nw) {
+        const uint16_t* src = x + t * (int64_t)cols;
+        float amax = 0.f;
+        for (int c = lane * 8; c < cols; c += kWave * 8) {
+            const Vec16 v = *(const Vec16*)(src + c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                amax = fmaxf(amax, fabsf(__uint_as_float(v[i] << 16)));
+                amax = fmaxf(amax, fabsf(__uint_as_float(v[i] & 0xFFFF0000u)));
+            }
+        }
+#pragma unroll
+        for (int o = kWave / 2; o > 0; o >>= 1)
+            amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+        const int e = fp8_scale_exp(amax);
+        const float inv_s = ldexpf(1.0f, -e);  // exact: multiplying by it is exact
+        for (int c = lane * 8; c < cols; c += kWave * 8)
+            *(uint2*)(codes + t * (int64_t)cols + c) = encode8(*(const Vec16*)(src + c), inv_s);
+        if (inv) {
+            if (lane < k)
+                scales[inv[t * k + lane]] = ldexpf(1.0f, e);
+        } else if (lane == 0) {
+            scales[t] = ldexpf(1.0f, e);
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_act_quant(const void* x, int64_t rows, int cols, int k, const int32_t* inv, uint8_t* codes,
+                            float* scales, hipStream_t s)
+{
+    const int64_t blocks = std::min<int64_t>((rows + 3) / 4, 8192);
+    if (blocks < 1)
+        return hipSuccess;
+    hipLaunchKernelGGL(act_quant_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const uint16_t*)x, rows, cols, k,
+                       inv, codes, scales);
+    return hipGetLastError();
+}
 
 hipError_t launch_fp8_row_scales(const void* w0, const void* w1, float* scales, int64_t rows, int rows_per_e, int cols,
                                  hipStream_t s)

@@ -81,8 +81,10 @@ def sample_tokens(g: dict, T: int, n_random: int = 16, seed: int = 0) -> np.ndar
 
 
 def compare(cfg: synth.LayerConfig, inp: dict, g: dict, tokens: np.ndarray | None = None,
-            ref_layer: oracle.Layer | None = None) -> dict:
-    """Assert every rule in the module docstring; returns a small report."""
+            ref_layer: oracle.Layer | None = None, act_fp8: bool = False, tol_y: float | None = None) -> dict:
+    """Assert every rule in the module docstring; returns a small report.
+    act_fp8: the reference y is the oracle's 8-bit activation mode; tol_y
+    replaces the dtype's per-token y tolerance."""
     x = inp["x"]
     T, k, E = x.shape[0], cfg.k, cfg.E
     L = ref_layer or oracle.Layer.from_inputs(inp, k)
@@ -111,12 +113,12 @@ def compare(cfg: synth.LayerConfig, inp: dict, g: dict, tokens: np.ndarray | Non
         assert np.array_equal(g["perm"], d_ref["perm"]) and np.array_equal(g["expert_counts"], d_ref["counts"])
 
     toks = np.arange(T, dtype=np.int32) if tokens is None else np.asarray(tokens, np.int32)
-    y_ref = L.forward(x, tokens=toks, forced_ids=g["topk_ids"])
+    y_ref = L.forward(x, tokens=toks, forced_ids=g["topk_ids"], act_fp8=act_fp8)
     y = g["y"][toks]
     den = np.max(np.abs(y_ref), axis=1)
     err = np.max(np.abs(y - y_ref), axis=1) / np.where(den > 0, den, 1.0)
-    tol = TOL_Y[cfg.dtype]
+    tol = TOL_Y[cfg.dtype] if tol_y is None else tol_y
     worst = int(np.argmax(err))
     assert err.max() <= tol, f"y per-token error {err.max():.3e} > {tol} at token {toks[worst]}"
-    return dict(max_err=float(err.max()), near_ties=int(near.sum()), tokens_checked=int(toks.size),
-                empty_experts=int((g["expert_counts"] == 0).sum()))
+    return dict(max_err=float(err.max()), mean_err=float(err.mean()), near_ties=int(near.sum()),
+                tokens_checked=int(toks.size), empty_experts=int((g["expert_counts"] == 0).sum()))

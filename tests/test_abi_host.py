@@ -62,6 +62,9 @@ FAKE = 0x100000  # never dereferenced: validation fails before any use
     (dict(d_ff=192), cm.ERR_UNSUPPORTED),
     (dict(max_tokens=(1 << 24) + 1), cm.ERR_UNSUPPORTED),
     (dict(dtype=cm.F32, flags=cm.FLAG_FP8_WEIGHTS), cm.ERR_UNSUPPORTED),
+    (dict(flags=cm.FLAG_FP8_ACTIVATIONS), cm.ERR_UNSUPPORTED),
+    (dict(flags=cm.FLAG_FP8_WEIGHTS | cm.FLAG_FP8_ACTIVATIONS), cm.ERR_UNSUPPORTED),  # d_ff = 128
+    (dict(d_model=128, d_ff=256, flags=cm.FLAG_FP8_WEIGHTS | cm.FLAG_FP8_ACTIVATIONS), cm.ERR_UNSUPPORTED),
 ])
 def test_init_rejects_bad_configs(kw, status):
     w = cm.Weights(FAKE, None, FAKE, FAKE, FAKE)

@@ -180,33 +180,70 @@ __global__ __launch_bounds__(256) void fp8_encode_rows_kernel(const uint16_t* w,
 // weights' rule), one wave per row. The scale goes to scales[t], or, with
 // inv, to scales[inv[t*k + j]] for each of token t's k assignments (the
 // sorted positions the GEMMs index their A rows by).
+// One 256-thread block per row: a row of up to kActChunks * 2048 values is
+// read once into registers (every load in flight together), its largest
+// magnitude reduced across the block, then encoded from the registers;
+// longer rows are read twice.
+constexpr int kActChunks = 8;
+
+__device__ __forceinline__ float amax8(const Vec16& v, float amax)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        amax = fmaxf(amax, fabsf(__uint_as_float(v[i] << 16)));
+        amax = fmaxf(amax, fabsf(__uint_as_float(v[i] & 0xFFFF0000u)));
+    }
+    return amax;
+}
+
 __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* x, int64_t rows, int cols, int k,
                                                         const int32_t* inv, uint8_t* codes, float* scales)
 {
-    const int lane = threadIdx.x % kWave;
-    const int64_t nw = (int64_t)gridDim.x * (blockDim.x / kWave);
-    for (int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; t < rows; t += nw) {
+    __shared__ float red[256 / kWave];
+    const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+    const int step = 256 * 8;  // values per block-wide chunk
+    for (int64_t t = blockIdx.x; t < rows; t += gridDim.x) {
         const uint16_t* src = x + t * (int64_t)cols;
+        uint8_t* dst = codes + t * (int64_t)cols;
+        const bool regs = cols <= kActChunks * step;
+        Vec16 v[kActChunks];
         float amax = 0.f;
-        for (int c = lane * 8; c < cols; c += kWave * 8) {
-            const Vec16 v = *(const Vec16*)(src + c);
+        if (regs) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                amax = fmaxf(amax, fabsf(__uint_as_float(v[i] << 16)));
-                amax = fmaxf(amax, fabsf(__uint_as_float(v[i] & 0xFFFF0000u)));
-            }
+            for (int i = 0; i < kActChunks; ++i)
+                if (tid * 8 + i * step < cols)
+                    v[i] = *(const Vec16*)(src + tid * 8 + i * step);
+#pragma unroll
+            for (int i = 0; i < kActChunks; ++i)
+                if (tid * 8 + i * step < cols)
+                    amax = amax8(v[i], amax);
+        } else {
+            for (int c = tid * 8; c < cols; c += step)
+                amax = amax8(*(const Vec16*)(src + c), amax);
         }
 #pragma unroll
         for (int o = kWave / 2; o > 0; o >>= 1)
             amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+        if (lane == 0)
+            red[wv] = amax;
+        __syncthreads();
+        amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        __syncthreads();  // red is reused by the next row
         const int e = fp8_scale_exp(amax);
         const float inv_s = ldexpf(1.0f, -e);  // exact: multiplying by it is exact
-        for (int c = lane * 8; c < cols; c += kWave * 8)
-            *(uint2*)(codes + t * (int64_t)cols + c) = encode8(*(const Vec16*)(src + c), inv_s);
+        if (regs) {
+#pragma unroll
+            for (int i = 0; i < kActChunks; ++i)
+                if (tid * 8 + i * step < cols)
+                    *(uint2*)(dst + tid * 8 + i * step) = encode8(v[i], inv_s);
+        } else {
+            for (int c = tid * 8; c < cols; c += step)
+                *(uint2*)(dst + c) = encode8(*(const Vec16*)(src + c), inv_s);
+        }
         if (inv) {
-            if (lane < k)
-                scales[inv[t * k + lane]] = ldexpf(1.0f, e);
-        } else if (lane == 0) {
+            if (tid < k)
+                scales[inv[t * k + tid]] = ldexpf(1.0f, e);
+        } else if (tid == 0) {
             scales[t] = ldexpf(1.0f, e);
         }
     }
@@ -217,7 +254,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* x, int64
 hipError_t launch_act_quant(const void* x, int64_t rows, int cols, int k, const int32_t* inv, uint8_t* codes,
                             float* scales, hipStream_t s)
 {
-    const int64_t blocks = std::min<int64_t>((rows + 3) / 4, 8192);
+    const int64_t blocks = std::min<int64_t>(rows, 16384);
     if (blocks < 1)
         return hipSuccess;
     hipLaunchKernelGGL(act_quant_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const uint16_t*)x, rows, cols, k,

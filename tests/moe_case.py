@@ -120,5 +120,6 @@ def compare(cfg: synth.LayerConfig, inp: dict, g: dict, tokens: np.ndarray | Non
     tol = TOL_Y[cfg.dtype] if tol_y is None else tol_y
     worst = int(np.argmax(err))
     assert err.max() <= tol, f"y per-token error {err.max():.3e} > {tol} at token {toks[worst]}"
-    return dict(max_err=float(err.max()), mean_err=float(err.mean()), near_ties=int(near.sum()),
-                tokens_checked=int(toks.size), empty_experts=int((g["expert_counts"] == 0).sum()))
+    return dict(max_err=float(err.max()), mean_err=float(err.mean()), over_2e2=int((err > 2e-2).sum()),
+                near_ties=int(near.sum()), tokens_checked=int(toks.size),
+                empty_experts=int((g["expert_counts"] == 0).sum()))

@@ -139,17 +139,29 @@ __global__ __launch_bounds__(kThreads) void router_bf16_kernel(RouterArgs a)
     for (int n = 0; n < NG; ++n)
         acc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+    // Wave w takes steps w, w+4, w+8, ... in order; the loads of U of its
+    // steps are issued before their MFMAs (with few tokens per call the loop
+    // is load-latency bound). The summation order does not depend on U.
+    constexpr int U = NG >= 8 ? 1 : 8 / NG;
     const int steps = d / 32;
-    for (int s = wv; s < steps; s += 4) {
-        const int k0 = s * 32;
-        Vec16 av = *(const Vec16*)(xr + k0);
-        Vec16 bv[NG];
+    for (int s0 = wv; s0 < steps; s0 += 4 * U) {
+        Vec16 av[U], bv[U][NG];
 #pragma unroll
-        for (int n = 0; n < NG; ++n)
-            bv[n] = *(const Vec16*)(wr[n] + k0);
+        for (int u = 0; u < U; ++u) {
+            const int k0 = min(s0 + 4 * u, steps - 1) * 32;
+            av[u] = *(const Vec16*)(xr + k0);
 #pragma unroll
-        for (int n = 0; n < NG; ++n)
-            acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv[n]), acc[n], 0, 0, 0);
+            for (int n = 0; n < NG; ++n)
+                bv[u][n] = *(const Vec16*)(wr[n] + k0);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (s0 + 4 * u < steps) {
+#pragma unroll
+                for (int n = 0; n < NG; ++n)
+                    acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[u]), as_bf16x8(bv[u][n]), acc[n], 0,
+                                                                     0, 0);
+            }
     }
 
     // D layout of a 16x16 MFMA: lane holds rows 4*(lane/16)+i, column lane%16.

@@ -217,12 +217,16 @@ struct FragReader {
 // s+2 and s+3 and the first half of stage s+4's. The instruction order is
 // fixed by hand (sched_barrier between the pieces keeps the compiler's
 // scheduler from regrouping them).
-// The last m-tile of an expert runs the same code: its rows past the segment
-// end repeat the last valid row and their results are dropped. (A variant
-// that skips their MFMAs needs more registers than the persistent loop has.)
+// The last m-tile of an expert: its rows past the segment end repeat the
+// last valid row (their results are stored to that row again, same values);
+// 32-row groups made only of such rows are skipped (below).
 // With fp8 weights (F8) the B fragments are read as 8 codes each and turned
 // into bf16 (row scale sc[j]) in the shadow of the MFMA before their first use.
-template <int BM, int BN, int WM, int WN, bool F8, int A_INS, int B_INS>
+// Only the wave's first RG 32-row groups hold rows of the tile (RG < WM/32 in
+// an expert's last, partial m-tile): the MFMAs of the other groups, and the
+// reads of their k step 1 fragments, are left out. Loads, waits, barriers and
+// the next stage's fragment reads are the same in every variant.
+template <int BM, int BN, int WM, int WN, bool F8, int A_INS, int B_INS, int RG>
 __device__ __forceinline__ void stage(const i32x4& ra, const LoadSrc<A_INS>& ls, uint32_t ld_lds, int KB, int wv,
                                       uint32_t lane16, const Stage<BM, BN, F8>* st,
                                       const Stage<BM, BN, F8>* st_next, int wm, int wn, int lane,
@@ -242,19 +246,21 @@ __device__ __forceinline__ void stage(const i32x4& ra, const LoadSrc<A_INS>& ls,
     bf16x8 cb[NI];
 
     int nread = 0, nld = 0;
-    cb[0] = to_bf16(fb[0], sc[0]);
+    if constexpr (RG > 0)
+        cb[0] = to_bf16(fb[0], sc[0]);
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         const int i = m / NI, j = m % NI;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], cb[j], acc[i][j], 0, 0, 0);
-        if (i == 0 && j + 1 < NI)
+        if (i < RG)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], cb[j], acc[i][j], 0, 0, 0);
+        if (RG > 0 && i == 0 && j + 1 < NI)
             cb[j + 1] = to_bf16(fb[j + 1], sc[j + 1]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (; nread < R && nread < ((m + 1) * R + RS - 1) / RS; ++nread) {
             if (nread < NI)
                 gb[nread] = rd.b(1, nread);
-            else
+            else if (nread - NI < RG)
                 ga[nread - NI] = rd.a(1, nread - NI);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -270,12 +276,14 @@ __device__ __forceinline__ void stage(const i32x4& ra, const LoadSrc<A_INS>& ls,
     __builtin_amdgcn_sched_barrier(0);
 
     nread = 0;
-    cb[0] = to_bf16(gb[0], sc[0]);
+    if constexpr (RG > 0)
+        cb[0] = to_bf16(gb[0], sc[0]);
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         const int i = m / NI, j = m % NI;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[i], cb[j], acc[i][j], 0, 0, 0);
-        if (i == 0 && j + 1 < NI)
+        if (i < RG)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[i], cb[j], acc[i][j], 0, 0, 0);
+        if (RG > 0 && i == 0 && j + 1 < NI)
             cb[j + 1] = to_bf16(gb[j + 1], sc[j + 1]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -342,7 +350,7 @@ struct FragReaderQ8 {
 // ordered by weight block, each block's fragment re-read for the next stage
 // as soon as its last MFMA is issued, then the next stage's first A
 // fragments. Half of the loads in each half.
-template <int BM, int BN, int WM, int WN, int A_INS, int B_INS>
+template <int BM, int BN, int WM, int WN, int A_INS, int B_INS, int RG>
 __device__ __forceinline__ void stage_q8(const i32x4& ra, const LoadSrc<A_INS>& ls, uint32_t ld_lds, int KB, int wv,
                                          uint32_t lane16, const Stage<BM, BN, false>* st,
                                          const Stage<BM, BN, false>* st_next, int wm, int wn, int lane,
@@ -361,9 +369,11 @@ __device__ __forceinline__ void stage_q8(const i32x4& ra, const LoadSrc<A_INS>& 
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         const int i = m / NI, j = m % NI;
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, sa[i], 0, sb[j]);
+        if (i < RG)
+            acc[i][j] =
+                __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, sa[i], 0, sb[j]);
         __builtin_amdgcn_sched_barrier(0);
-        if (m == 0 || m == NI / 2) {
+        if ((m == 0 && RG > 2) || (m == NI / 2 && RG > 3)) {
             ga[m == 0 ? 0 : 1] = rd.a(m == 0 ? 2 : 3);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -381,8 +391,9 @@ __device__ __forceinline__ void stage_q8(const i32x4& ra, const LoadSrc<A_INS>& 
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         const int j = m / 2, ii = m % 2;
-        acc[2 + ii][j] =
-            __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ga[ii], fb[j], acc[2 + ii][j], 0, 0, 0, sa[2 + ii], 0, sb[j]);
+        if (2 + ii < RG)
+            acc[2 + ii][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ga[ii], fb[j], acc[2 + ii][j], 0, 0, 0,
+                                                                             sa[2 + ii], 0, sb[j]);
         __builtin_amdgcn_sched_barrier(0);
         if (ii == 1) {
             fb[j] = rn.b(j);
@@ -511,7 +522,7 @@ __device__ __forceinline__ i32x4 panel_rsrc(const void* b, const Tile& t, int N,
 // tile, or of the next tile (its A rows are `held`), or, past the last
 // tile, a reload of this tile's last stage that nobody reads (it keeps the
 // loads per stage, and so every wait count, the same).
-template <int BM, int BN, int WM, int WN, bool F8, bool EPBUF, int A_INS, int B_INS>
+template <int BM, int BN, int WM, int WN, bool F8, bool EPBUF, int A_INS, int B_INS, int RG>
 __device__ __forceinline__ void tile_stages(const i32x4& ra, const LoadSrc<A_INS>& cs, int nkt, bool has_nxt,
                                             const i32x4& nrb, int nkt0, const uint32_t (&cpart)[A_INS],
                                             uint32_t Kbytes, int KB, int wv, uint32_t lane16,
@@ -540,14 +551,14 @@ __device__ __forceinline__ void tile_stages(const i32x4& ra, const LoadSrc<A_INS
             ls.kt = __builtin_amdgcn_readfirstlane(ls.kt);
         const int bl = b + kAhead >= kRing ? b + kAhead - kRing : b + kAhead;
         const int bn = b + 1 >= kRing ? 0 : b + 1;
-        stage<BM, BN, WM, WN, F8, A_INS, B_INS>(ra, ls, ring0 + (uint32_t)bl * kStageBytes, KB, wv, lane16,
-                                                &ring.st[b], &ring.st[bn], wm, wn, lane, fa, fb, sc, acc);
+        stage<BM, BN, WM, WN, F8, A_INS, B_INS, RG>(ra, ls, ring0 + (uint32_t)bl * kStageBytes, KB, wv, lane16,
+                                                   &ring.st[b], &ring.st[bn], wm, wn, lane, fa, fb, sc, acc);
         b = bn;
     } while (++j < nkt);
 }
 
 // tile_stages for Q8 (same stream, stage_q8 per stage).
-template <int BM, int BN, int WM, int WN, int A_INS, int B_INS>
+template <int BM, int BN, int WM, int WN, int A_INS, int B_INS, int RG>
 __device__ __forceinline__ void tile_stages_q8(const i32x4& ra, const LoadSrc<A_INS>& cs, int nkt, bool has_nxt,
                                                const i32x4& nrb, int nkt0, const uint32_t (&cpart)[A_INS],
                                                uint32_t Kbytes, int KB, int wv, uint32_t lane16,
@@ -575,8 +586,8 @@ __device__ __forceinline__ void tile_stages_q8(const i32x4& ra, const LoadSrc<A_
         ls.kt = __builtin_amdgcn_readfirstlane(ls.kt);
         const int bl = b + kAhead >= kRing ? b + kAhead - kRing : b + kAhead;
         const int bn = b + 1 >= kRing ? 0 : b + 1;
-        stage_q8<BM, BN, WM, WN, A_INS, B_INS>(ra, ls, ring0 + (uint32_t)bl * kStageBytes, KB, wv, lane16,
-                                               &ring.st[b], &ring.st[bn], wm, wn, lane, fa, fb, sa, sb, acc);
+        stage_q8<BM, BN, WM, WN, A_INS, B_INS, RG>(ra, ls, ring0 + (uint32_t)bl * kStageBytes, KB, wv, lane16,
+                                                  &ring.st[b], &ring.st[bn], wm, wn, lane, fa, fb, sa, sb, acc);
         b = bn;
     } while (++j < nkt);
 }
@@ -657,7 +668,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     int L = blockIdx.x;
     if (L >= total)
         return;
-    const int G = gridDim.x;
+    const int GRID = gridDim.x;
 
     // Per-lane slot rows and swizzled chunk byte offsets of this wave's A loads.
     const uint32_t Kbytes = (uint32_t)K * (Q8 ? 1u : 2u);
@@ -679,7 +690,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
     for (int i = 0; i < A_INS; ++i)
         cs.aoff[i] = (uint32_t)row_src<GATE_UP>(g.perm, cur, slot[i]) * Kbytes + cpart[i];
-    bool has_nxt = L + G < total;
+    bool has_nxt = L + GRID < total;
     Tile nxt = cur;
     i32x4 nrb = cs.rb;
     uint32_t held[A_INS];
@@ -687,12 +698,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     for (int i = 0; i < A_INS; ++i)
         held[i] = 0;
     if (has_nxt) {
-        nxt = decode<BM>(tt, L + G, NT, S, g.group_n, KT);
+        nxt = decode<BM>(tt, L + GRID, NT, S, g.group_n, KT);
         nrb = panel_rsrc<BN>(g.b, nxt, N, KB);
 #pragma unroll
         for (int i = 0; i < A_INS; ++i)
             held[i] = (uint32_t)row_src<GATE_UP>(g.perm, nxt, slot[i]);
     }
+    // Waited for here, before the stream starts (see the scales below).
+#pragma unroll
+    for (int i = 0; i < A_INS; ++i)
+        asm volatile("" : "+v"(held[i]) : : "memory");
 
     float sc[NI];
 #pragma unroll
@@ -777,21 +792,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     int b = 0;
 
     for (;;) {
-        if constexpr (Q8)
-            tile_stages_q8<BM, BN, WM, WN, A_INS, B_INS>(ra, cs, cur.nkt, has_nxt, nrb, nxt.kt0, cpart, Kbytes, KB,
-                                                         wv, lane16, ring, ring0, b, wm, wn, lane, qa, qb, sa, sb,
-                                                         held, acc);
+        // 32-row groups of this wave that hold rows of the tile (the rest of
+        // an expert's last m-tile is padding): 0, 1, 2 or all.
+        const int wrows = cur.rows - wm * WM;
+        const int RG = wrows <= 0 ? 0 : wrows <= 32 ? 1 : wrows <= 64 ? 2 : MI;
+        auto run = [&](auto g_const) {
+            constexpr int GG = decltype(g_const)::value;
+            if constexpr (Q8)
+                tile_stages_q8<BM, BN, WM, WN, A_INS, B_INS, GG>(ra, cs, cur.nkt, has_nxt, nrb, nxt.kt0, cpart,
+                                                                 Kbytes, KB, wv, lane16, ring, ring0, b, wm, wn,
+                                                                 lane, qa, qb, sa, sb, held, acc);
+            else
+                tile_stages<BM, BN, WM, WN, F8, EPBUF, A_INS, B_INS, GG>(ra, cs, cur.nkt, has_nxt, nrb, nxt.kt0,
+                                                                         cpart, Kbytes, KB, wv, lane16, ring, ring0,
+                                                                         b, wm, wn, lane, fa, fb, sc, held, acc);
+        };
+        static_assert(MI == 4 || MI == 2, "row-group variants");
+        if (RG == MI)
+            run(std::integral_constant<int, MI>{});
+        else if (RG == 2)
+            run(std::integral_constant<int, 2>{});
+        else if (RG == 1)
+            run(std::integral_constant<int, 1>{});
         else
-            tile_stages<BM, BN, WM, WN, F8, EPBUF, A_INS, B_INS>(ra, cs, cur.nkt, has_nxt, nrb, nxt.kt0, cpart,
-                                                                 Kbytes, KB, wv, lane16, ring, ring0, b, wm, wn, lane,
-                                                                 fa, fb, sc, held, acc);
+            run(std::integral_constant<int, 0>{});
 
         // The tile after next: decode it and fetch its token rows now, so the
         // fetch overlaps the epilogue. Its first use is pinned after the
         // epilogue (below); loads complete in issue order, so the wait the
         // compiler puts there also covers the loads of the next tile's first
         // stages, which have had the whole epilogue to land.
-        const bool has_nn = has_nxt && L + 2 * G < total;
+        const bool has_nn = has_nxt && L + 2 * GRID < total;
         Tile nn = nxt;
         i32x4 nnrb = nrb;
         uint32_t nheld[A_INS];
@@ -799,7 +830,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         for (int i = 0; i < A_INS; ++i)
             nheld[i] = held[i];
         if (has_nn) {
-            nn = decode<BM>(tt, L + 2 * G, NT, S, g.group_n, KT);
+            nn = decode<BM>(tt, L + 2 * GRID, NT, S, g.group_n, KT);
             nnrb = panel_rsrc<BN>(g.b, nn, N, KB);
 #pragma unroll
             for (int i = 0; i < A_INS; ++i)
@@ -832,103 +863,119 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         // values), which keeps the epilogue free of branches. The lane's row
         // base goes through an opaque move so that the row and address
         // arithmetic is not hoisted out of the tile loop.
-        int rbase = wm * WM + 4 * (lane >> 5);
-        asm volatile("" : "+v"(rbase));
-        if constexpr (GATE_UP) {
-            // Through LDS, one (32-row group, gate/up block pair) at a time:
-            // the accumulators go from AGPRs straight into this wave's 8 KiB
-            // of the ring slot the tile's last stage used (free until the
-            // next stage refills it, after the barrier below; with fp8
-            // weights a slot is too small and the ring has an epilogue buffer
-            // of its own), as fp32 rows of 32 with the 16-byte chunk index
-            // XORed with row%8 (conflict-free writes and reads); each lane
-            // then reads back 16 consecutive gate and up values of one row,
-            // applies SiLU(g)*u and stores 16 bf16 of H with two 16-byte
-            // stores.
-            static_assert(BN == 256 && WN == 128 && NI == 4, "gate/up epilogue layout");
-            float* ep;
-            if constexpr (EPBUF) {
-                ep = ring.ep + wv * 2048;
+        // The epilogue and the pins of the prefetched values, in one copy for
+        // full tiles and one for partial ones: the stores a copy issues are
+        // then known, and so is the wait the compiler puts at the pins (with
+        // the skipped stores of a partial tile it has to wait for all).
+        auto epilogue = [&](auto partial) {
+            constexpr bool PARTIAL = decltype(partial)::value;
+            (void)nheld, (void)nsc, (void)nsa, (void)nsb;  // captured (used only in asm operands)
+            int rbase = wm * WM + 4 * (lane >> 5);
+            asm volatile("" : "+v"(rbase));
+            if constexpr (GATE_UP) {
+                // Through LDS, one (32-row group, gate/up block pair) at a time:
+                // the accumulators go from AGPRs straight into this wave's 8 KiB
+                // of the ring slot the tile's last stage used (free until the
+                // next stage refills it, after the barrier below; with fp8
+                // weights a slot is too small and the ring has an epilogue buffer
+                // of its own), as fp32 rows of 32 with the 16-byte chunk index
+                // XORed with row%8 (conflict-free writes and reads); each lane
+                // then reads back 16 consecutive gate and up values of one row,
+                // applies SiLU(g)*u and stores 16 bf16 of H with two 16-byte
+                // stores.
+                static_assert(BN == 256 && WN == 128 && NI == 4, "gate/up epilogue layout");
+                float* ep;
+                if constexpr (EPBUF) {
+                    ep = ring.ep + wv * 2048;
+                } else {
+                    const int bfree = b == 0 ? kRing - 1 : b - 1;
+                    ep = (float*)&ring.st[bfree] + wv * 2048;
+                }
+                const int wr = 8 * 0 + 4 * (lane >> 5);  // row of q = 0 inside the 32-row group
+                const int wc = lane & 31;
+                const int rr = lane >> 1;                  // row read back by this lane
+                const int rc = (lane & 1) * 4;             // first 16-byte chunk read back
+                uint16_t* H = (uint16_t*)g.out;
+    #pragma unroll
+                for (int i = 0; i < MI; ++i) {
+                    if (PARTIAL && i >= RG)  // padding rows only: nothing to store
+                        continue;
+    #pragma unroll
+                    for (int jp = 0; jp < NI; jp += 2) {
+    #pragma unroll
+                        for (int q = 0; q < 16; ++q) {
+                            const int r = wr + 8 * (q / 4) + (q % 4);
+                            const int o = r * 32 + (((wc >> 2) ^ (r & 7)) << 2) + (wc & 3);
+                            ep[o] = acc[i][jp][q];
+                            ep[1024 + o] = acc[i][jp + 1][q];
+                        }
+                        uint32_t hv[8];
+    #pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            const int o = rr * 32 + (((rc + t) ^ (rr & 7)) << 2);
+                            const floatx4 gv = *(const floatx4*)(ep + o);
+                            const floatx4 uv = *(const floatx4*)(ep + 1024 + o);
+                            hv[2 * t] = (uint32_t)f32_to_bf16_bits(silu_rcp(gv[0]) * uv[0]) |
+                                        ((uint32_t)f32_to_bf16_bits(silu_rcp(gv[1]) * uv[1]) << 16);
+                            hv[2 * t + 1] = (uint32_t)f32_to_bf16_bits(silu_rcp(gv[2]) * uv[2]) |
+                                            ((uint32_t)f32_to_bf16_bits(silu_rcp(gv[3]) * uv[3]) << 16);
+                        }
+                        const int row = min(rbase - 4 * (lane >> 5) + i * 32 + rr, cur.rows - 1);
+                        const int col = (cur.n * BN + wn * WN + jp * 32) / 2 + rc * 4;
+                        Vec16* dst = (Vec16*)(H + (int64_t)(cur.row0 + row) * g.f + col);
+                        dst[0] = Vec16{hv[0], hv[1], hv[2], hv[3]};
+                        dst[1] = Vec16{hv[4], hv[5], hv[6], hv[7]};
+                    }
+                }
+                // Every wave is done with the slot before the next stage loads it
+                // (a wave's own epilogue buffer needs no barrier).
+                if constexpr (!EPBUF) {
+                    __builtin_amdgcn_s_barrier();
+                    asm volatile("" ::: "memory");
+                }
             } else {
-                const int bfree = b == 0 ? kRing - 1 : b - 1;
-                ep = (float*)&ring.st[bfree] + wv * 2048;
-            }
-            const int wr = 8 * 0 + 4 * (lane >> 5);  // row of q = 0 inside the 32-row group
-            const int wc = lane & 31;
-            const int rr = lane >> 1;                  // row read back by this lane
-            const int rc = (lane & 1) * 4;             // first 16-byte chunk read back
-            uint16_t* H = (uint16_t*)g.out;
-#pragma unroll
-            for (int i = 0; i < MI; ++i) {
-#pragma unroll
-                for (int jp = 0; jp < NI; jp += 2) {
-#pragma unroll
+                float* Ys = (float*)g.out + (int64_t)cur.s * g.A_max * g.d;
+    #pragma unroll
+                for (int i = 0; i < MI; ++i) {
+                    if (PARTIAL && i >= RG)  // padding rows only: nothing to store
+                        continue;
+    #pragma unroll
                     for (int q = 0; q < 16; ++q) {
-                        const int r = wr + 8 * (q / 4) + (q % 4);
-                        const int o = r * 32 + (((wc >> 2) ^ (r & 7)) << 2) + (wc & 3);
-                        ep[o] = acc[i][jp][q];
-                        ep[1024 + o] = acc[i][jp + 1][q];
+                        const int r = min(rbase + i * 32 + 8 * (q / 4) + (q % 4), cur.rows - 1);
+                        float* yrow = Ys + (int64_t)(cur.row0 + r) * g.d + cur.n * BN + wn * WN + (lane & 31);
+    #pragma unroll
+                        for (int j = 0; j < NI; ++j)
+                            yrow[j * 32] = acc[i][j][q];
                     }
-                    uint32_t hv[8];
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const int o = rr * 32 + (((rc + t) ^ (rr & 7)) << 2);
-                        const floatx4 gv = *(const floatx4*)(ep + o);
-                        const floatx4 uv = *(const floatx4*)(ep + 1024 + o);
-                        hv[2 * t] = (uint32_t)f32_to_bf16_bits(silu_rcp(gv[0]) * uv[0]) |
-                                    ((uint32_t)f32_to_bf16_bits(silu_rcp(gv[1]) * uv[1]) << 16);
-                        hv[2 * t + 1] = (uint32_t)f32_to_bf16_bits(silu_rcp(gv[2]) * uv[2]) |
-                                        ((uint32_t)f32_to_bf16_bits(silu_rcp(gv[3]) * uv[3]) << 16);
-                    }
-                    const int row = min(rbase - 4 * (lane >> 5) + i * 32 + rr, cur.rows - 1);
-                    const int col = (cur.n * BN + wn * WN + jp * 32) / 2 + rc * 4;
-                    Vec16* dst = (Vec16*)(H + (int64_t)(cur.row0 + row) * g.f + col);
-                    dst[0] = Vec16{hv[0], hv[1], hv[2], hv[3]};
-                    dst[1] = Vec16{hv[4], hv[5], hv[6], hv[7]};
                 }
             }
-            // Every wave is done with the slot before the next stage loads it
-            // (a wave's own epilogue buffer needs no barrier).
-            if constexpr (!EPBUF) {
-                __builtin_amdgcn_s_barrier();
-                asm volatile("" ::: "memory");
-            }
-        } else {
-            float* Ys = (float*)g.out + (int64_t)cur.s * g.A_max * g.d;
-#pragma unroll
-            for (int i = 0; i < MI; ++i) {
-#pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int r = min(rbase + i * 32 + 8 * (q / 4) + (q % 4), cur.rows - 1);
-                    float* yrow = Ys + (int64_t)(cur.row0 + r) * g.d + cur.n * BN + wn * WN + (lane & 31);
-#pragma unroll
-                    for (int j = 0; j < NI; ++j)
-                        yrow[j * 32] = acc[i][j][q];
-                }
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-            for (int j = 0; j < NI; ++j)
-#pragma unroll
-                for (int q = 0; q < 16; ++q)
-                    acc[i][j][q] = 0.f;
-        if constexpr (GATE_UP)
-            asm volatile("" : "+v"(nheld[0]), "+v"(nheld[1]), "+v"(nheld[2]), "+v"(nheld[3]) : : "memory");
-        if constexpr (F8) {
-#pragma unroll
-            for (int j = 0; j < NI; ++j)
-                asm volatile("" : "+v"(nsc[j]) : : "memory");
-        }
-        if constexpr (Q8) {
-#pragma unroll
+    #pragma unroll
             for (int i = 0; i < MI; ++i)
-                asm volatile("" : "+v"(nsa[i]) : : "memory");
-#pragma unroll
-            for (int j = 0; j < NI; ++j)
-                asm volatile("" : "+v"(nsb[j]) : : "memory");
-        }
+    #pragma unroll
+                for (int j = 0; j < NI; ++j)
+    #pragma unroll
+                    for (int q = 0; q < 16; ++q)
+                        acc[i][j][q] = 0.f;
+            if constexpr (GATE_UP)
+                asm volatile("" : "+v"(nheld[0]), "+v"(nheld[1]), "+v"(nheld[2]), "+v"(nheld[3]) : : "memory");
+            if constexpr (F8) {
+    #pragma unroll
+                for (int j = 0; j < NI; ++j)
+                    asm volatile("" : "+v"(nsc[j]) : : "memory");
+            }
+            if constexpr (Q8) {
+    #pragma unroll
+                for (int i = 0; i < MI; ++i)
+                    asm volatile("" : "+v"(nsa[i]) : : "memory");
+    #pragma unroll
+                for (int j = 0; j < NI; ++j)
+                    asm volatile("" : "+v"(nsb[j]) : : "memory");
+            }
+        };
+        if (RG == MI)
+            epilogue(std::false_type{});
+        else
+            epilogue(std::true_type{});
         if (!has_nxt)
             break;
 
@@ -939,7 +986,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
         for (int i = 0; i < A_INS; ++i)
             cs.aoff[i] = held[i] * Kbytes + cpart[i];
-        L += G;
+        L += GRID;
         has_nxt = has_nn;
         nxt = nn;
         nrb = nnrb;

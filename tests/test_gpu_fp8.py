@@ -170,6 +170,7 @@ CASES = [
     C("k8-E256", 64, 128, 256, 8, 128, "bf16"),
     C("skewed-masked-small", 2000, 256, 64, 2, 128, "bf16",
       {0: 4.0, 3: 4.0, **{e: -1.0e4 for e in range(44, 64)}}),
+    C("last-tile-padding", 1030, 256, 1, 1, 6656, "bf16"),
 ]
 
 
@@ -214,6 +215,7 @@ Q8_CASES = [
     C("k8-E256", 64, 256, 256, 8, 256, "bf16"),
     C("skewed-masked-small", 2000, 256, 64, 2, 256, "bf16",
       {0: 4.0, 3: 4.0, **{e: -1.0e4 for e in range(44, 64)}}),
+    C("last-tile-padding", 1030, 256, 1, 1, 6656, "bf16"),
 ]
 
 

@@ -30,6 +30,9 @@ SMALL = [
     C("k-equals-E", 90, 256, 4, 4, 128, "bf16"),
     C("all-to-one", 300, 128, 8, 1, 128, "bf16", {5: 100.0}),
     C("k8-E256", 64, 128, 256, 8, 128, "bf16"),
+    # more gate/up tiles than compute units (each workgroup walks several) and
+    # an expert whose last m-tile has 6 rows: waves whose rows are all padding
+    C("last-tile-padding", 1030, 256, 1, 1, 6656, "bf16"),
 ]
 
 

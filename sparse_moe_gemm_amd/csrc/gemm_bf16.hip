@@ -896,13 +896,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 const int rr = lane >> 1;                  // row read back by this lane
                 const int rc = (lane & 1) * 4;             // first 16-byte chunk read back
                 uint16_t* H = (uint16_t*)g.out;
-    #pragma unroll
+#pragma unroll
                 for (int i = 0; i < MI; ++i) {
                     if (PARTIAL && i >= RG)  // padding rows only: nothing to store
                         continue;
-    #pragma unroll
+#pragma unroll
                     for (int jp = 0; jp < NI; jp += 2) {
-    #pragma unroll
+#pragma unroll
                         for (int q = 0; q < 16; ++q) {
                             const int r = wr + 8 * (q / 4) + (q % 4);
                             const int o = r * 32 + (((wc >> 2) ^ (r & 7)) << 2) + (wc & 3);
@@ -910,7 +910,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                             ep[1024 + o] = acc[i][jp + 1][q];
                         }
                         uint32_t hv[8];
-    #pragma unroll
+#pragma unroll
                         for (int t = 0; t < 4; ++t) {
                             const int o = rr * 32 + (((rc + t) ^ (rr & 7)) << 2);
                             const floatx4 gv = *(const floatx4*)(ep + o);
@@ -935,39 +935,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 }
             } else {
                 float* Ys = (float*)g.out + (int64_t)cur.s * g.A_max * g.d;
-    #pragma unroll
+#pragma unroll
                 for (int i = 0; i < MI; ++i) {
                     if (PARTIAL && i >= RG)  // padding rows only: nothing to store
                         continue;
-    #pragma unroll
+#pragma unroll
                     for (int q = 0; q < 16; ++q) {
                         const int r = min(rbase + i * 32 + 8 * (q / 4) + (q % 4), cur.rows - 1);
                         float* yrow = Ys + (int64_t)(cur.row0 + r) * g.d + cur.n * BN + wn * WN + (lane & 31);
-    #pragma unroll
+#pragma unroll
                         for (int j = 0; j < NI; ++j)
                             yrow[j * 32] = acc[i][j][q];
                     }
                 }
             }
-    #pragma unroll
+#pragma unroll
             for (int i = 0; i < MI; ++i)
-    #pragma unroll
+#pragma unroll
                 for (int j = 0; j < NI; ++j)
-    #pragma unroll
+#pragma unroll
                     for (int q = 0; q < 16; ++q)
                         acc[i][j][q] = 0.f;
             if constexpr (GATE_UP)
                 asm volatile("" : "+v"(nheld[0]), "+v"(nheld[1]), "+v"(nheld[2]), "+v"(nheld[3]) : : "memory");
             if constexpr (F8) {
-    #pragma unroll
+#pragma unroll
                 for (int j = 0; j < NI; ++j)
                     asm volatile("" : "+v"(nsc[j]) : : "memory");
             }
             if constexpr (Q8) {
-    #pragma unroll
+#pragma unroll
                 for (int i = 0; i < MI; ++i)
                     asm volatile("" : "+v"(nsa[i]) : : "memory");
-    #pragma unroll
+#pragma unroll
                 for (int j = 0; j < NI; ++j)
                     asm volatile("" : "+v"(nsb[j]) : : "memory");
             }

@@ -18,7 +18,9 @@
 //     compiler's wait counts are exact);
 //   - it writes the fp32 partial sums of its slice: P[s][p][nb*32 + j].
 // K slices split every expert's weights into many equal, independent items,
-// which keeps all compute units streaming. For gate/up a second kernel sums
+// which keeps all compute units streaming. Weights are read with
+// non-temporal loads: each is used once per call, and not keeping them in
+// the caches streams them ~5-7% faster. For gate/up a second kernel sums
 // the slices and applies SiLU(g)*u into H; for down the slices are the Ys
 // partials that combine already sums.
 // With 8-bit expert weights (E4M3 codes in the fp8 blocked layout, one scale
@@ -78,16 +80,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             for (int i = 0; i < kP; ++i) {
                 const int kb = min(kb0 + i, kb1 - 1);
                 a0[i] = ap[kb * 2];
-                b0[i] = bp[(int64_t)kb * kWave];
-                c0[i] = bp[bst + (int64_t)kb * kWave];
+                b0[i] = __builtin_nontemporal_load(&bp[(int64_t)kb * kWave]);
+                c0[i] = __builtin_nontemporal_load(&bp[bst + (int64_t)kb * kWave]);
             }
             for (int kb = kb0; kb < kb1; kb += 2 * kP) {
 #pragma unroll
                 for (int i = 0; i < kP; ++i) {
                     const int kk = min(kb + kP + i, kb1 - 1);
                     a1[i] = ap[kk * 2];
-                    b1[i] = bp[(int64_t)kk * kWave];
-                    c1[i] = bp[bst + (int64_t)kk * kWave];
+                    b1[i] = __builtin_nontemporal_load(&bp[(int64_t)kk * kWave]);
+                    c1[i] = __builtin_nontemporal_load(&bp[bst + (int64_t)kk * kWave]);
                 }
 #pragma unroll
                 for (int i = 0; i < kP; ++i)
@@ -99,8 +101,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 for (int i = 0; i < kP; ++i) {
                     const int kk = min(kb + 2 * kP + i, kb1 - 1);
                     a0[i] = ap[kk * 2];
-                    b0[i] = bp[(int64_t)kk * kWave];
-                    c0[i] = bp[bst + (int64_t)kk * kWave];
+                    b0[i] = __builtin_nontemporal_load(&bp[(int64_t)kk * kWave]);
+                    c0[i] = __builtin_nontemporal_load(&bp[bst + (int64_t)kk * kWave]);
                 }
 #pragma unroll
                 for (int i = 0; i < kP; ++i)
@@ -174,8 +176,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
                     a0[i][h] = ap[kb * 4 + h];
-                b0[i] = bp[(int64_t)kb * kWave];
-                c0[i] = bp[bst + (int64_t)kb * kWave];
+                b0[i] = __builtin_nontemporal_load(&bp[(int64_t)kb * kWave]);
+                c0[i] = __builtin_nontemporal_load(&bp[bst + (int64_t)kb * kWave]);
             }
             for (int kb = kb0; kb < kb1; kb += 2 * kQ) {
 #pragma unroll
@@ -184,8 +186,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
                         a1[i][h] = ap[kk * 4 + h];
-                    b1[i] = bp[(int64_t)kk * kWave];
-                    c1[i] = bp[bst + (int64_t)kk * kWave];
+                    b1[i] = __builtin_nontemporal_load(&bp[(int64_t)kk * kWave]);
+                    c1[i] = __builtin_nontemporal_load(&bp[bst + (int64_t)kk * kWave]);
                 }
 #pragma unroll
                 for (int i = 0; i < kQ; ++i)
@@ -205,8 +207,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
                         a0[i][h] = ap[kk * 4 + h];
-                    b0[i] = bp[(int64_t)kk * kWave];
-                    c0[i] = bp[bst + (int64_t)kk * kWave];
+                    b0[i] = __builtin_nontemporal_load(&bp[(int64_t)kk * kWave]);
+                    c0[i] = __builtin_nontemporal_load(&bp[bst + (int64_t)kk * kWave]);
                 }
 #pragma unroll
                 for (int i = 0; i < kQ; ++i)
@@ -300,8 +302,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     a0[i][h] = ap[kb * 4 + 2 * h];
-                    b0[i][h] = bp[(int64_t)(2 * kb + h) * kWave];
-                    c0[i][h] = bp[bst + (int64_t)(2 * kb + h) * kWave];
+                    b0[i][h] = __builtin_nontemporal_load(&bp[(int64_t)(2 * kb + h) * kWave]);
+                    c0[i][h] = __builtin_nontemporal_load(&bp[bst + (int64_t)(2 * kb + h) * kWave]);
                 }
             }
             for (int kb = kb0; kb < kb1; kb += 2 * kQ) {
@@ -311,8 +313,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         a1[i][h] = ap[kk * 4 + 2 * h];
-                        b1[i][h] = bp[(int64_t)(2 * kk + h) * kWave];
-                        c1[i][h] = bp[bst + (int64_t)(2 * kk + h) * kWave];
+                        b1[i][h] = __builtin_nontemporal_load(&bp[(int64_t)(2 * kk + h) * kWave]);
+                        c1[i][h] = __builtin_nontemporal_load(&bp[bst + (int64_t)(2 * kk + h) * kWave]);
                     }
                 }
 #pragma unroll
@@ -330,8 +332,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         a0[i][h] = ap[kk * 4 + 2 * h];
-                        b0[i][h] = bp[(int64_t)(2 * kk + h) * kWave];
-                        c0[i][h] = bp[bst + (int64_t)(2 * kk + h) * kWave];
+                        b0[i][h] = __builtin_nontemporal_load(&bp[(int64_t)(2 * kk + h) * kWave]);
+                        c0[i][h] = __builtin_nontemporal_load(&bp[bst + (int64_t)(2 * kk + h) * kWave]);
                     }
                 }
 #pragma unroll

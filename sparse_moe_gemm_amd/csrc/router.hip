@@ -13,9 +13,10 @@
 // the order of the logits, so exponentials are taken for the k winners only.
 //
 // bf16 path: the projection runs on v_mfma_f32_16x16x32_bf16 (16 tokens x 16
-// experts per MFMA); the 4 waves of a block split the reduction dimension in
-// interleaved 32-wide steps and add their partial sums through LDS in a fixed
-// order, so results are bit-reproducible.
+// experts per MFMA); the 16 waves of a block (8 for more than 128 experts)
+// split the reduction dimension in interleaved 32-wide steps and add their
+// partial sums through LDS in a fixed order, so results are bit-reproducible
+// and do not depend on the number of tokens in the call.
 // fp32 path: plain FMA dot products (gfx950 has no faster fp32 matrix rate).
 #include "common.hpp"
 
@@ -24,7 +25,7 @@ namespace cmoe {
 namespace {
 
 constexpr int kTok = 16;     // tokens per block
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;  // fp32 path
 
 // Monotone map of a float to an unsigned key (larger float -> larger key).
 // -0 is first turned into +0 so that the two zeros tie, as they compare equal.
@@ -48,14 +49,14 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
     return v;
 }
 
-// Top-k + softmax for the block's tokens, reading logits (bias included) from
-// LDS `lg` laid out [kTok][ldl]. Each wave handles 4 tokens.
-__device__ void topk_softmax_epilogue(const float* lg, int ldl, int t0, int T, int E, int k,
+// Top-k + softmax for the block's bt tokens, reading logits (bias included)
+// from LDS `lg` laid out [bt][ldl]. Wave w of W handles tokens w, w+W, ...
+__device__ void topk_softmax_epilogue(const float* lg, int ldl, int bt, int t0, int T, int E, int k,
                                       int32_t* ids, float* wout)
 {
     const int lane = threadIdx.x % kWave;
     const int wv = threadIdx.x / kWave;
-    for (int r = wv; r < kTok; r += kThreads / kWave) {
+    for (int r = wv; r < bt; r += (int)blockDim.x / kWave) {
         const int t = t0 + r;
         if (t >= T)
             break;
@@ -100,91 +101,116 @@ __device__ void topk_softmax_epilogue(const float* lg, int ldl, int t0, int T, i
     }
 }
 
-__device__ void store_logits(const float* lg, int ldl, int t0, int T, int E, float* logits)
+__device__ void store_logits(const float* lg, int ldl, int bt, int t0, int T, int E, float* logits)
 {
     if (!logits)
         return;
-    for (int i = threadIdx.x; i < kTok * E; i += kThreads) {
+    for (int i = threadIdx.x; i < bt * E; i += (int)blockDim.x) {
         const int r = i / E, e = i % E;
         if (t0 + r < T)
             logits[(int64_t)(t0 + r) * E + e] = lg[r * ldl + e];
     }
 }
 
-// NG = number of 16-expert column groups (E <= 16 * NG).
-template <int NG>
-__global__ __launch_bounds__(kThreads) void router_bf16_kernel(RouterArgs a)
+// NG = number of 16-expert column groups (E <= 16 * NG); TG = number of
+// 16-token groups per block; W = waves per block, which split the reduction
+// dimension. Each wave's loads form a chain of dependent batches (one memory
+// round trip each, and the router's inputs are usually cold: the expert GEMMs
+// stream gigabytes through the caches between two calls), so W is as large as
+// the register budget allows: 16 waves (8 for 256 experts). A token's logits
+// do not depend on T or TG: every token is reduced by the same interleaving
+// of K over the W waves and the same LDS summation order.
+template <int NG, int TG, int W>
+__global__ __launch_bounds__(W * kWave) void router_bf16_kernel(RouterArgs a)
 {
     constexpr int EP = 16 * NG;      // padded expert count
     constexpr int LDL = EP + 1;      // LDS row stride (floats)
-    __shared__ float part[kTok][LDL];
+    constexpr int BT = kTok * TG;    // tokens per block
+    __shared__ float part[BT][LDL];
 
     const int lane = threadIdx.x % kWave;
-    const int wv = threadIdx.x / kWave;
-    const int t0 = blockIdx.x * kTok;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
+    const int t0 = blockIdx.x * BT;
     const int d = a.d;
 
-    // Fragment rows: token row for A, expert row for B (clamped: padded rows
+    // Fragment rows: token rows for A, expert row for B (clamped: padded rows
     // read valid memory and their results are dropped).
-    const int trow = min(t0 + (lane & 15), a.T - 1);
     const int kq = (lane >> 4) * 8;
-    const uint16_t* xr = (const uint16_t*)a.x + (int64_t)trow * d + kq;
+    const uint16_t* xr[TG];
+#pragma unroll
+    for (int g = 0; g < TG; ++g)
+        xr[g] = (const uint16_t*)a.x + (int64_t)min(t0 + g * kTok + (lane & 15), a.T - 1) * d + kq;
     const uint16_t* wr[NG];
 #pragma unroll
     for (int n = 0; n < NG; ++n)
         wr[n] = (const uint16_t*)a.w_rt + (int64_t)min(n * 16 + (lane & 15), a.E - 1) * d + kq;
 
-    floatx4 acc[NG];
+    floatx4 acc[TG][NG];
 #pragma unroll
-    for (int n = 0; n < NG; ++n)
-        acc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < TG; ++g)
+#pragma unroll
+        for (int n = 0; n < NG; ++n)
+            acc[g][n] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // Wave w takes steps w, w+4, w+8, ... in order; the loads of U of its
-    // steps are issued before their MFMAs (with few tokens per call the loop
-    // is load-latency bound). The summation order does not depend on U.
-    constexpr int U = NG >= 8 ? 1 : 8 / NG;
+    // Wave w takes steps w, w+W, w+2W, ... in order; the loads of U of its
+    // steps are issued before their MFMAs. The summation order does not
+    // depend on U. Past the last step a batch reloads the last step with a
+    // zero token fragment (adding exact zeros), so that every MFMA and every
+    // load is unconditional: a step under a branch lets the compiler move its
+    // loads into the branch and wait for each of them there.
+    constexpr int U = NG * TG >= 8 ? 1 : 8 / (NG * TG);
     const int steps = d / 32;
-    for (int s0 = wv; s0 < steps; s0 += 4 * U) {
-        Vec16 av[U], bv[U][NG];
+    for (int s0 = wv; s0 < steps; s0 += W * U) {
+        Vec16 av[U][TG], bv[U][NG];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int k0 = min(s0 + 4 * u, steps - 1) * 32;
-            av[u] = *(const Vec16*)(xr + k0);
+            const int k0 = min(s0 + W * u, steps - 1) * 32;
+#pragma unroll
+            for (int g = 0; g < TG; ++g)
+                av[u][g] = *(const Vec16*)(xr[g] + k0);
 #pragma unroll
             for (int n = 0; n < NG; ++n)
                 bv[u][n] = *(const Vec16*)(wr[n] + k0);
         }
+        __builtin_amdgcn_sched_barrier(0);  // all loads of the batch first
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (s0 + 4 * u < steps) {
+        for (int u = 0; u < U; ++u) {
+            const bool past = s0 + W * u >= steps;  // wave-uniform
+#pragma unroll
+            for (int g = 0; g < TG; ++g) {
+                const Vec16 z = {0u, 0u, 0u, 0u};
+                const Vec16 a_ = past ? z : av[u][g];
 #pragma unroll
                 for (int n = 0; n < NG; ++n)
-                    acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[u]), as_bf16x8(bv[u][n]), acc[n], 0,
-                                                                     0, 0);
+                    acc[g][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a_), as_bf16x8(bv[u][n]), acc[g][n],
+                                                                        0, 0, 0);
             }
+        }
     }
 
     // D layout of a 16x16 MFMA: lane holds rows 4*(lane/16)+i, column lane%16.
-    // The four partial sums are added in wave order ((w0 + w1) + w2) + w3.
-    for (int w = 0; w < 4; ++w) {
+    // The W partial sums are added in wave order (((w0 + w1) + w2) + ...).
+    for (int w = 0; w < W; ++w) {
         if (wv == w) {
 #pragma unroll
-            for (int n = 0; n < NG; ++n)
+            for (int g = 0; g < TG; ++g)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float& dst = part[(lane >> 4) * 4 + i][n * 16 + (lane & 15)];
-                    dst = (w == 0) ? acc[n][i] : dst + acc[n][i];
-                }
+                for (int n = 0; n < NG; ++n)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float& dst = part[g * kTok + (lane >> 4) * 4 + i][n * 16 + (lane & 15)];
+                        dst = (w == 0) ? acc[g][n][i] : dst + acc[g][n][i];
+                    }
         }
         __syncthreads();
     }
-    for (int i = threadIdx.x; i < kTok * a.E; i += kThreads) {
+    for (int i = threadIdx.x; i < BT * a.E; i += W * kWave) {
         const int r = i / a.E, e = i % a.E;
         part[r][e] += a.b[e];
     }
     __syncthreads();
-    store_logits(&part[0][0], LDL, t0, a.T, a.E, a.logits);
-    topk_softmax_epilogue(&part[0][0], LDL, t0, a.T, a.E, a.k, a.ids, a.w);
+    store_logits(&part[0][0], LDL, BT, t0, a.T, a.E, a.logits);
+    topk_softmax_epilogue(&part[0][0], LDL, BT, t0, a.T, a.E, a.k, a.ids, a.w);
 }
 
 __global__ __launch_bounds__(kThreads) void router_f32_kernel(RouterArgs a)
@@ -204,8 +230,8 @@ __global__ __launch_bounds__(kThreads) void router_f32_kernel(RouterArgs a)
         lg[r][e] = s + a.b[e];
     }
     __syncthreads();
-    store_logits(&lg[0][0], kMaxExperts + 1, t0, a.T, a.E, a.logits);
-    topk_softmax_epilogue(&lg[0][0], kMaxExperts + 1, t0, a.T, a.E, a.k, a.ids, a.w);
+    store_logits(&lg[0][0], kMaxExperts + 1, kTok, t0, a.T, a.E, a.logits);
+    topk_softmax_epilogue(&lg[0][0], kMaxExperts + 1, kTok, t0, a.T, a.E, a.k, a.ids, a.w);
 }
 
 __global__ void transpose_router_kernel(const uint8_t* src, uint8_t* dst, int d, int E, int esize)
@@ -222,22 +248,43 @@ __global__ void transpose_router_kernel(const uint8_t* src, uint8_t* dst, int d,
     }
 }
 
+template <int NG, int TG>
+hipError_t launch_router_tg(const RouterArgs& a, hipStream_t s)
+{
+    constexpr int W = NG >= 16 ? 8 : 16;  // 16 waves need <= 128 registers
+    const int bt = kTok * TG;
+    hipLaunchKernelGGL((router_bf16_kernel<NG, TG, W>), dim3((a.T + bt - 1) / bt), dim3(W * kWave), 0, s, a);
+    return hipGetLastError();
+}
+
+// Token groups per block: with many experts and many tokens, blocks of 32
+// (128 experts) or 64 tokens (64 experts) read the router weights fewer
+// times (measured on MI355X: 16384 tokens x 64 experts 99 -> 68 us, 8192 x 128
+// 58 -> 46 us); with few tokens or experts, 16-token blocks keep more blocks
+// in flight.
+template <int NG>
+hipError_t launch_router_ng(const RouterArgs& a, hipStream_t s)
+{
+    if constexpr (NG == 4 || NG == 8) {
+        if (a.T >= 4096)
+            return launch_router_tg<NG, NG == 4 ? 4 : 2>(a, s);
+    }
+    return launch_router_tg<NG, 1>(a, s);
+}
+
 }  // namespace
 
 hipError_t launch_router_bf16(const RouterArgs& a, hipStream_t s)
 {
-    const dim3 grid((a.T + kTok - 1) / kTok), block(kThreads);
     if (a.E <= 16)
-        hipLaunchKernelGGL(router_bf16_kernel<1>, grid, block, 0, s, a);
-    else if (a.E <= 32)
-        hipLaunchKernelGGL(router_bf16_kernel<2>, grid, block, 0, s, a);
-    else if (a.E <= 64)
-        hipLaunchKernelGGL(router_bf16_kernel<4>, grid, block, 0, s, a);
-    else if (a.E <= 128)
-        hipLaunchKernelGGL(router_bf16_kernel<8>, grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL(router_bf16_kernel<16>, grid, block, 0, s, a);
-    return hipGetLastError();
+        return launch_router_ng<1>(a, s);
+    if (a.E <= 32)
+        return launch_router_ng<2>(a, s);
+    if (a.E <= 64)
+        return launch_router_ng<4>(a, s);
+    if (a.E <= 128)
+        return launch_router_ng<8>(a, s);
+    return launch_router_ng<16>(a, s);
 }
 
 hipError_t launch_router_f32(const RouterArgs& a, hipStream_t s)

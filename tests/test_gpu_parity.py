@@ -127,6 +127,23 @@ def test_handle_reuse_with_smaller_batch_and_determinism():
     compare(cfg.with_(T=123), dict(inp, x=inp["x"][:123]), g2)
 
 
+@pytest.mark.parametrize("E", [64, 128])
+def test_routing_does_not_depend_on_batch_size(E):
+    """The router takes 16, 32 or 64 tokens per block depending on the batch
+    size and the expert count; a token's logits, experts and weights must not
+    change with it (same bits), also for a token at another position in its
+    block."""
+    cfg = C(f"batch-invariance-E{E}", 4096, 512, E, 2, 128, "bf16")
+    inp = synth.make_inputs(cfg)
+    layer = make_layer(cfg, inp)
+    print(f"routing batch invariance {cfg}", flush=True)
+    full = run_gpu(layer, inp["x"])
+    part = run_gpu(layer, inp["x"][37:137])
+    layer.close()
+    for key in ("logits", "topk_ids", "topk_w"):
+        assert np.array_equal(part[key], full[key][37:137]), key
+
+
 def test_partial_routing_outputs():
     import torch
 

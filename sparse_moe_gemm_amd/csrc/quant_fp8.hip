@@ -209,10 +209,13 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* x, int64
         Vec16 v[kActChunks];
         float amax = 0.f;
         if (regs) {
+            // Every chunk load is unconditional (a chunk past the row end
+            // re-reads the row's last 8 values and is not used): loads under
+            // a branch each get a wait for all earlier ones, which would
+            // serialise the row's loads.
 #pragma unroll
             for (int i = 0; i < kActChunks; ++i)
-                if (tid * 8 + i * step < cols)
-                    v[i] = *(const Vec16*)(src + tid * 8 + i * step);
+                v[i] = *(const Vec16*)(src + min(tid * 8 + i * step, cols - 8));
 #pragma unroll
             for (int i = 0; i < kActChunks; ++i)
                 if (tid * 8 + i * step < cols)
@@ -249,16 +252,63 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* x, int64
     }
 }
 
+// The same for rows of at most 4096 values, one wave per row (4 rows per
+// block): lane l holds values l*8 + i*512, i < 8 (chunk loads
+// unconditional, as above), the row maximum is a wave reduction, and no
+// barrier is needed.
+__global__ __launch_bounds__(256) void act_quant_rows_kernel(const uint16_t* x, int64_t rows, int cols, int k,
+                                                             const int32_t* inv, uint8_t* codes, float* scales)
+{
+    constexpr int kCh = 8, kStep = kWave * 8;
+    const int lane = threadIdx.x % kWave;
+    const int64_t w0 = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + threadIdx.x / kWave));
+    const int64_t nw = (int64_t)gridDim.x * 4;
+    for (int64_t t = w0; t < rows; t += nw) {
+        const uint16_t* src = x + t * (int64_t)cols;
+        uint8_t* dst = codes + t * (int64_t)cols;
+        Vec16 v[kCh];
+#pragma unroll
+        for (int i = 0; i < kCh; ++i)
+            v[i] = *(const Vec16*)(src + min(lane * 8 + i * kStep, cols - 8));
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < kCh; ++i)
+            if (lane * 8 + i * kStep < cols)
+                amax = amax8(v[i], amax);
+#pragma unroll
+        for (int o = kWave / 2; o > 0; o >>= 1)
+            amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+        const int e = fp8_scale_exp(amax);
+        const float inv_s = ldexpf(1.0f, -e);
+#pragma unroll
+        for (int i = 0; i < kCh; ++i)
+            if (lane * 8 + i * kStep < cols)
+                *(uint2*)(dst + lane * 8 + i * kStep) = encode8(v[i], inv_s);
+        if (inv) {
+            if (lane < k)
+                scales[inv[t * k + lane]] = ldexpf(1.0f, e);
+        } else if (lane == 0) {
+            scales[t] = ldexpf(1.0f, e);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_act_quant(const void* x, int64_t rows, int cols, int k, const int32_t* inv, uint8_t* codes,
                             float* scales, hipStream_t s)
 {
-    const int64_t blocks = std::min<int64_t>(rows, 16384);
-    if (blocks < 1)
+    if (rows < 1)
         return hipSuccess;
-    hipLaunchKernelGGL(act_quant_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const uint16_t*)x, rows, cols, k,
-                       inv, codes, scales);
+    if (cols <= 4096) {
+        const int64_t blocks = std::min<int64_t>((rows + 3) / 4, 16384);
+        hipLaunchKernelGGL(act_quant_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const uint16_t*)x, rows,
+                           cols, k, inv, codes, scales);
+    } else {
+        const int64_t blocks = std::min<int64_t>(rows, 16384);
+        hipLaunchKernelGGL(act_quant_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const uint16_t*)x, rows, cols,
+                           k, inv, codes, scales);
+    }
     return hipGetLastError();
 }
 

@@ -303,6 +303,116 @@ __device__ __forceinline__ void stage(const i32x4& ra, const LoadSrc<A_INS>& ls,
 }
 
 // ---------------------------------------------------------------------------
+// bf16 weights on v_mfma_f32_16x16x32_bf16 (M16 path): one MFMA k step per
+// 32-wide K stage. A wave's 128 x 128 block is 8 x 8 MFMA blocks of 16 x 16;
+// Acc4 holds the four 16x16 blocks of one 32x32 region, q[2*ri + cj] for
+// rows 16*ri .. and columns 16*cj ... Operand lanes: A lane l holds row l%16
+// and k 8*(l/16) .. +8 (chunk l/16 of the stage's A row), B lane l the same
+// k of weight row l%16; D lane l holds column l%16, rows 4*(l/16) + q. Per
+// element of work this shape moves half the accumulator registers of the
+// 32x32x16 shape, which saves power in a power-bound loop.
+struct Acc4 {
+    floatx4 q[4];
+};
+
+template <int BM, int BN, int WM, int WN>
+struct FragReader16 {
+    const Stage<BM, BN, false>* st;
+    int wm, wn, lane;
+    // A fragment of the wave's 16-row group i.
+    __device__ __forceinline__ bf16x8 a(int i) const
+    {
+        const int r = wm * WM + i * 16 + (lane & 15);
+        return as_bf16x8(st->a[r * kCH + swz(r, lane >> 4)]);
+    }
+    // B fragment of the wave's 16-row weight group j: weight row n of the
+    // tile and k chunk c = lane/16 are lane slot n%32 + 32*(c%2) of the 1 KiB
+    // block (n/32, 16-k step c/2).
+    __device__ __forceinline__ bf16x8 b(int j) const
+    {
+        const int n = wn * WN + j * 16 + (lane & 15);
+        const int c = lane >> 4;
+        return as_bf16x8(st->b[((n >> 5) * 2 + (c >> 1)) * 64 + (n & 31) + 32 * (c & 1)]);
+    }
+};
+
+// One K stage of the M16 path, software-pipelined like stage():
+//   first half:  MFMAs of the upper row groups (0 .. MH-1), column-major,
+//                with fragments read during the previous stage; the reads of
+//                this stage's lower-row A fragments; half of the loads.
+//   middle:      the same wait and barrier as stage().
+//   second half: MFMAs of the lower row groups, column-major; right after a
+//                column's last MFMA its B fragment is read again from the
+//                NEXT stage, and the next stage's upper-row A fragments are
+//                read first thing; the other half of the loads.
+// Row groups (32 rows) past RG hold only padding: their MFMAs and their
+// this-stage reads are left out; loads, waits, barriers and next-stage reads
+// are the same in every variant.
+template <int BM, int BN, int WM, int WN, int A_INS, int B_INS, int RG>
+__device__ __forceinline__ void stage16(const i32x4& ra, const LoadSrc<A_INS>& ls, uint32_t ld_lds, int KB, int wv,
+                                        uint32_t lane16, const Stage<BM, BN, false>* st,
+                                        const Stage<BM, BN, false>* st_next, int wm, int wn, int lane,
+                                        bf16x8 (&fa)[WM / 16], bf16x8 (&fb)[WN / 16], Acc4 (&acc)[WM / 32][WN / 32])
+{
+    constexpr int MI = WM / 16, NI = WN / 16;  // 16-row and 16-column groups
+    constexpr int MH = MI / 2;                 // row groups per half
+    constexpr int NLD = A_INS + B_INS;
+    constexpr int L0 = NLD / 2;                // loads in the first half
+    constexpr int M = MH * NI;                 // MFMAs per half
+    constexpr int RS = M / 2;                  // first-half reads spread over the first RS MFMAs
+    const FragReader16<BM, BN, WM, WN> rd{st, wm, wn, lane}, rn{st_next, wm, wn, lane};
+
+    int nread = 0, nld = 0;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const int j = m / MH, i = m % MH;
+        if ((i >> 1) < RG) {
+            floatx4& c = acc[i >> 1][j >> 1].q[(i & 1) * 2 + (j & 1)];
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], c, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (; nread < MH && nread < ((m + 1) * MH + RS - 1) / RS; ++nread) {
+            if (((MH + nread) >> 1) < RG)
+                fa[MH + nread] = rd.a(MH + nread);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (; nld < ((m + 1) * L0) / M; ++nld) {
+            issue_load<BM, BN, false, A_INS, B_INS>(nld, ra, ls, KB, wv, lane16, ld_lds);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(%0)" ::"n"(2 * NLD + L0) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const int j = m / MH, i = MH + m % MH;
+        if ((i >> 1) < RG) {
+            floatx4& c = acc[i >> 1][j >> 1].q[(i & 1) * 2 + (j & 1)];
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], c, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (m < MH) {  // the upper-row A fragments are free after the first half
+            fa[m] = rn.a(m);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (m % MH == MH - 1) {  // column j done
+            fb[j] = rn.b(j);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (; nld < L0 + ((m + 1) * (NLD - L0)) / M; ++nld) {
+            issue_load<BM, BN, false, A_INS, B_INS>(nld, ra, ls, KB, wv, lane16, ld_lds);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // 8-bit activations and weights (Q8): v_mfma_scale_f32_32x32x64_f8f6f4, E4M3 x
 // E4M3, one 64-wide k step per stage. A stage has the bf16 stage's shape in
 // bytes: A rows of 64 codes (four 16-byte chunks, swizzled as for bf16), and
@@ -557,6 +667,39 @@ __device__ __forceinline__ void tile_stages(const i32x4& ra, const LoadSrc<A_INS
     } while (++j < nkt);
 }
 
+// tile_stages for the M16 path (stage16 per stage).
+template <int BM, int BN, int WM, int WN, int A_INS, int B_INS, int RG>
+__device__ __forceinline__ void tile_stages16(const i32x4& ra, const LoadSrc<A_INS>& cs, int nkt, bool has_nxt,
+                                              const i32x4& nrb, int nkt0, const uint32_t (&cpart)[A_INS],
+                                              uint32_t Kbytes, int KB, int wv, uint32_t lane16,
+                                              Ring<BM, BN, false, false>& ring, uint32_t ring0, int& b, int wm,
+                                              int wn, int lane, bf16x8 (&fa)[WM / 16], bf16x8 (&fb)[WN / 16],
+                                              const uint32_t (&held)[A_INS], Acc4 (&acc)[WM / 32][WN / 32])
+{
+    constexpr uint32_t kStageBytes = sizeof(Stage<BM, BN, false>);
+    int j = 0;
+    do {  // a tile has at least kAhead stages
+        const int ja = j + kAhead;
+        LoadSrc<A_INS> ls = cs;
+        if (ja < nkt) {
+            ls.kt = cs.kt + ja;
+        } else if (has_nxt) {
+            ls.rb = nrb;
+#pragma unroll
+            for (int i = 0; i < A_INS; ++i)
+                ls.aoff[i] = held[i] * Kbytes + cpart[i];
+            ls.kt = nkt0 + (ja - nkt);
+        } else {
+            ls.kt = cs.kt + nkt - 1;
+        }
+        const int bl = b + kAhead >= kRing ? b + kAhead - kRing : b + kAhead;
+        const int bn = b + 1 >= kRing ? 0 : b + 1;
+        stage16<BM, BN, WM, WN, A_INS, B_INS, RG>(ra, ls, ring0 + (uint32_t)bl * kStageBytes, KB, wv, lane16,
+                                                 &ring.st[b], &ring.st[bn], wm, wn, lane, fa, fb, acc);
+        b = bn;
+    } while (++j < nkt);
+}
+
 // tile_stages for Q8 (same stream, stage_q8 per stage).
 template <int BM, int BN, int WM, int WN, int A_INS, int B_INS, int RG>
 __device__ __forceinline__ void tile_stages_q8(const i32x4& ra, const LoadSrc<A_INS>& cs, int nkt, bool has_nxt,
@@ -744,14 +887,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         }
     }
 
-    floatx16 acc[MI][NI];
+    // bf16 weights run the M16 path (16x16x32 MFMAs); fp8 weights the
+    // 32x32 shapes.
+    constexpr bool M16 = !F8 && !Q8;
+    using AccT = typename std::conditional<M16, Acc4, floatx16>::type;
+    AccT acc[MI][NI];
+    auto zero_acc = [&]() {
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < NI; ++j)
+            for (int j = 0; j < NI; ++j) {
+                if constexpr (M16) {
 #pragma unroll
-            for (int q = 0; q < 16; ++q)
-                acc[i][j][q] = 0.f;
+                    for (int c = 0; c < 4; ++c)
+                        acc[i][j].q[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 16; ++q)
+                        acc[i][j][q] = 0.f;
+                }
+            }
+    };
+    zero_acc();
 
     // Prologue: the first kAhead stages of the stream (all of the first tile,
     // which has at least kAhead stages), then the k step 0 fragments of the
@@ -771,8 +928,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     asm volatile("" ::: "memory");
     bf16x8 fa[MI];
     typename BFrag<F8>::raw fb[NI];
-    v8i qa[2], qb[NI];  // Q8 fragments
-    if constexpr (Q8) {
+    v8i qa[2], qb[NI];                   // Q8 fragments
+    bf16x8 fa16[2 * MI], fb16[2 * NI];  // M16 fragments
+    if constexpr (M16) {
+        const FragReader16<BM, BN, WM, WN> r0{&ring.st[0], wm, wn, lane};
+#pragma unroll
+        for (int j = 0; j < 2 * NI; ++j)
+            fb16[j] = r0.b(j);
+#pragma unroll
+        for (int i = 0; i < MI; ++i)  // the upper row groups (first half)
+            fa16[i] = r0.a(i);
+    } else if constexpr (Q8) {
         const FragReaderQ8<BM, BN, WM, WN> r0{&ring.st[0], wm, wn, lane};
 #pragma unroll
         for (int j = 0; j < NI; ++j)
@@ -802,6 +968,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 tile_stages_q8<BM, BN, WM, WN, A_INS, B_INS, GG>(ra, cs, cur.nkt, has_nxt, nrb, nxt.kt0, cpart,
                                                                  Kbytes, KB, wv, lane16, ring, ring0, b, wm, wn,
                                                                  lane, qa, qb, sa, sb, held, acc);
+            else if constexpr (M16)
+                tile_stages16<BM, BN, WM, WN, A_INS, B_INS, GG>(ra, cs, cur.nkt, has_nxt, nrb, nxt.kt0, cpart, Kbytes,
+                                                                KB, wv, lane16, ring, ring0, b, wm, wn, lane, fa16,
+                                                                fb16, held, acc);
             else
                 tile_stages<BM, BN, WM, WN, F8, EPBUF, A_INS, B_INS, GG>(ra, cs, cur.nkt, has_nxt, nrb, nxt.kt0,
                                                                          cpart, Kbytes, KB, wv, lane16, ring, ring0,
@@ -870,7 +1040,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         auto epilogue = [&](auto partial) {
             constexpr bool PARTIAL = decltype(partial)::value;
             (void)nheld, (void)nsc, (void)nsa, (void)nsb;  // captured (used only in asm operands)
-            int rbase = wm * WM + 4 * (lane >> 5);
+            // Row of the lane's q = 0 accumulator inside a 32-row group (M16:
+            // of its 16-row block).
+            const int lq = M16 ? (lane >> 4) : (lane >> 5);
+            int rbase = wm * WM + 4 * lq;
             asm volatile("" : "+v"(rbase));
             if constexpr (GATE_UP) {
                 // Through LDS, one (32-row group, gate/up block pair) at a time:
@@ -902,12 +1075,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                         continue;
 #pragma unroll
                     for (int jp = 0; jp < NI; jp += 2) {
+                        if constexpr (M16) {
 #pragma unroll
-                        for (int q = 0; q < 16; ++q) {
-                            const int r = wr + 8 * (q / 4) + (q % 4);
-                            const int o = r * 32 + (((wc >> 2) ^ (r & 7)) << 2) + (wc & 3);
-                            ep[o] = acc[i][jp][q];
-                            ep[1024 + o] = acc[i][jp + 1][q];
+                            for (int c = 0; c < 4; ++c)  // 16x16 block (c/2, c%2) of the region
+#pragma unroll
+                                for (int q = 0; q < 4; ++q) {
+                                    const int r = 16 * (c >> 1) + 4 * (lane >> 4) + q;
+                                    const int cc = 16 * (c & 1) + (lane & 15);
+                                    const int o = r * 32 + (((cc >> 2) ^ (r & 7)) << 2) + (cc & 3);
+                                    ep[o] = acc[i][jp].q[c][q];
+                                    ep[1024 + o] = acc[i][jp + 1].q[c][q];
+                                }
+                        } else {
+#pragma unroll
+                            for (int q = 0; q < 16; ++q) {
+                                const int r = wr + 8 * (q / 4) + (q % 4);
+                                const int o = r * 32 + (((wc >> 2) ^ (r & 7)) << 2) + (wc & 3);
+                                ep[o] = acc[i][jp][q];
+                                ep[1024 + o] = acc[i][jp + 1][q];
+                            }
                         }
                         uint32_t hv[8];
 #pragma unroll
@@ -920,7 +1106,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                             hv[2 * t + 1] = (uint32_t)f32_to_bf16_bits(silu_rcp(gv[2]) * uv[2]) |
                                             ((uint32_t)f32_to_bf16_bits(silu_rcp(gv[3]) * uv[3]) << 16);
                         }
-                        const int row = min(rbase - 4 * (lane >> 5) + i * 32 + rr, cur.rows - 1);
+                        const int row = min(rbase - 4 * lq + i * 32 + rr, cur.rows - 1);
                         const int col = (cur.n * BN + wn * WN + jp * 32) / 2 + rc * 4;
                         Vec16* dst = (Vec16*)(H + (int64_t)(cur.row0 + row) * g.f + col);
                         dst[0] = Vec16{hv[0], hv[1], hv[2], hv[3]};
@@ -939,23 +1125,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 for (int i = 0; i < MI; ++i) {
                     if (PARTIAL && i >= RG)  // padding rows only: nothing to store
                         continue;
+                    if constexpr (M16) {
 #pragma unroll
-                    for (int q = 0; q < 16; ++q) {
-                        const int r = min(rbase + i * 32 + 8 * (q / 4) + (q % 4), cur.rows - 1);
-                        float* yrow = Ys + (int64_t)(cur.row0 + r) * g.d + cur.n * BN + wn * WN + (lane & 31);
+                        for (int ri = 0; ri < 2; ++ri)
 #pragma unroll
-                        for (int j = 0; j < NI; ++j)
-                            yrow[j * 32] = acc[i][j][q];
+                            for (int q = 0; q < 4; ++q) {
+                                const int r = min(rbase + i * 32 + 16 * ri + q, cur.rows - 1);
+                                float* yrow = Ys + (int64_t)(cur.row0 + r) * g.d + cur.n * BN + wn * WN + (lane & 15);
+#pragma unroll
+                                for (int j = 0; j < NI; ++j)
+#pragma unroll
+                                    for (int cj = 0; cj < 2; ++cj)
+                                        yrow[j * 32 + 16 * cj] = acc[i][j].q[ri * 2 + cj][q];
+                            }
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 16; ++q) {
+                            const int r = min(rbase + i * 32 + 8 * (q / 4) + (q % 4), cur.rows - 1);
+                            float* yrow = Ys + (int64_t)(cur.row0 + r) * g.d + cur.n * BN + wn * WN + (lane & 31);
+#pragma unroll
+                            for (int j = 0; j < NI; ++j)
+                                yrow[j * 32] = acc[i][j][q];
+                        }
                     }
                 }
             }
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int j = 0; j < NI; ++j)
-#pragma unroll
-                    for (int q = 0; q < 16; ++q)
-                        acc[i][j][q] = 0.f;
+            zero_acc();
             if constexpr (GATE_UP)
                 asm volatile("" : "+v"(nheld[0]), "+v"(nheld[1]), "+v"(nheld[2]), "+v"(nheld[3]) : : "memory");
             if constexpr (F8) {

@@ -33,6 +33,10 @@ SMALL = [
     # more gate/up tiles than compute units (each workgroup walks several) and
     # an expert whose last m-tile has 6 rows: waves whose rows are all padding
     C("last-tile-padding", 1030, 256, 1, 1, 6656, "bf16"),
+    # at least 4096 assignments: each expert's compaction is split over
+    # several workgroups; one hot expert takes every token, the other none
+    C("hot-expert-split-dispatch", 4608, 128, 2, 1, 128, "bf16", {0: 100.0}),
+    C("split-dispatch-k4", 1100, 128, 16, 4, 128, "bf16", {3: 2.0}),
 ]
 
 
@@ -49,6 +53,8 @@ def test_small_layer_parity(cfg):
         assert g["expert_counts"][5] == cfg.T and rep["empty_experts"] == cfg.E - 1
     if cfg.name == "skewed-masked-small":
         assert np.all(g["expert_counts"][44:] == 0)
+    if cfg.name == "hot-expert-split-dispatch":
+        assert g["expert_counts"][0] == cfg.T and g["expert_counts"][1] == 0
 
 
 # Both bf16 GEMM paths on the same inputs: the tiled grouped GEMMs and the

@@ -42,33 +42,6 @@ __device__ __forceinline__ int fp8_scale_exp(float amax)
     return e < -126 ? -126 : e;
 }
 
-// E4M3 code of v = w * 2^-e (exact), |v| <= 448.
-__device__ __forceinline__ uint32_t fp8_encode(float v)
-{
-    const uint32_t bits = __float_as_uint(v);
-    const uint32_t sign = (bits >> 31) << 7;
-    const float a = fabsf(v);
-    uint32_t E, m;
-    if (a < 0.015625f) {  // below 2^-6: steps of 2^-9 (a count of 8 is the smallest normal)
-        const uint32_t q = (uint32_t)rintf(a * 512.0f);  // exact scaling, round half to even
-        E = q >> 3;
-        m = q & 7u;
-    } else {
-        const uint32_t ab = bits & 0x7FFFFFFFu;
-        const uint32_t mant = ab & 0x7FFFFFu;
-        E = (ab >> 23) - 127 + 7;
-        m = mant >> 20;
-        const uint32_t rem = mant & 0xFFFFFu;  // the 20 bits dropped
-        if (rem > 0x80000u || (rem == 0x80000u && (m & 1u)))
-            ++m;
-        if (m == 8u) {
-            m = 0;
-            ++E;
-        }
-    }
-    return sign | (E << 3) | m;
-}
-
 // Per-row scales. One wave per row of `cols` bf16 values (cols % 8 == 0);
 // with `two_src`, combined row n of a [E][2f] matrix comes from w0 (gate) when
 // n % 64 < 32, else from w1 (up), source row (n/64)*32 + n%32 of expert e.
@@ -114,15 +87,25 @@ __device__ __forceinline__ float inv_pow2(float s)
 
 // Codes of 8 consecutive bf16 values (16 bytes) scaled by 1/scale, packed
 // little-endian into two words.
+// E4M3 codes of 8 bf16 values times 2^-e (exact, |v| <= 448), value i in
+// byte i. v_cvt_pk_fp8_f32 rounds to the nearest E4M3 value, ties to the even
+// mantissa, and gives a small value that rounds to zero the sign of its input:
+// the rule above (it agrees with an integer model of the rule on every f32
+// input of magnitude at most 448). It packs its two inputs into bytes 0, 1 of
+// the result, or into bytes 2, 3 over the old value.
 __device__ __forceinline__ uint2 encode8(const Vec16 v, float inv_scale)
 {
-    uint32_t c[8];
+    uint32_t w[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        c[2 * i] = fp8_encode(__uint_as_float(v[i] << 16) * inv_scale);
-        c[2 * i + 1] = fp8_encode(__uint_as_float(v[i] & 0xFFFF0000u) * inv_scale);
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t a = v[2 * h], b = v[2 * h + 1];
+        int r = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(a << 16) * inv_scale,
+                                                __uint_as_float(a & 0xFFFF0000u) * inv_scale, 0, false);
+        r = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(b << 16) * inv_scale,
+                                            __uint_as_float(b & 0xFFFF0000u) * inv_scale, r, true);
+        w[h] = (uint32_t)r;
     }
-    return make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+    return make_uint2(w[0], w[1]);
 }
 
 // Blocked fp8 layout (see the file comment), one 16-byte lane chunk per thread.
@@ -253,13 +236,14 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* x, int64
 }
 
 // The same for rows of at most 4096 values, one wave per row (4 rows per
-// block): lane l holds values l*8 + i*512, i < 8 (chunk loads
-// unconditional, as above), the row maximum is a wave reduction, and no
-// barrier is needed.
+// block): lane l holds values l*8 + i*512, i < kCh, with cols <= kCh*512
+// (chunk loads unconditional, as above), the row maximum is a wave
+// reduction, and no barrier is needed.
+template <int kCh>
 __global__ __launch_bounds__(256) void act_quant_rows_kernel(const uint16_t* x, int64_t rows, int cols, int k,
                                                              const int32_t* inv, uint8_t* codes, float* scales)
 {
-    constexpr int kCh = 8, kStep = kWave * 8;
+    constexpr int kStep = kWave * 8;
     const int lane = threadIdx.x % kWave;
     const int64_t w0 = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + threadIdx.x / kWave));
     const int64_t nw = (int64_t)gridDim.x * 4;
@@ -302,8 +286,18 @@ hipError_t launch_act_quant(const void* x, int64_t rows, int cols, int k, const 
         return hipSuccess;
     if (cols <= 4096) {
         const int64_t blocks = std::min<int64_t>((rows + 3) / 4, 16384);
-        hipLaunchKernelGGL(act_quant_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const uint16_t*)x, rows,
-                           cols, k, inv, codes, scales);
+        auto go = [&](auto kern) {
+            hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, s, (const uint16_t*)x, rows, cols, k, inv,
+                               codes, scales);
+        };
+        if (cols <= 512)
+            go(act_quant_rows_kernel<1>);
+        else if (cols <= 1024)
+            go(act_quant_rows_kernel<2>);
+        else if (cols <= 2048)
+            go(act_quant_rows_kernel<4>);
+        else
+            go(act_quant_rows_kernel<8>);
     } else {
         const int64_t blocks = std::min<int64_t>(rows, 16384);
         hipLaunchKernelGGL(act_quant_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const uint16_t*)x, rows, cols,

@@ -106,6 +106,30 @@ def test_quantize_matches_oracle_on_special_rows():
     assert np.array_equal(scales.view(np.uint32), rs.view(np.uint32))
 
 
+def test_quantize_matches_oracle_on_every_bf16_value():
+    # Every finite bf16 value of magnitude at most 448 (both signs, the
+    # subnormals included), scaled by 2^s: a row whose largest magnitude is
+    # 448 * 2^s, so its scale is 2^s and each value meets the encoder unscaled.
+    pos = np.arange(0x0000, 0x43E1, dtype=np.uint32)
+    base = np.concatenate([pos, pos | 0x8000]).astype(np.uint32)
+    vals = (base << 16).view(np.float32)
+    cols = (vals.size + 63) // 64 * 64
+    rows = []
+    for s in (0, 5, 100):
+        r = np.zeros(cols, dtype=np.float32)
+        r[: vals.size] = vals * np.float32(2.0 ** s)  # exact: no overflow, no rounding
+        rows.append(r)
+    w = f32_to_bf16_bits(np.stack(rows))
+    assert np.array_equal(w[0, : vals.size], base.astype(np.uint16))
+    print(f"every bf16 value: {w.shape}", flush=True)
+    codes, scales = gpu_quantize(w)
+    rc, rs = oracle.quantize_fp8(w)
+    assert np.array_equal(scales.view(np.uint32), rs.view(np.uint32))
+    assert rs.tolist() == [1.0, 32.0, 2.0 ** 100]
+    bad = np.argwhere(codes != rc)
+    assert bad.size == 0, f"codes differ at {bad[:5].tolist()}: gpu {codes[tuple(bad[0])]} oracle {rc[tuple(bad[0])]}"
+
+
 @pytest.mark.parametrize("shape", [(8 * 2 * 256, 512), (3, 8), (1000, 136), (64, 14336)])
 def test_quantize_matches_oracle_on_weights(shape):
     rows, cols = shape

@@ -63,9 +63,11 @@ struct colibri_moe {
     int32_t* inv;
     void* H;      // [A][f] dtype
     float* Ys;    // down GEMM output: kMaxSplit (bf16) or 1 (f32) partials of [A][d] fp32
+    int32_t* ccnt;  // fused combine: arrivals per token and 128-column tile [max_tokens][d/128], zero between calls
     bool timing;
     hipEvent_t ev[kStages + 1];
     int group_n;    // tile order of the grouped GEMMs (n-tiles per group)
+    bool fuse_combine;  // bf16 tiled path: combine in the down GEMM's epilogue
     int cus;        // compute units of the device (persistent GEMM grid)
     int dec_max_a;  // bf16 calls with T*k <= dec_max_a take the small-batch path
     int dec_split_gu, dec_split_dn;  // its K slices (gate/up, down)
@@ -196,6 +198,7 @@ colibri_moe_status_t init_impl(colibri_moe* h, const colibri_moe_weights_t* w)
         ys_floats = std::max(ys_floats, (size_t)h->dec_split_dn * ad * d);
     }
     const size_t o_ys = cv.take(ys_floats * sizeof(float));
+    const size_t o_ccnt = h->fuse_combine ? cv.take((size_t)c.max_tokens * (d / 128) * sizeof(int32_t)) : 0;
     h->arena_bytes = cv.off;
 
     if (hipMalloc(&h->arena, h->arena_bytes) != hipSuccess) {
@@ -223,8 +226,11 @@ colibri_moe_status_t init_impl(colibri_moe* h, const colibri_moe_weights_t* w)
     h->inv = (int32_t*)(base + o_inv);
     h->H = base + o_h;
     h->Ys = (float*)(base + o_ys);
+    h->ccnt = h->fuse_combine ? (int32_t*)(base + o_ccnt) : nullptr;
 
     hipStream_t s = h->stream;
+    if (h->ccnt)
+        CMOE_HIP(hipMemsetAsync(h->ccnt, 0, (size_t)c.max_tokens * (d / 128) * sizeof(int32_t), s));
     CMOE_HIP(launch_transpose_router(w->w_router, h->w_rt, (int)d, (int)E, (int)es, s));
     if (w->b_router)
         CMOE_HIP(hipMemcpyAsync(h->b_r, w->b_router, E * sizeof(float), hipMemcpyDeviceToDevice, s));
@@ -284,6 +290,14 @@ colibri_moe_status_t colibri_moe_init(colibri_moe_t** out, const colibri_moe_con
     // Tile order of the grouped GEMMs (tuning only; results do not depend
     // on it): CMOE_GROUP_N n-tiles per group.
     h->group_n = env_int("CMOE_GROUP_N", 64, 1, 1 << 20);
+    // Combine fused into the down GEMM's epilogue (bf16 layers, tiled path)
+    // with CMOE_FUSE_COMBINE=1; the default runs the combine kernel, which is
+    // faster here: the fused form needs device-scope release/acquire fences
+    // in every tile's epilogue (L2 write-back and invalidation across the
+    // XCDs' separate L2s) and reads the other rows of a token with little
+    // memory parallelism on the GEMM's critical path. Results are identical
+    // either way.
+    h->fuse_combine = cfg->dtype == COLIBRI_MOE_BF16 && env_int("CMOE_FUSE_COMBINE", 0, 0, 1) != 0;
     if (hipGetDevice(&h->device) != hipSuccess ||
         hipDeviceGetAttribute(&h->cus, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess ||
         h->cus <= 0) {
@@ -369,6 +383,7 @@ colibri_moe_status_t colibri_moe_forward(colibri_moe_t* h, const void* x, int32_
 
     const int A = T * c.top_k;
     int split = 1;
+    bool fused = false;  // combine done by the down GEMM
     if (bf && A <= h->dec_max_a) {
         // small-batch path: weight streaming with K slices, then the slice sum
         // and SiLU(g)*u
@@ -399,13 +414,22 @@ colibri_moe_status_t colibri_moe_forward(colibri_moe_t* h, const void* x, int32_
         split = bf ? down_split_bf16(A, c.n_experts, c.d_model, c.d_ff, h->cus, q8 ? 1 : 0) : 1;
         GemmArgs dn{q8 ? (const void*)h->hq : h->H, h->w_d, h->s_d, q8 ? h->hsc : nullptr, h->Ys, offsets, perm, A,
                     c.n_experts, c.top_k, c.d_model, c.d_ff, h->group_n, split, h->cus};
+        if (bf && h->ccnt) {
+            dn.cnt = h->ccnt;
+            dn.inv = inv;
+            dn.topw = topw;
+            dn.y = y;
+            fused = true;
+        }
         CMOE_HIP(bf ? launch_down_bf16(dn, s) : launch_down_f32(dn, s));
     }
     if (tm)
         CMOE_HIP(hipEventRecord(h->ev[5], s));
 
-    CombineArgs ca{h->Ys, inv, topw, y, T, c.top_k, c.d_model, split, bf ? 1 : 0};
-    CMOE_HIP(launch_combine(ca, s));
+    if (!fused) {
+        CombineArgs ca{h->Ys, inv, topw, y, T, c.top_k, c.d_model, split, bf ? 1 : 0};
+        CMOE_HIP(launch_combine(ca, s));
+    }
     if (tm)
         CMOE_HIP(hipEventRecord(h->ev[6], s));
 

@@ -109,6 +109,16 @@ struct GemmArgs {
     int group_n;              // n-tiles per tile group (tile order), >= 1
     int split;                // K splits of the down GEMM (1 or 2; gate/up: 1)
     int grid;                 // workgroups of a persistent launch (compute units)
+    // Combine fused into the down GEMM (bf16 tiled path, optional; cnt ==
+    // nullptr: the combine kernel runs instead). cnt [T][d/128] counts, per token and
+    // n-tile, the k*split partial rows stored so far; the workgroup whose
+    // increment completes a count sums that token's columns of the tile
+    // (inv, topw: as for combine) into y (bf16 [T][d]) and resets the count
+    // to zero, so the counts are zero between calls.
+    int32_t* cnt;
+    const int32_t* inv;
+    const float* topw;
+    void* y;
 };
 hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t s);
 hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t s);

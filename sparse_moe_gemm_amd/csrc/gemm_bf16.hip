@@ -618,6 +618,92 @@ __device__ __forceinline__ Tile decode(const TileTable& t, int L, int NT, int S,
     return r;
 }
 
+// The combine, fused into the down GEMM's epilogue: after a tile has stored
+// its partial rows (rows row0 .. row0+rows of split s, columns n*BN .. +BN),
+// each of them counts one arrival for its token and n-tile. The arrival that
+// completes a count (k assignments times the K splits) finds every partial
+// row of that token and n-tile stored, and its wave computes the token's
+// columns of y exactly as the combine kernel does: partials added in split
+// order, weighted sum over the k slots in slot order (fused multiply-add in
+// fp32), rounded to bf16. Which workgroup does it changes nothing in the
+// result. Ordering: every wave's stores are released at device scope before
+// the barrier after which the counts are incremented; a wave that completed
+// counts acquires at device scope before it reads the other rows. Lane l of
+// wave w counts tile row w*64 + l (BM = 256 rows, 4 waves).
+template <int BN>
+__device__ __forceinline__ void fused_combine(const GemmArgs& g, int row0, int rows, int n, int wv, int lane)
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __builtin_amdgcn_s_barrier();
+    const int NTd = g.d / BN;
+    const int r = wv * kWave + lane;
+    int t = 0;
+    bool last = false;
+    if (r < rows) {
+        t = g.perm[row0 + r];
+        const int old = __hip_atomic_fetch_add(g.cnt + (int64_t)t * NTd + n, 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        last = old == g.k * g.split - 1;
+    }
+    uint64_t m = __ballot(last);
+    if (m == 0)
+        return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    // Lane b of a completed count fetches its token's k sorted positions and
+    // weights (k <= kMaxTopK) at once; the wave then sums the tokens one by one with
+    // all k*split row loads of a token in flight together.
+    int pos[kMaxTopK];
+    float wgt[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+        const bool on = last && j < g.k;
+        pos[j] = on ? g.inv[(int64_t)t * g.k + j] : 0;
+        wgt[j] = on ? g.topw[(int64_t)t * g.k + j] : 0.f;
+    }
+    const float* Ys = (const float*)g.out;
+    const int64_t stride = (int64_t)g.A_max * g.d;  // between K-split partials
+    const int c = n * BN + min(lane * 4, BN - 4);   // this lane's 4 columns (BN / 4 lanes)
+    while (m != 0) {
+        const int b = __builtin_ctzll(m);
+        m &= m - 1;
+        const int tt = __builtin_amdgcn_readlane(t, b);
+        float4 v[kMaxTopK][kMaxSplit];
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) {
+            const int p = __builtin_amdgcn_readlane(pos[j], b);
+            const float* row = Ys + (int64_t)p * g.d + c;
+            v[j][0] = *(const float4*)row;
+            v[j][1] = g.split > 1 ? *(const float4*)(row + stride) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) {
+            if (j < g.k) {
+                const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wgt[j]), b));
+                float4 u = v[j][0];
+                if (g.split > 1) {
+                    u.x += v[j][1].x;
+                    u.y += v[j][1].y;
+                    u.z += v[j][1].z;
+                    u.w += v[j][1].w;
+                }
+                acc.x = fmaf(wj, u.x, acc.x);
+                acc.y = fmaf(wj, u.y, acc.y);
+                acc.z = fmaf(wj, u.z, acc.z);
+                acc.w = fmaf(wj, u.w, acc.w);
+            }
+        }
+        if (lane * 4 < BN) {
+            uint2 packed;
+            packed.x = (uint32_t)f32_to_bf16_bits(acc.x) | ((uint32_t)f32_to_bf16_bits(acc.y) << 16);
+            packed.y = (uint32_t)f32_to_bf16_bits(acc.z) | ((uint32_t)f32_to_bf16_bits(acc.w) << 16);
+            *(uint2*)((uint16_t*)g.y + (int64_t)tt * g.d + c) = packed;
+        }
+        if (lane == 0)
+            __hip_atomic_store(g.cnt + (int64_t)tt * NTd + n, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 // Buffer resource of a tile's weight panel (blocked layout), bounded by the
 // end of its expert's weights.
 template <int BN>
@@ -1149,6 +1235,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                         }
                     }
                 }
+                if (g.cnt != nullptr)
+                    fused_combine<BN>(g, cur.row0, cur.rows, cur.n, wv, lane);
             }
             zero_acc();
             if constexpr (GATE_UP)

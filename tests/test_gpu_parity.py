@@ -86,6 +86,55 @@ def test_both_gemm_paths(cfg, path, monkeypatch):
     print(compare(cfg, inp, g), flush=True)
 
 
+# The combine fused into the down GEMM's epilogue (CMOE_FUSE_COMBINE=1, tiled
+# bf16 path) against the combine kernel (the default): both add the
+# same fp32 values in the same order, so y must be bit-identical, also with the
+# K split of the down GEMM (mixtral-small), 128-column tiles (ragged-17, d=384)
+# and k = 8; calls in a row and a smaller batch in between check that the
+# arrival counts are back at zero after every call.
+FUSED = [
+    C("mixtral-small", 700, 256, 8, 2, 512, "bf16"),
+    C("ragged-17", 17, 384, 16, 3, 384, "bf16"),
+    C("k8-E256", 64, 128, 256, 8, 128, "bf16"),
+    C("skewed-small", 2000, 256, 64, 2, 128, "bf16", {0: 4.0, 3: 4.0}),
+    C("fine-grained-small", 1000, 256, 128, 4, 256, "bf16"),
+]
+
+
+WEIGHTS = {"bf16": 0, "fp8-weights": 1 << 2, "w8a8": (1 << 2) | (1 << 3)}
+
+
+@pytest.mark.parametrize("weights", list(WEIGHTS))
+@pytest.mark.parametrize("cfg", FUSED, ids=[c.name for c in FUSED])
+def test_fused_combine_matches_combine_kernel(cfg, weights, monkeypatch):
+    import sparse_moe_gemm_amd as cm
+
+    assert WEIGHTS["w8a8"] == cm.FLAG_FP8_WEIGHTS | cm.FLAG_FP8_ACTIVATIONS
+    if weights == "w8a8" and min(cfg.d, cfg.f) < 256:
+        pytest.skip("8-bit activations need d_model, d_ff >= 256")
+    monkeypatch.setenv("CMOE_DECODE_MAX_A", "0")
+    print(f"case {cfg} {weights}", flush=True)
+    inp = synth.make_inputs(cfg)
+    monkeypatch.setenv("CMOE_FUSE_COMBINE", "0")
+    plain = make_layer(cfg, inp, flags=WEIGHTS[weights])
+    ref = run_gpu(plain, inp["x"])
+    ref_small = run_gpu(plain, inp["x"][: cfg.T // 2 + 1])
+    plain.close()
+    monkeypatch.setenv("CMOE_FUSE_COMBINE", "1")
+    fused = make_layer(cfg, inp, flags=WEIGHTS[weights])
+    runs = [run_gpu(fused, inp["x"]), run_gpu(fused, inp["x"])]
+    small = run_gpu(fused, inp["x"][: cfg.T // 2 + 1])
+    runs.append(run_gpu(fused, inp["x"]))
+    fused.close()
+    for g in runs:
+        for key in ref:
+            assert np.array_equal(g[key], ref[key]), key
+    for key in ref_small:
+        assert np.array_equal(small[key], ref_small[key]), key
+    if weights == "bf16":
+        print(compare(cfg, inp, runs[0]), flush=True)
+
+
 def test_empty_batch_and_errors():
     import torch
 

@@ -864,7 +864,9 @@ __device__ __forceinline__ void load_scales(const float* scales, const Tile& t, 
 // F8: 8-bit weights multiplied as bf16 (W8A16); Q8: 8-bit weights and
 // activations on the fp8 MFMA (W8A8; F8 is false then: the stage has the
 // bf16 layout's shape).
-template <int BM, int BN, int WM, int WN, bool GATE_UP, bool F8, bool Q8>
+// FC: the down GEMM with the combine fused into its epilogue (a separate
+// instantiation: its epilogue code would cost the plain kernel registers).
+template <int BM, int BN, int WM, int WN, bool GATE_UP, bool F8, bool Q8, bool FC = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void grouped_gemm_kernel(GemmArgs g)
 {
     static_assert(!(F8 && Q8), "one weight mode");
@@ -1235,7 +1237,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                         }
                     }
                 }
-                if (g.cnt != nullptr)
+                if constexpr (FC)
                     fused_combine<BN>(g, cur.row0, cur.rows, cur.n, wv, lane);
             }
             zero_acc();
@@ -1375,6 +1377,13 @@ hipError_t launch_grouped(const GemmArgs& a, hipStream_t s)
         // 2 * d_ff is a multiple of 256 (d_ff % 128 == 0 is checked at init)
         hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 256, 128, 128, true, F8, Q8>), dim3(grid), dim3(kThreads), 0,
                            s, a);
+    } else if (a.cnt != nullptr) {
+        if (BN == 256)
+            hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 256, 128, 128, false, F8, Q8, true>), dim3(grid),
+                               dim3(kThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 128, 128, 64, false, F8, Q8, true>), dim3(grid),
+                               dim3(kThreads), 0, s, a);
     } else {
         if (BN == 256)
             hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 256, 128, 128, false, F8, Q8>), dim3(grid), dim3(kThreads),

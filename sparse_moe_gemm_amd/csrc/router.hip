@@ -37,15 +37,11 @@ __device__ __forceinline__ uint32_t order_key(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        uint32_t lo = __shfl_xor((uint32_t)v, off, kWave);
-        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, kWave);
-        unsigned long long o = ((unsigned long long)hi << 32) | lo;
-        v = o > v ? o : v;
-    }
+    for (int off = 32; off >= 1; off >>= 1)
+        v = max(v, (uint32_t)__shfl_xor((int)v, off, kWave));
     return v;
 }
 
@@ -60,29 +56,33 @@ __device__ void topk_softmax_epilogue(const float* lg, int ldl, int bt, int t0, 
         const int t = t0 + r;
         if (t >= T)
             break;
-        unsigned long long key[4];
+        // Order keys of the token's logits (expert e = lane + 64q); an expert
+        // not present, or already taken, has key 0, below every logit's key.
+        // The largest key wins; among equal keys the lowest expert index.
+        uint32_t key[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int e = lane + q * kWave;
-            key[q] = e < E ? (((unsigned long long)order_key(lg[r * ldl + e]) << 32) |
-                              (uint32_t)(0xFFFFu - e))
-                           : 0ull;
+            key[q] = e < E ? order_key(lg[r * ldl + e]) : 0u;
         }
         float lsel[kMaxTopK];
         int isel[kMaxTopK];
         for (int j = 0; j < k; ++j) {
-            unsigned long long best = key[0];
+            uint32_t best = max(max(key[0], key[1]), max(key[2], key[3]));
+            best = wave_max_u32(best);
+            int e = E - 1;
 #pragma unroll
-            for (int q = 1; q < 4; ++q)
-                best = key[q] > best ? key[q] : best;
-            best = wave_max_u64(best);
-            const int e = min(0xFFFF - (int)(best & 0xFFFFu), E - 1);
+            for (int q = 3; q >= 0; --q) {
+                const uint64_t m = __ballot(key[q] == best && lane + q * kWave < E);
+                if (m != 0)
+                    e = q * kWave + __builtin_ctzll(m);
+            }
             isel[j] = e;
             lsel[j] = lg[r * ldl + e];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                if (key[q] == best)
-                    key[q] = 0ull;
+                if (lane + q * kWave == e)
+                    key[q] = 0u;
         }
         if (lane == 0) {
             const float l0 = lsel[0];
@@ -189,24 +189,43 @@ __global__ __launch_bounds__(W * kWave) void router_bf16_kernel(RouterArgs a)
     }
 
     // D layout of a 16x16 MFMA: lane holds rows 4*(lane/16)+i, column lane%16.
-    // The W partial sums are added in wave order (((w0 + w1) + w2) + ...).
-    for (int w = 0; w < W; ++w) {
-        if (wv == w) {
+    // The W partial sums are added in wave order (((w0 + w1) + w2) + ...):
+    // groups of up to 8 waves store their partials to LDS side by side, then
+    // every thread adds the group's partials of its elements in wave order.
+    constexpr int WG = W < 8 ? W : 8;
+    constexpr int NE = BT * EP;                       // logits of the block (padded)
+    constexpr int NS = (NE + W * kWave - 1) / (W * kWave);  // elements per thread
+    __shared__ float red[WG][NE];
+    float sum[NS];
+    for (int wg = 0; wg < W; wg += WG) {
+        if (wv >= wg && wv < wg + WG) {
+            float* dst = red[wv - wg];
 #pragma unroll
             for (int g = 0; g < TG; ++g)
 #pragma unroll
                 for (int n = 0; n < NG; ++n)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        float& dst = part[g * kTok + (lane >> 4) * 4 + i][n * 16 + (lane & 15)];
-                        dst = (w == 0) ? acc[g][n][i] : dst + acc[g][n][i];
-                    }
+                    for (int i = 0; i < 4; ++i)
+                        dst[(g * kTok + (lane >> 4) * 4 + i) * EP + n * 16 + (lane & 15)] = acc[g][n][i];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            const int idx = threadIdx.x + j * W * kWave;
+            if (idx < NE) {
+#pragma unroll
+                for (int w = 0; w < WG; ++w)
+                    sum[j] = (wg + w == 0) ? red[w][idx] : sum[j] + red[w][idx];
+            }
         }
         __syncthreads();
     }
-    for (int i = threadIdx.x; i < BT * a.E; i += W * kWave) {
-        const int r = i / a.E, e = i % a.E;
-        part[r][e] += a.b[e];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        const int idx = threadIdx.x + j * W * kWave;
+        const int e = idx % EP;
+        if (idx < NE)
+            part[idx / EP][e] = e < a.E ? sum[j] + a.b[e] : sum[j];  // then the bias
     }
     __syncthreads();
     store_logits(&part[0][0], LDL, BT, t0, a.T, a.E, a.logits);

@@ -17,15 +17,72 @@ namespace cmoe {
 
 namespace {
 
+__device__ __forceinline__ void store_out(const CombineArgs& g, int64_t t, int o, float4 acc)
+{
+    if (g.bf16_out) {
+        uint2 packed;
+        packed.x = (uint32_t)f32_to_bf16_bits(acc.x) | ((uint32_t)f32_to_bf16_bits(acc.y) << 16);
+        packed.y = (uint32_t)f32_to_bf16_bits(acc.z) | ((uint32_t)f32_to_bf16_bits(acc.w) << 16);
+        *(uint2*)((uint16_t*)g.y + t * g.d + o) = packed;
+    } else {
+        *(float4*)((float*)g.y + t * g.d + o) = acc;
+    }
+}
+
+// K slots and S partials known at compile time: the token's positions and
+// weights are loaded first, then all K*S row loads are in flight together.
+template <int K, int S>
+__global__ __launch_bounds__(256) void combine_ks_kernel(CombineArgs g)
+{
+    const int64_t groups = (int64_t)g.T * (g.d / 4);
+    const int64_t stride = (int64_t)g.T * K * g.d;
+    for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < groups;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t t = idx / (g.d / 4);
+        const int o = (int)(idx % (g.d / 4)) * 4;
+        int pos[K];
+        float wgt[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            pos[j] = g.inv[t * K + j];
+            wgt[j] = g.w[t * K + j];
+        }
+        float4 v[K][S];
+#pragma unroll
+        for (int j = 0; j < K; ++j)
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+                v[j][s] = *(const float4*)(g.ys + (int64_t)pos[j] * g.d + o + s * stride);
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            float4 u = v[j][0];
+#pragma unroll
+            for (int s = 1; s < S; ++s) {
+                u.x += v[j][s].x;
+                u.y += v[j][s].y;
+                u.z += v[j][s].z;
+                u.w += v[j][s].w;
+            }
+            acc.x = fmaf(wgt[j], u.x, acc.x);
+            acc.y = fmaf(wgt[j], u.y, acc.y);
+            acc.z = fmaf(wgt[j], u.z, acc.z);
+            acc.w = fmaf(wgt[j], u.w, acc.w);
+        }
+        store_out(g, t, o, acc);
+    }
+}
+
+// Any k and number of partials (the small-batch path's K slices).
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs g)
 {
     const int64_t groups = (int64_t)g.T * (g.d / 4);
+    const int64_t stride = (int64_t)g.T * g.k * g.d;
     for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < groups;
          idx += (int64_t)gridDim.x * blockDim.x) {
         const int64_t t = idx / (g.d / 4);
         const int o = (int)(idx % (g.d / 4)) * 4;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        const int64_t stride = (int64_t)g.T * g.k * g.d;
         for (int j = 0; j < g.k; ++j) {
             const float wj = g.w[t * g.k + j];
             const float* row = g.ys + (int64_t)g.inv[t * g.k + j] * g.d + o;
@@ -42,15 +99,20 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs g)
             acc.z = fmaf(wj, v.z, acc.z);
             acc.w = fmaf(wj, v.w, acc.w);
         }
-        if (g.bf16_out) {
-            uint2 packed;
-            packed.x = (uint32_t)f32_to_bf16_bits(acc.x) | ((uint32_t)f32_to_bf16_bits(acc.y) << 16);
-            packed.y = (uint32_t)f32_to_bf16_bits(acc.z) | ((uint32_t)f32_to_bf16_bits(acc.w) << 16);
-            *(uint2*)((uint16_t*)g.y + t * g.d + o) = packed;
-        } else {
-            *(float4*)((float*)g.y + t * g.d + o) = acc;
-        }
+        store_out(g, t, o, acc);
     }
+}
+
+template <int K>
+bool launch_ks(const CombineArgs& a, dim3 grid, hipStream_t s)
+{
+    if (a.k != K || a.split > 2)
+        return false;
+    if (a.split == 1)
+        hipLaunchKernelGGL((combine_ks_kernel<K, 1>), grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((combine_ks_kernel<K, 2>), grid, dim3(256), 0, s, a);
+    return true;
 }
 
 }  // namespace
@@ -61,7 +123,11 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s)
     int64_t blocks = (groups + 255) / 256;
     if (blocks > 8192)
         blocks = 8192;
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    const dim3 grid((unsigned)blocks);
+    if (!(launch_ks<1>(a, grid, s) || launch_ks<2>(a, grid, s) || launch_ks<3>(a, grid, s) ||
+          launch_ks<4>(a, grid, s) || launch_ks<5>(a, grid, s) || launch_ks<6>(a, grid, s) ||
+          launch_ks<7>(a, grid, s) || launch_ks<8>(a, grid, s)))
+        hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -125,6 +125,8 @@ hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t s);
 // K splits the bf16 down GEMM uses for a call with A = T*k assignments on
 // `cus` compute units (1 or 2; the Ys workspace holds kMaxSplit partials).
 constexpr int kMaxSplit = 2;
+// (the fused combine's loads in gemm_bf16.hip cover at most two partials)
+static_assert(kMaxSplit == 2, "fused combine: one or two K-split partials");
 int down_split_bf16(int A, int E, int d, int f, int cus, int q8);
 hipError_t launch_gate_up_f32(const GemmArgs& a, hipStream_t s);
 hipError_t launch_down_f32(const GemmArgs& a, hipStream_t s);

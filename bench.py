@@ -252,7 +252,7 @@ def main():
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak_mm, "unit": "TFLOP/s",
                 "frac": achieved / peak_mm, "traffic": profiled_traffic(prof_key, dom),
                 "kernel": "grouped_gemm_kernel<256,256,128,128,true,"
-                          f"{str(fp8 and not q8).lower()},{str(q8).lower()}> (gate/up)"}
+                          f"{str(fp8 and not q8).lower()},{str(q8).lower()},false> (gate/up)"}
 
     out = {
         "metric": METRIC,

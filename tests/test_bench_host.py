@@ -41,7 +41,7 @@ def test_traffic_missing_summary_or_value(tmp_path, monkeypatch):
     assert bench.profiled_traffic("other", "gate_up_gemm") is None
 
 
-def test_committed_summaries_match_their_sources():
+def test_committed_summaries_are_complete():
     # every committed summary gives the command it came from, its traffic
     # figure and the hash of the source file its counters were taken on
     prof = os.path.join(bench.ROOT, "profiles")

@@ -58,6 +58,7 @@ def lib():
             "moe_oracle_widen": [P, ctypes.c_int, i64, P],
             "moe_oracle_router": [LP, P, i32, P],
             "moe_oracle_topk": [P, i32, i32, i32, P, P, P],
+            "moe_oracle_route_weights": [P, i32, i32, i32, P, P, P],
             "moe_oracle_dispatch": [P, i32, i32, i32, P, P, P, P, P],
             "moe_oracle_expert_ffn": [LP, i32, P, P, P],
             "moe_oracle_expert_ffn_ex": [LP, i32, P, P, P, i32],
@@ -183,6 +184,20 @@ def topk(logits, k: int):
     wd = np.empty((T, k), dtype=np.float64)
     _check(lib().moe_oracle_topk(_ptr(lg), T, E, k, _ptr(ids), _ptr(w), _ptr(wd)), "topk")
     return ids, w, wd
+
+
+def route_weights(logits, ids):
+    """(w [T][k] fp32, w [T][k] double): the softmax over the logits of the given
+    experts ids [T][k], renormalised, exponent shifted by slot 0's logit."""
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    T, E = lg.shape
+    k = ids.shape[1]
+    assert ids.shape[0] == T
+    w = np.empty((T, k), dtype=np.float32)
+    wd = np.empty((T, k), dtype=np.float64)
+    _check(lib().moe_oracle_route_weights(_ptr(lg), T, E, k, _ptr(ids), _ptr(w), _ptr(wd)), "route_weights")
+    return w, wd
 
 
 def dispatch(ids, E: int):

@@ -82,13 +82,8 @@ static int precedes(const float* l, int a, int b)
     return l[a] > l[b] || (l[a] == l[b] && a < b);
 }
 
-/* Top-k selection and routing weights for one token. Selection on the raw
- * logits («Colibri 是什么» (xxqk.cn) §3.2 selects on logits; softmax is
- * monotone so the set equals the top-k of the softmax that
- * «Colibri：面向MoE模型的高性能C语言推理引擎» (zskr.cn) §2.2 fuses in); the
- * weights are the softmax restricted to the k winners, renormalised, with the
- * exponent shifted by the slot-0 logit. */
-static void topk_one(const float* l, int E, int k, int32_t* ids, double* wd)
+/* The k winners of one token, slot 0 first, in the selection order. */
+static void select_topk(const float* l, int E, int k, int32_t* ids)
 {
     unsigned char taken[1024];
     int big = E > 1024;
@@ -108,6 +103,13 @@ static void topk_one(const float* l, int E, int k, int32_t* ids, double* wd)
     }
     if (big)
         free(tk);
+}
+
+/* Routing weights of the given k experts: the softmax restricted to their
+ * logits, renormalised, with the exponent shifted by the slot-0 logit, in
+ * double. */
+static void route_weights(const float* l, int k, const int32_t* ids, double* wd)
+{
     double l0 = (double)l[ids[0]];
     double s = 0.0;
     for (int j = 0; j < k; ++j) {
@@ -116,6 +118,17 @@ static void topk_one(const float* l, int E, int k, int32_t* ids, double* wd)
     }
     for (int j = 0; j < k; ++j)
         wd[j] = wd[j] / s;
+}
+
+/* Top-k selection and routing weights for one token. Selection on the raw
+ * logits («Colibri 是什么» (xxqk.cn) §3.2 selects on logits; softmax is
+ * monotone so the set equals the top-k of the softmax that
+ * «Colibri：面向MoE模型的高性能C语言推理引擎» (zskr.cn) §2.2 fuses in); the
+ * weights are the softmax restricted to the k winners. */
+static void topk_one(const float* l, int E, int k, int32_t* ids, double* wd)
+{
+    select_topk(l, E, k, ids);
+    route_weights(l, k, ids, wd);
 }
 
 int moe_oracle_topk(const float* logits, int32_t T, int32_t E, int32_t k,
@@ -128,6 +141,30 @@ int moe_oracle_topk(const float* logits, int32_t T, int32_t E, int32_t k,
         double wd[256];
         double* wp = k <= 256 ? wd : (double*)malloc(sizeof(double) * (size_t)k);
         topk_one(logits + (int64_t)t * E, E, k, ids + (int64_t)t * k, wp);
+        for (int j = 0; j < k; ++j) {
+            w[(int64_t)t * k + j] = (float)wp[j];
+            if (w_f64)
+                w_f64[(int64_t)t * k + j] = wp[j];
+        }
+        if (wp != wd)
+            free(wp);
+    }
+    return 0;
+}
+
+int moe_oracle_route_weights(const float* logits, int32_t T, int32_t E, int32_t k,
+                             const int32_t* ids, float* w, double* w_f64)
+{
+    if (!logits || !ids || !w || T < 0 || E <= 0 || k <= 0 || k > E)
+        return -1;
+    for (int64_t a = 0; a < (int64_t)T * k; ++a)
+        if (ids[a] < 0 || ids[a] >= E)
+            return -2;
+#pragma omp parallel for schedule(static)
+    for (int32_t t = 0; t < T; ++t) {
+        double wd[256];
+        double* wp = k <= 256 ? wd : (double*)malloc(sizeof(double) * (size_t)k);
+        route_weights(logits + (int64_t)t * E, k, ids + (int64_t)t * k, wp);
         for (int j = 0; j < k; ++j) {
             w[(int64_t)t * k + j] = (float)wp[j];
             if (w_f64)
@@ -190,11 +227,10 @@ int moe_oracle_dispatch(const int32_t* ids, int32_t T, int32_t k, int32_t E,
  *   h_i = SiLU(g_i) * u_i = g_i / (1 + exp(-g_i)) * u_i
  *   out_o = sum_i h_i W_d[e][o][i] */
 static void quantize_row_values(double* v, int64_t n);
-static double bf16_round(double v);
 
-/* With act_fp8 (8-bit activations, reading in moe_oracle.h) the input row and
- * h enter their GEMMs as their 8-bit row-quantized values: the input row v as
- * given, h after rounding to bf16. xv is scratch of d doubles. */
+/* With act_fp8 (8-bit activations, reading in moe_oracle.h) the input row
+ * enters the gate and up products as its 8-bit row-quantized value; h stays
+ * in double. xv is scratch of d doubles. */
 static void expert_ffn(const moe_oracle_layer_t* L, int32_t e, const void* xbase, int64_t xoff,
                        double* h, double* out, int act_fp8, double* xv)
 {
@@ -213,11 +249,6 @@ static void expert_ffn(const moe_oracle_layer_t* L, int32_t e, const void* xbase
             u += xv[c] * elem(L->w_up, dt, wg0 + i * d + c);
         }
         h[i] = g / (1.0 + exp(-g)) * u;
-    }
-    if (act_fp8) {
-        for (int64_t i = 0; i < f; ++i)
-            h[i] = bf16_round(h[i]);
-        quantize_row_values(h, f);
     }
     for (int64_t o = 0; o < d; ++o) {
         double acc = 0.0;
@@ -304,13 +335,7 @@ int moe_oracle_forward_ex(const moe_oracle_layer_t* L, const void* x, int32_t T,
             if (forced_ids) {
                 for (int32_t j = 0; j < k; ++j)
                     ids[j] = forced_ids[(int64_t)t * k + j];
-                double l0 = (double)lg[ids[0]], s = 0.0;
-                for (int32_t j = 0; j < k; ++j) {
-                    wd[j] = exp((double)lg[ids[j]] - l0);
-                    s += wd[j];
-                }
-                for (int32_t j = 0; j < k; ++j)
-                    wd[j] = wd[j] / s;
+                route_weights(lg, k, ids, wd);
             } else {
                 topk_one(lg, E, k, ids, wd);
             }
@@ -411,19 +436,6 @@ static void quantize_row_values(double* v, int64_t n)
     const int e = row_scale_exp(amax);
     for (int64_t i = 0; i < n; ++i)
         v[i] = ldexp(moe_oracle_fp8_value(fp8_encode(ldexp(v[i], -e))), e);
-}
-
-/* v rounded to bf16 (8 significant bits), to nearest, ties to even; values
- * are far inside bf16's exponent range here. */
-static double bf16_round(double v)
-{
-    if (v == 0.0 || !isfinite(v))
-        return v;
-    int x;
-    (void)frexp(fabs(v), &x); /* |v| in [2^(x-1), 2^x) */
-    const double q = round_half_even(ldexp(fabs(v), 8 - x)); /* 8 significant bits */
-    const double r = ldexp(q, x - 8);
-    return v < 0 ? -r : r;
 }
 
 int moe_oracle_quantize_fp8(const void* w, int dtype, int64_t rows, int64_t cols,

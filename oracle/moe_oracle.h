@@ -74,6 +74,13 @@ int moe_oracle_router(const moe_oracle_layer_t* L, const void* x, int32_t T, flo
 int moe_oracle_topk(const float* logits, int32_t T, int32_t E, int32_t k,
                     int32_t* ids, float* w, double* w_f64);
 
+/* Routing weights of given experts: for each token the softmax over the
+ * logits of ids[t][0..k) renormalised, exponents shifted by the slot-0 logit
+ * (the weights the top-k would give if these were its winners, in this slot
+ * order). ids must lie in [0, E) (else -2). w [T][k] fp32; w_f64 nullable. */
+int moe_oracle_route_weights(const float* logits, int32_t T, int32_t E, int32_t k,
+                             const int32_t* ids, float* w, double* w_f64);
+
 /* Stable counting sort of assignments (t, j) by expert ids[t*k+j].
  * counts [E], offsets [E+1], perm [T*k] token ids, perm_slot [T*k] slots,
  * inv [T*k]: inv[t*k+j] = position p of that assignment. Any output but
@@ -131,13 +138,13 @@ double moe_oracle_fp8_value(uint8_t code);
 
 /* 8-bit activations (MOE_ORACLE_ACT_FP8): the pages store the expert weights
  * in 8 bits and say nothing of the activations; this optional mode reads the
- * roadmap's FP8 as FP8 matrix products, which need 8-bit inputs on both
- * sides. Reading: each expert GEMM input row is quantized by the rule above
- * (E4M3, one power-of-two scale per row): the token row x[t] (as given, per
- * token; the router still sees the full-precision x) before gate/up, and the
- * row h of each (token, expert) assignment before down, after rounding h to
- * bf16 (the activation storage type), nearest, ties to even. The products
- * and sums are then those of the dequantized values, in double as always. */
+ * roadmap's FP8 as an FP8 matrix product for the first expert GEMM, which
+ * needs 8-bit inputs on both sides. Reading: the token row x[t] (as given,
+ * per token; the router still sees the full-precision x) is quantized by the
+ * rule above (E4M3, one power-of-two scale per row) before the gate and up
+ * products; h and the down product keep the layer's precision (the weights'
+ * dequantized values, h in double here). The products and sums are those of
+ * the dequantized values, in double as always. */
 
 #ifdef __cplusplus
 }

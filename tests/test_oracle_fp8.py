@@ -3,8 +3,11 @@ one power-of-two scale per weight row; the reading is stated in
 oracle/moe_oracle.h). Each check uses something other than the encoder's own
 formula: values the E4M3 format fixes, a brute-force nearest-code search over
 all 256 codes, the minimality of the scale, and exactness of dequantization.
-The optional 8-bit activation mode is pinned by recomputing an expert FFN with
-those brute-force pieces and numpy, and by its routing on full-precision x."""
+The optional 8-bit activation mode (the token row enters the gate and up
+products 8-bit quantized; h and the down product keep the layer's precision) is
+pinned by recomputing an expert FFN with those brute-force pieces and numpy,
+by its routing on full-precision x, and by constructed rows where quantizing h,
+or rounding x before quantizing it, would change the result."""
 import math
 
 import numpy as np
@@ -140,15 +143,6 @@ def brute_force_row(vals):
     return [oracle.fp8_value(brute_force_code(v / 2.0 ** e)) * 2.0 ** e for v in vals]
 
 
-def bf16_nearest(v: float) -> float:
-    """Nearest value with 8 significant bits, ties to even (Python's round is
-    exact and ties to even on the scaled mantissa)."""
-    if v == 0.0:
-        return v
-    m, ex = math.frexp(v)  # v = m * 2^ex, 0.5 <= |m| < 1
-    return round(m * 256.0) / 256.0 * 2.0 ** ex
-
-
 def test_act_fp8_expert_ffn_by_brute_force():
     cfg = synth.LayerConfig("q8", 6, 32, 3, 2, 16, "bf16")
     inp = oracle.quantized_expert_weights(synth.make_inputs(cfg))
@@ -162,10 +156,9 @@ def test_act_fp8_expert_ffn_by_brute_force():
         for e in range(cfg.E):
             g, u = wg[e] @ xq, wu[e] @ xq
             h = g / (1.0 + np.exp(-g)) * u
-            hq = np.array(brute_force_row([bf16_nearest(float(v)) for v in h]))
-            want = wd[e] @ hq
+            want = wd[e] @ h
             out, h_or = L.expert_ffn(e, xrow, want_h=True, act_fp8=True)
-            assert np.allclose(h_or, hq, rtol=0, atol=0), (t, e)
+            assert np.allclose(h_or, h, rtol=1e-13, atol=1e-15), (t, e)
             assert np.allclose(out, want, rtol=1e-12, atol=1e-14), (t, e)
             # the mode changes the result (else this pin would be vacuous)
             assert not np.allclose(out, L.expert_ffn(e, xrow), rtol=1e-6, atol=0)
@@ -187,7 +180,7 @@ def test_act_fp8_routes_on_full_precision_x():
 
 
 def test_act_fp8_constructed_rounding_order():
-    """h is rounded to bf16 before it is quantized; x is quantized as given.
+    """x is quantized as given (not rounded to bf16 first); h is not quantized.
     fp32 layer, one expert, d = f = 2, identity down projection. Gate
     pre-activations of 64 make SiLU exact (SiLU(64) = 64 in double), so h is
     64 * up exactly."""
@@ -195,19 +188,18 @@ def test_act_fp8_constructed_rounding_order():
     small = 1.0625 + 2.0 ** -12  # just above the midpoint of codes 1.0 and 1.125
     wr = np.ones((2, 1), f32)
     wd = np.eye(2, dtype=f32)[None]
-    # 1) x = [1, 0] -> xq = x; h = [64*7, 64*small/64] = [448, small]: row scale
-    #    1; bf16 rounds small to the tie 1.0625, which goes to the even code
-    #    1.0 (quantized unrounded it would give 1.125).
+    # 1) x = [1, 0] -> xq = x; h = [64*7, 64*small/64] = [448, small]: h keeps
+    #    its value (quantized it would be [448, 1.125]; rounded to bf16 first,
+    #    [448, 1.0]).
     L = oracle.Layer(wr, None, np.array([[[64.0, 0.0], [64.0, 0.0]]], f32),
                      np.array([[[7.0, 0.0], [small / 64.0, 0.0]]], f32), wd, 1)
     x = np.array([1.0, 0.0], f32)
     out, h = L.expert_ffn(0, x, want_h=True, act_fp8=True)
-    assert list(h) == [448.0, 1.0] and list(out) == [448.0, 1.0]
-    out0, h0 = L.expert_ffn(0, x, want_h=True)
-    assert list(h0) == [448.0, small] and list(out0) == [448.0, small]
-    # 2) x = [small, 256]: row scale 1, quantized directly: xq = [1.125, 256].
-    #    g = 0.25 * x_1 = 64 for both units; u_0 = x_0 / 64, u_1 = 7/256 * x_1
-    #    = 7, so h = [xq_0, 448] = [1.125, 448] (already codes of scale 1).
+    assert list(h) == [448.0, small] and list(out) == [448.0, small]
+    # 2) x = [small, 256]: row scale 1, quantized directly: xq = [1.125, 256]
+    #    (rounded to bf16 first, small would be the tie 1.0625 and go to the
+    #    even code 1.0). g = 0.25 * x_1 = 64 for both units; u_0 = x_0 / 64,
+    #    u_1 = 7/256 * x_1 = 7, so h = [xq_0, 448] = [1.125, 448].
     L2 = oracle.Layer(wr, None, np.array([[[0.0, 0.25], [0.0, 0.25]]], f32),
                       np.array([[[1.0 / 64.0, 0.0], [0.0, 7.0 / 256.0]]], f32), wd, 1)
     x2 = np.array([small, 256.0], f32)
@@ -216,3 +208,13 @@ def test_act_fp8_constructed_rounding_order():
     assert list(h2) == [1.125, 448.0] and list(out2) == [1.125, 448.0]
     _, h2raw = L2.expert_ffn(0, x2, want_h=True)
     assert list(h2raw) == [small, 448.0]
+    # 3) the row scale comes from the whole row: x = [1.25 * 2^-9, 512] has
+    #    scale 2 (512 > 448), so x_0 / 2 = 0.625 subnormal steps of 2^-9
+    #    rounds to one step: xq_0 = 2^-9 * 2 = 2^-8 (at scale 1 it would be
+    #    1.25 steps -> 2^-9). g = x_1 / 8 = 64, u_0 = x_0 / 64, u_1 = 7/512 *
+    #    x_1 = 7, so h = [xq_0, 448].
+    x3 = np.array([1.25 * 2.0 ** -9, 512.0], f32)
+    L3 = oracle.Layer(wr, None, np.array([[[0.0, 0.125], [0.0, 0.125]]], f32),
+                      np.array([[[1.0 / 64.0, 0.0], [0.0, 7.0 / 512.0]]], f32), wd, 1)
+    out3, h3 = L3.expert_ffn(0, x3, want_h=True, act_fp8=True)
+    assert list(h3) == [2.0 ** -8, 448.0] and list(out3) == [2.0 ** -8, 448.0], list(h3)

@@ -53,14 +53,13 @@
  * bytes of the bf16 layer.
  *
  * 8-bit activations (COLIBRI_MOE_FLAG_FP8_ACTIVATIONS, on top of FP8_WEIGHTS):
- * the roadmap's FP8 read as FP8 matrix products. Each expert GEMM input row is
- * quantized by the same rule (E4M3, one power-of-two scale per row): the token
- * row x[t] before the gate/up GEMM (the router still sees the full x), and
- * each assignment's h row, after it is stored as bf16, before the down GEMM.
- * Both GEMMs then multiply E4M3 by E4M3 on gfx950's fp8 MFMA
+ * the roadmap's FP8 read as an FP8 matrix product for the first expert GEMM.
+ * Each token row x[t] is quantized by the same rule (E4M3, one power-of-two
+ * scale per row; the router still sees the full x), and the gate/up GEMM
+ * multiplies E4M3 by E4M3 on gfx950's fp8 MFMA
  * (v_mfma_scale_f32_32x32x64_f8f6f4, the scales applied as E8M0 exponents),
- * exact products summed in fp32. With stage timing, stage 1 includes the x
- * quantization and stage 3 the h quantization.
+ * exact products summed in fp32. h stays bf16 and the down GEMM is the 8-bit
+ * weight one. With stage timing, stage 1 includes the x quantization.
  */
 #ifndef COLIBRI_MOE_H
 #define COLIBRI_MOE_H
@@ -80,7 +79,8 @@ typedef enum {
                                          2*d_ff*d_model reaching 2^31, FP8_WEIGHTS with
                                          dtype F32, FP8_ACTIVATIONS without FP8_WEIGHTS
                                          or with d_model or d_ff below 256 */
-    COLIBRI_MOE_ERR_ALIGNMENT = 3,    /* a tensor pointer not 16-byte aligned */
+    COLIBRI_MOE_ERR_ALIGNMENT = 3,    /* x, y, a weight or topk_ids not 16-byte aligned, another
+                                         routing buffer or b_router not 4-byte aligned */
     COLIBRI_MOE_ERR_OUT_OF_MEMORY = 4,/* init could not allocate its memory */
     COLIBRI_MOE_ERR_HIP = 5           /* a HIP launch, copy or sync failed */
 } colibri_moe_status_t;
@@ -93,7 +93,7 @@ enum {
     COLIBRI_MOE_FLAG_FP8_WEIGHTS = 1u << 2,  /* bf16 only: keep expert weights as 8-bit codes
                                                 (format above) */
     COLIBRI_MOE_FLAG_FP8_ACTIVATIONS = 1u << 3 /* with FP8_WEIGHTS, d_model and d_ff >= 256:
-                                                  8-bit expert GEMM inputs, fp8 MFMAs (above) */
+                                                  8-bit token rows, fp8 MFMA gate/up GEMM (above) */
 };
 
 typedef struct {
@@ -120,7 +120,8 @@ typedef struct {
  * assignment a = t * k + j is slot j of token t. */
 typedef struct {
     float* logits;          /* [T][E] fp32 router logits (bias included) */
-    int32_t* topk_ids;      /* [T][k] selected experts, slot 0 = largest logit */
+    int32_t* topk_ids;      /* [T][k] selected experts, slot 0 = largest logit; 16-byte aligned
+                               (the other fields: 4-byte aligned), else ERR_ALIGNMENT */
     float* topk_w;          /* [T][k] routing weights, sum to 1 per token */
     int32_t* expert_counts; /* [E] assignments per expert */
     int32_t* expert_offsets;/* [E+1] exclusive prefix sum of counts */

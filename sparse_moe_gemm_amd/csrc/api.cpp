@@ -31,6 +31,24 @@ const char* const kStageNames[kStages] = {"router",         "dispatch",  "gate_u
 
 }  // namespace
 
+// Per-call working memory of a forward, for A = T*k assignments: routing
+// buffers the caller did not supply, H, the fp32 partial sums, and the 8-bit
+// token rows of the W8A8 mode.
+struct Workspace {
+    uint8_t* xq;  // q8: token rows as E4M3 codes [T][d]
+    float* xsc;   // q8: their scales by sorted position [A]
+    float* topw;
+    int32_t* ids;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* perm;
+    int32_t* perm_slot;
+    int32_t* inv;
+    void* H;      // [A][f] dtype
+    float* Ys;    // down GEMM output: kMaxSplit (bf16) or 1 (f32) partials of [A][d] fp32; on the
+                  // small-batch path first the gate/up slice partials
+};
+
 struct colibri_moe {
     uint32_t magic;
     colibri_moe_config_t cfg;
@@ -48,21 +66,8 @@ struct colibri_moe {
     float* s_gu;  // fp8 row scales [E][2f] (interleaved rows), else null
     float* s_d;   // fp8 row scales [E][d], else null
     bool fp8;
-    bool q8;      // 8-bit activations too (fp8 MFMA)
-    uint8_t* xq;  // q8: token rows as E4M3 codes [max_tokens][d]
-    float* xsc;   // q8: their scales by sorted position [A]
-    uint8_t* hq;  // q8: h rows as E4M3 codes [A][f]
-    float* hsc;   // q8: their scales [A]
-    // workspace, sized for max_tokens
-    float* topw;
-    int32_t* ids;
-    int32_t* counts;
-    int32_t* offsets;
-    int32_t* perm;
-    int32_t* perm_slot;
-    int32_t* inv;
-    void* H;      // [A][f] dtype
-    float* Ys;    // down GEMM output: kMaxSplit (bf16) or 1 (f32) partials of [A][d] fp32
+    bool q8;      // 8-bit token rows for the gate/up GEMM too (fp8 MFMA)
+    Workspace ws; // in the arena, sized for max_tokens
     int32_t* ccnt;  // fused combine: arrivals per token and 128-column tile [max_tokens][d/128], zero between calls
     bool timing;
     hipEvent_t ev[kStages + 1];
@@ -162,25 +167,18 @@ void release(colibri_moe* h)
     delete h;
 }
 
-colibri_moe_status_t init_impl(colibri_moe* h, const colibri_moe_weights_t* w)
+// Layout of the working memory of a call with T tokens (up_to: of every call
+// with at most T tokens), carved from `base` (nullptr: sizes only). Returns the
+// bytes it spans.
+size_t layout_workspace(const colibri_moe* h, int64_t T, bool up_to, uint8_t* base, Workspace* ws)
 {
     const colibri_moe_config_t& c = h->cfg;
     const size_t es = (size_t)h->esize;
     const size_t d = c.d_model, f = c.d_ff, E = c.n_experts, k = c.top_k;
-    const size_t A = (size_t)c.max_tokens * k;
-
+    const size_t A = (size_t)T * k;
     Carver cv;
-    const size_t o_wrt = cv.take(E * d * es);
-    const size_t o_br = cv.take(E * sizeof(float));
-    const size_t wes = h->fp8 ? 1 : es;  // bytes per stored expert weight
-    const size_t o_wgu = cv.take(E * 2 * f * d * wes);
-    const size_t o_wd = cv.take(E * d * f * wes);
-    const size_t o_sgu = h->fp8 ? cv.take(E * 2 * f * sizeof(float)) : 0;
-    const size_t o_sd = h->fp8 ? cv.take(E * d * sizeof(float)) : 0;
-    const size_t o_xq = h->q8 ? cv.take((size_t)c.max_tokens * d) : 0;
+    const size_t o_xq = h->q8 ? cv.take((size_t)T * d) : 0;
     const size_t o_xsc = h->q8 ? cv.take(A * sizeof(float)) : 0;
-    const size_t o_hq = h->q8 ? cv.take(A * f) : 0;
-    const size_t o_hsc = h->q8 ? cv.take(A * sizeof(float)) : 0;
     const size_t o_topw = cv.take(A * sizeof(float));
     const size_t o_ids = cv.take(A * sizeof(int32_t));
     const size_t o_cnt = cv.take(E * sizeof(int32_t));
@@ -192,13 +190,45 @@ colibri_moe_status_t init_impl(colibri_moe* h, const colibri_moe_weights_t* w)
     // Ys: the down GEMM's partial sums (kMaxSplit for bf16), and on the
     // small-batch path also the gate/up slice partials before SiLU.
     size_t ys_floats = (c.dtype == COLIBRI_MOE_BF16 ? (size_t)cmoe::kMaxSplit : 1) * A * d;
-    if (c.dtype == COLIBRI_MOE_BF16 && h->dec_max_a > 0) {
-        const size_t ad = (size_t)h->dec_max_a;
+    // (a call takes the small-batch path when A <= dec_max_a)
+    if (c.dtype == COLIBRI_MOE_BF16 && h->dec_max_a > 0 && (up_to || A <= (size_t)h->dec_max_a)) {
+        const size_t ad = std::min(A, (size_t)h->dec_max_a);
         ys_floats = std::max(ys_floats, (size_t)h->dec_split_gu * ad * 2 * f);
         ys_floats = std::max(ys_floats, (size_t)h->dec_split_dn * ad * d);
     }
     const size_t o_ys = cv.take(ys_floats * sizeof(float));
+    if (base && ws) {
+        ws->xq = h->q8 ? base + o_xq : nullptr;
+        ws->xsc = h->q8 ? (float*)(base + o_xsc) : nullptr;
+        ws->topw = (float*)(base + o_topw);
+        ws->ids = (int32_t*)(base + o_ids);
+        ws->counts = (int32_t*)(base + o_cnt);
+        ws->offsets = (int32_t*)(base + o_off);
+        ws->perm = (int32_t*)(base + o_perm);
+        ws->perm_slot = (int32_t*)(base + o_ps);
+        ws->inv = (int32_t*)(base + o_inv);
+        ws->H = base + o_h;
+        ws->Ys = (float*)(base + o_ys);
+    }
+    return cv.off;
+}
+
+colibri_moe_status_t init_impl(colibri_moe* h, const colibri_moe_weights_t* w)
+{
+    const colibri_moe_config_t& c = h->cfg;
+    const size_t es = (size_t)h->esize;
+    const size_t d = c.d_model, f = c.d_ff, E = c.n_experts;
+
+    Carver cv;
+    const size_t o_wrt = cv.take(E * d * es);
+    const size_t o_br = cv.take(E * sizeof(float));
+    const size_t wes = h->fp8 ? 1 : es;  // bytes per stored expert weight
+    const size_t o_wgu = cv.take(E * 2 * f * d * wes);
+    const size_t o_wd = cv.take(E * d * f * wes);
+    const size_t o_sgu = h->fp8 ? cv.take(E * 2 * f * sizeof(float)) : 0;
+    const size_t o_sd = h->fp8 ? cv.take(E * d * sizeof(float)) : 0;
     const size_t o_ccnt = h->fuse_combine ? cv.take((size_t)c.max_tokens * (d / 128) * sizeof(int32_t)) : 0;
+    const size_t o_ws = cv.take(layout_workspace(h, c.max_tokens, true, nullptr, nullptr));
     h->arena_bytes = cv.off;
 
     if (hipMalloc(&h->arena, h->arena_bytes) != hipSuccess) {
@@ -213,20 +243,8 @@ colibri_moe_status_t init_impl(colibri_moe* h, const colibri_moe_weights_t* w)
     h->w_d = base + o_wd;
     h->s_gu = h->fp8 ? (float*)(base + o_sgu) : nullptr;
     h->s_d = h->fp8 ? (float*)(base + o_sd) : nullptr;
-    h->xq = h->q8 ? base + o_xq : nullptr;
-    h->xsc = h->q8 ? (float*)(base + o_xsc) : nullptr;
-    h->hq = h->q8 ? base + o_hq : nullptr;
-    h->hsc = h->q8 ? (float*)(base + o_hsc) : nullptr;
-    h->topw = (float*)(base + o_topw);
-    h->ids = (int32_t*)(base + o_ids);
-    h->counts = (int32_t*)(base + o_cnt);
-    h->offsets = (int32_t*)(base + o_off);
-    h->perm = (int32_t*)(base + o_perm);
-    h->perm_slot = (int32_t*)(base + o_ps);
-    h->inv = (int32_t*)(base + o_inv);
-    h->H = base + o_h;
-    h->Ys = (float*)(base + o_ys);
     h->ccnt = h->fuse_combine ? (int32_t*)(base + o_ccnt) : nullptr;
+    layout_workspace(h, c.max_tokens, true, base + o_ws, &h->ws);
 
     hipStream_t s = h->stream;
     if (h->ccnt)
@@ -321,9 +339,12 @@ colibri_moe_status_t colibri_moe_init(colibri_moe_t** out, const colibri_moe_con
         const int64_t amax = (int64_t)cfg->max_tokens * cfg->top_k;
         h->dec_max_a = (int)std::min<int64_t>(amax, env_int("CMOE_DECODE_MAX_A", 256, 0, 1 << 16));
         const int waves = cmoe::decode_waves(h->cus);
-        const int kstep = h->q8 ? 64 : h->fp8 ? 32 : 16;
-        h->dec_split_gu = cmoe::decode_split(cfg->n_experts, 2 * cfg->d_ff, cfg->d_model, kstep, waves, 64);
-        h->dec_split_dn = cmoe::decode_split(cfg->n_experts, cfg->d_model, cfg->d_ff, kstep, waves, 64);
+        // k step of the small-batch kernels: 16 (bf16 weights), 32 (8-bit
+        // weights), 64 (8-bit token rows, gate/up only)
+        const int kstep_dn = h->fp8 ? 32 : 16;
+        const int kstep_gu = h->q8 ? 64 : kstep_dn;
+        h->dec_split_gu = cmoe::decode_split(cfg->n_experts, 2 * cfg->d_ff, cfg->d_model, kstep_gu, waves, 64);
+        h->dec_split_dn = cmoe::decode_split(cfg->n_experts, cfg->d_model, cfg->d_ff, kstep_dn, waves, 64);
     }
     st = init_impl(h, w);
     if (st != COLIBRI_MOE_OK) {
@@ -338,37 +359,25 @@ colibri_moe_status_t colibri_moe_init(colibri_moe_t** out, const colibri_moe_con
     return COLIBRI_MOE_OK;
 }
 
-colibri_moe_status_t colibri_moe_forward(colibri_moe_t* h, const void* x, int32_t T, void* y,
-                                         const colibri_moe_routing_t* r)
+}  // extern "C"
+
+namespace {
+
+// The enqueued work of one forward (T >= 1, arguments checked by
+// check_call) with its working memory in ws; fused: the combine runs in the
+// down GEMM's epilogue (handle arena only: its counters must be zero).
+colibri_moe_status_t forward_impl(colibri_moe* h, const void* x, int32_t T, void* y,
+                                  const colibri_moe_routing_t& ro, const Workspace& ws, bool fused_ok)
 {
-    if (!h || !is_live(h) || h->magic != kMagic)
-        return COLIBRI_MOE_ERR_INVALID_ARG;
     const colibri_moe_config_t& c = h->cfg;
-    if (T < 0 || T > c.max_tokens)
-        return COLIBRI_MOE_ERR_INVALID_ARG;
-    if (T == 0)
-        return COLIBRI_MOE_OK;
-    if (!x || !y)
-        return COLIBRI_MOE_ERR_INVALID_ARG;
-    if (!aligned16(x) || !aligned16(y))
-        return COLIBRI_MOE_ERR_ALIGNMENT;
-
-    colibri_moe_routing_t ro = {};
-    if (r)
-        ro = *r;
     // Caller-provided routing buffers double as the working buffers (no copy).
-    float* topw = ro.topk_w ? ro.topk_w : h->topw;
-    int32_t* ids = ro.topk_ids ? ro.topk_ids : h->ids;
-    int32_t* counts = ro.expert_counts ? ro.expert_counts : h->counts;
-    int32_t* offsets = ro.expert_offsets ? ro.expert_offsets : h->offsets;
-    int32_t* perm = ro.perm ? ro.perm : h->perm;
-    int32_t* perm_slot = ro.perm_slot ? ro.perm_slot : h->perm_slot;
-    int32_t* inv = ro.inv ? ro.inv : h->inv;
-    if (((uintptr_t)ids & 15u) || ((uintptr_t)topw & 3u) || ((uintptr_t)counts & 3u) ||
-        ((uintptr_t)offsets & 3u) || ((uintptr_t)perm & 3u) || ((uintptr_t)perm_slot & 3u) ||
-        ((uintptr_t)inv & 3u) || ((uintptr_t)ro.logits & 3u))
-        return COLIBRI_MOE_ERR_ALIGNMENT;
-
+    float* topw = ro.topk_w ? ro.topk_w : ws.topw;
+    int32_t* ids = ro.topk_ids ? ro.topk_ids : ws.ids;
+    int32_t* counts = ro.expert_counts ? ro.expert_counts : ws.counts;
+    int32_t* offsets = ro.expert_offsets ? ro.expert_offsets : ws.offsets;
+    int32_t* perm = ro.perm ? ro.perm : ws.perm;
+    int32_t* perm_slot = ro.perm_slot ? ro.perm_slot : ws.perm_slot;
+    int32_t* inv = ro.inv ? ro.inv : ws.inv;
     const bool bf = c.dtype == COLIBRI_MOE_BF16;
     hipStream_t s = h->stream;
     const bool tm = h->timing;
@@ -384,7 +393,7 @@ colibri_moe_status_t colibri_moe_forward(colibri_moe_t* h, const void* x, int32_
     CMOE_HIP(launch_dispatch(da, s));
     const bool q8 = h->q8;
     if (q8)  // token rows to 8 bits, scales by sorted position
-        CMOE_HIP(launch_act_quant(x, T, c.d_model, c.top_k, inv, h->xq, h->xsc, s));
+        CMOE_HIP(launch_act_quant(x, T, c.d_model, c.top_k, inv, ws.xq, ws.xsc, s));
     if (tm)
         CMOE_HIP(hipEventRecord(h->ev[2], s));
 
@@ -394,34 +403,30 @@ colibri_moe_status_t colibri_moe_forward(colibri_moe_t* h, const void* x, int32_
     if (bf && A <= h->dec_max_a) {
         // small-batch path: weight streaming with K slices, then the slice sum
         // and SiLU(g)*u
-        DecodeArgs gu{q8 ? (const void*)h->xq : x, h->w_gu, h->s_gu, q8 ? h->xsc : nullptr, h->Ys, offsets, perm,
+        DecodeArgs gu{q8 ? (const void*)ws.xq : x, h->w_gu, h->s_gu, q8 ? ws.xsc : nullptr, ws.Ys, offsets, perm,
                       A, c.n_experts, c.d_model, c.d_ff, h->dec_split_gu};
         CMOE_HIP(launch_decode_gemm(gu, 1, h->cus, s));
         if (tm)
             CMOE_HIP(hipEventRecord(h->ev[3], s));
-        CMOE_HIP(launch_decode_silu(h->Ys, h->H, A, c.d_ff, h->dec_split_gu, s));
-        if (q8)
-            CMOE_HIP(launch_act_quant(h->H, A, c.d_ff, 0, nullptr, h->hq, h->hsc, s));
+        CMOE_HIP(launch_decode_silu(ws.Ys, ws.H, A, c.d_ff, h->dec_split_gu, s));
         if (tm)
             CMOE_HIP(hipEventRecord(h->ev[4], s));
-        DecodeArgs dn{q8 ? (const void*)h->hq : h->H, h->w_d, h->s_d, q8 ? h->hsc : nullptr, h->Ys, offsets, perm,
+        DecodeArgs dn{ws.H, h->w_d, h->s_d, nullptr, ws.Ys, offsets, perm,
                       A, c.n_experts, c.d_model, c.d_ff, h->dec_split_dn};
         CMOE_HIP(launch_decode_gemm(dn, 0, h->cus, s));
         split = h->dec_split_dn;
     } else {
-        GemmArgs gu{q8 ? (const void*)h->xq : x, h->w_gu, h->s_gu, q8 ? h->xsc : nullptr, h->H, offsets, perm, A,
+        GemmArgs gu{q8 ? (const void*)ws.xq : x, h->w_gu, h->s_gu, q8 ? ws.xsc : nullptr, ws.H, offsets, perm, A,
                     c.n_experts, c.top_k, c.d_model, c.d_ff, h->group_n_gu, 1, h->cus};
         CMOE_HIP(bf ? launch_gate_up_bf16(gu, s) : launch_gate_up_f32(gu, s));
-        if (tm)
+        if (tm) {
             CMOE_HIP(hipEventRecord(h->ev[3], s));
-        if (q8)  // h rows to 8 bits (the only reduce step on this path)
-            CMOE_HIP(launch_act_quant(h->H, A, c.d_ff, 0, nullptr, h->hq, h->hsc, s));
-        if (tm)
             CMOE_HIP(hipEventRecord(h->ev[4], s));
-        split = bf ? down_split_bf16(A, c.n_experts, c.d_model, c.d_ff, h->cus, q8 ? 1 : 0) : 1;
-        GemmArgs dn{q8 ? (const void*)h->hq : h->H, h->w_d, h->s_d, q8 ? h->hsc : nullptr, h->Ys, offsets, perm, A,
+        }
+        split = bf ? down_split_bf16(A, c.n_experts, c.d_model, c.d_ff, h->cus, 0) : 1;
+        GemmArgs dn{ws.H, h->w_d, h->s_d, nullptr, ws.Ys, offsets, perm, A,
                     c.n_experts, c.top_k, c.d_model, c.d_ff, h->group_n_dn, split, h->cus};
-        if (bf && h->ccnt) {
+        if (bf && h->ccnt && fused_ok) {
             dn.cnt = h->ccnt;
             dn.inv = inv;
             dn.topw = topw;
@@ -434,7 +439,7 @@ colibri_moe_status_t colibri_moe_forward(colibri_moe_t* h, const void* x, int32_
         CMOE_HIP(hipEventRecord(h->ev[5], s));
 
     if (!fused) {
-        CombineArgs ca{h->Ys, inv, topw, y, T, c.top_k, c.d_model, split, bf ? 1 : 0};
+        CombineArgs ca{ws.Ys, inv, topw, y, T, c.top_k, c.d_model, split, bf ? 1 : 0};
         CMOE_HIP(launch_combine(ca, s));
     }
     if (tm)
@@ -443,6 +448,51 @@ colibri_moe_status_t colibri_moe_forward(colibri_moe_t* h, const void* x, int32_
     if (!(c.flags & COLIBRI_MOE_FLAG_ASYNC))
         CMOE_HIP(hipStreamSynchronize(s));
     return COLIBRI_MOE_OK;
+}
+
+// Argument checks shared by both forward entry points. Returns OK with
+// *skip set for T = 0 (nothing to do).
+colibri_moe_status_t check_call(colibri_moe* h, const void* x, int32_t T, void* y,
+                                const colibri_moe_routing_t* r, colibri_moe_routing_t* ro, bool* skip)
+{
+    *skip = false;
+    if (!h || !is_live(h) || h->magic != kMagic)
+        return COLIBRI_MOE_ERR_INVALID_ARG;
+    if (T < 0 || T > h->cfg.max_tokens)
+        return COLIBRI_MOE_ERR_INVALID_ARG;
+    if (T == 0) {
+        *skip = true;
+        return COLIBRI_MOE_OK;
+    }
+    if (!x || !y)
+        return COLIBRI_MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(y))
+        return COLIBRI_MOE_ERR_ALIGNMENT;
+    *ro = colibri_moe_routing_t{};
+    if (r)
+        *ro = *r;
+    // topk_ids is read as whole 16-byte rows by the dispatch kernel; the
+    // other routing buffers hold 4-byte elements.
+    if (((uintptr_t)ro->topk_ids & 15u) || ((uintptr_t)ro->topk_w & 3u) || ((uintptr_t)ro->expert_counts & 3u) ||
+        ((uintptr_t)ro->expert_offsets & 3u) || ((uintptr_t)ro->perm & 3u) || ((uintptr_t)ro->perm_slot & 3u) ||
+        ((uintptr_t)ro->inv & 3u) || ((uintptr_t)ro->logits & 3u))
+        return COLIBRI_MOE_ERR_ALIGNMENT;
+    return COLIBRI_MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+colibri_moe_status_t colibri_moe_forward(colibri_moe_t* h, const void* x, int32_t T, void* y,
+                                         const colibri_moe_routing_t* r)
+{
+    colibri_moe_routing_t ro;
+    bool skip;
+    const colibri_moe_status_t st = check_call(h, x, T, y, r, &ro, &skip);
+    if (st != COLIBRI_MOE_OK || skip)
+        return st;
+    return forward_impl(h, x, T, y, ro, h->ws, true);
 }
 
 colibri_moe_status_t colibri_moe_free(colibri_moe_t* h)
@@ -484,7 +534,7 @@ const char* colibri_moe_status_string(colibri_moe_status_t s)
     case COLIBRI_MOE_ERR_UNSUPPORTED:
         return "unsupported configuration";
     case COLIBRI_MOE_ERR_ALIGNMENT:
-        return "pointer not 16-byte aligned";
+        return "pointer not aligned (16 bytes for x, y, weights and topk_ids; 4 for the other routing buffers)";
     case COLIBRI_MOE_ERR_OUT_OF_MEMORY:
         return "out of device memory";
     case COLIBRI_MOE_ERR_HIP:

@@ -414,11 +414,10 @@ int decode_split(int E, int N, int K, int kstep, int waves, int max_split)
 
 hipError_t launch_decode_gemm(const DecodeArgs& a, int gate_up, int cus, hipStream_t s)
 {
-    if (a.a_scales) {
-        if (gate_up)
-            hipLaunchKernelGGL(decode_gemm_q8_kernel<true>, dim3(cus * 2), dim3(kThreads), 0, s, a);
-        else
-            hipLaunchKernelGGL(decode_gemm_q8_kernel<false>, dim3(cus * 2), dim3(kThreads), 0, s, a);
+    if (a.a_scales) {  // 8-bit A rows feed the gate/up GEMM only
+        if (!gate_up)
+            return hipErrorInvalidValue;
+        hipLaunchKernelGGL(decode_gemm_q8_kernel<true>, dim3(cus * 2), dim3(kThreads), 0, s, a);
     } else if (a.scales) {
         if (gate_up)
             hipLaunchKernelGGL(decode_gemm_f8_kernel<true>, dim3(cus * 2), dim3(kThreads), 0, s, a);

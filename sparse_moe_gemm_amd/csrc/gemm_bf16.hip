@@ -33,6 +33,7 @@
 // n-tile; workgroups are spread over the 8 XCDs round robin, so the tiles one
 // XCD runs together share a few token and weight panels in its L2.
 #include "common.hpp"
+#include "tiles.hpp"
 
 namespace cmoe {
 
@@ -132,12 +133,13 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes)
 // these LDS writes against the LDS reads of other stages is handled
 // explicitly (vmcnt waits and barriers), and an opaque instruction keeps the
 // compiler from adding its own full waits before LDS reads, which would drain
-// the stages in flight. Nothing else in these kernels uses M0.
+// the stages in flight. M0 is declared clobbered, so the compiler keeps none of
+// its own values there across the load.
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds)
 {
     asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc),
                  "s"(soff), "s"(lds)
-                 : "memory");
+                 : "memory", "m0");
 }
 
 // Where the loads of one stage come from: the tile's weight panel, the
@@ -519,103 +521,6 @@ __device__ __forceinline__ void stage_q8(const i32x4& ra, const LoadSrc<A_INS>& 
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-}
-
-// Per-lane view of the m-tiles: lane l holds experts 4l .. 4l+3 (E <= 256).
-struct TileTable {
-    int off[4];  // segment start offsets[e]
-    int cnt[4];  // rows of the expert
-    int mpre;    // m-tiles of all experts below 4l
-    int msum;    // m-tiles of this lane's experts
-};
-
-template <int BM>
-__device__ __forceinline__ int make_table(const int32_t* offsets, int E, int lane, TileTable& t)
-{
-    int ms = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int e = lane * 4 + q;
-        const int o0 = e < E ? offsets[e] : 0;
-        const int o1 = e < E ? offsets[e + 1] : 0;
-        t.off[q] = o0;
-        t.cnt[q] = o1 - o0;
-        ms += (o1 - o0 + BM - 1) / BM;
-    }
-    int incl = ms;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int o = __shfl_up(incl, d, kWave);
-        if (lane >= d)
-            incl += o;
-    }
-    t.mpre = incl - ms;
-    t.msum = ms;
-    return __builtin_amdgcn_readfirstlane(__shfl(incl, kWave - 1, kWave));  // total m-tiles (uniform)
-}
-
-struct Tile {
-    int e, m, n, s;
-    int row0, rows;  // first sorted row and valid rows of the m-tile
-    int kt0, nkt;    // K stages of the split
-};
-
-// Tile behind index L (< total). Tiles of one m-tile are consecutive in the
-// global m-tile order, NT * S of them, so L / (NT * S) is the global m-tile
-// index j; the lane whose experts cover j holds the expert.
-template <int BM>
-__device__ __forceinline__ Tile decode(const TileTable& t, int L, int NT, int S, int GN, int KT)
-{
-    const int per_m = NT * S;
-    const int j = L / per_m;
-    const uint64_t hit = __ballot(j >= t.mpre && j < t.mpre + t.msum);
-    const int ln = __builtin_ctzll(hit);
-    int base = __builtin_amdgcn_readlane(t.mpre, ln);
-    int e = 0, Me = 0, cnt = 0, seg0 = 0;
-    bool found = false;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int c = __builtin_amdgcn_readlane(t.cnt[q], ln);
-        const int o = __builtin_amdgcn_readlane(t.off[q], ln);
-        const int me = (c + BM - 1) / BM;
-        if (!found) {
-            if (j < base + me) {
-                found = true;
-                e = ln * 4 + q;
-                Me = me;
-                cnt = c;
-                seg0 = o;
-            } else {
-                base += me;
-            }
-        }
-    }
-    Tile r;
-    const int local = L - base * per_m;
-    r.s = local / (Me * NT);
-    const int rem = local - r.s * Me * NT;
-    const int grp = rem / (Me * GN);
-    const int gn = min(GN, NT - grp * GN);
-    const int idx = rem - grp * Me * GN;
-    r.e = e;
-    r.m = idx / gn;
-    r.n = grp * GN + (idx - r.m * gn);
-    r.row0 = seg0 + r.m * BM;
-    r.rows = min(BM, cnt - r.m * BM);
-    const int per_s = KT / S;
-    r.kt0 = r.s * per_s;
-    r.nkt = (r.s == S - 1) ? KT - r.kt0 : per_s;
-    // The divisions above run on the vector ALU; pin the (uniform) results to
-    // scalar registers so everything derived from them stays scalar.
-    r.e = __builtin_amdgcn_readfirstlane(r.e);
-    r.m = __builtin_amdgcn_readfirstlane(r.m);
-    r.n = __builtin_amdgcn_readfirstlane(r.n);
-    r.s = __builtin_amdgcn_readfirstlane(r.s);
-    r.row0 = __builtin_amdgcn_readfirstlane(r.row0);
-    r.rows = __builtin_amdgcn_readfirstlane(r.rows);
-    r.kt0 = __builtin_amdgcn_readfirstlane(r.kt0);
-    r.nkt = __builtin_amdgcn_readfirstlane(r.nkt);
-    return r;
 }
 
 // The combine, fused into the down GEMM's epilogue: after a tile has stored
@@ -1404,8 +1309,8 @@ hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t s)
 
 hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t s)
 {
-    if (a.a_scales)
-        return launch_grouped<false, false, true>(a, s);
+    if (a.a_scales)  // 8-bit A rows feed the gate/up GEMM only
+        return hipErrorInvalidValue;
     return a.scales ? launch_grouped<false, true, false>(a, s) : launch_grouped<false, false, false>(a, s);
 }
 

@@ -3,10 +3,12 @@
 // Same two GEMMs as gemm_bf16.hip (gate/up with the SiLU(g)*u epilogue, then
 // down), for layers stored in fp32. gfx950's fp32 matrix rate equals its fp32
 // vector rate, so these use plain FMA with LDS tiles: 64x64 output tiles, 256
-// threads, 4x4 outputs per thread, K staged 16 at a time. Tiles are mapped as
-// in the bf16 kernels (derived on the device from offsets[], empty experts get
-// none); the gate/up weights use the same 32-row gate/up interleave.
+// threads, 4x4 outputs per thread, K staged 16 at a time. Each block finds its
+// tile with the bf16 kernels' walker (tiles.hpp: derived on the device from
+// offsets[], empty experts get none); the gate/up weights use the same 32-row
+// gate/up interleave.
 #include "common.hpp"
+#include "tiles.hpp"
 
 namespace cmoe {
 
@@ -14,46 +16,27 @@ namespace {
 
 constexpr int kT = 64, kBK = 16, kThreads = 256;
 
-struct TileF {
-    int e, m, n, valid;
-};
-
-__device__ void find_tile_f32(const int32_t* offsets, int E, int NT, TileF* out)
-{
-    // Serial walk by one thread: these layers are small.
-    int L = blockIdx.x;
-    for (int e = 0; e < E; ++e) {
-        const int c = offsets[e + 1] - offsets[e];
-        const int tiles = ((c + kT - 1) / kT) * NT;
-        if (L < tiles) {
-            *out = TileF{e, L / NT, L % NT, 1};
-            return;
-        }
-        L -= tiles;
-    }
-    out->valid = 0;
-}
-
 template <bool GATE_UP>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_f32_kernel(GemmArgs g)
 {
     __shared__ float sA[kBK][kT + 1];
     __shared__ float sG[kBK][kT + 1];
     __shared__ float sU[kBK][kT + 1];
-    __shared__ TileF s_tile;
 
     const int NOUT = GATE_UP ? g.f : g.d;  // output columns per expert
     const int K = GATE_UP ? g.d : g.f;
     const int NT = NOUT / kT;
-    if (threadIdx.x == 0)
-        find_tile_f32(g.offsets, g.E, NT, &s_tile);
-    __syncthreads();
-    if (!s_tile.valid)
+    // Every wave derives the block's tile from offsets[] (the same walker as
+    // the bf16 GEMMs: one m-tile count per expert, a wave prefix sum, a ballot).
+    TileTable tt;
+    const int total = make_table<kT>(g.offsets, g.E, threadIdx.x % kWave, tt) * NT;
+    if ((int)blockIdx.x >= total)
         return;
-    const int e = s_tile.e;
-    const int row0 = g.offsets[e] + s_tile.m * kT;
-    const int rows = min(kT, g.offsets[e + 1] - row0);
-    const int col0 = s_tile.n * kT;
+    const Tile tl = decode<kT>(tt, blockIdx.x, NT, 1, NT, 1);
+    const int e = tl.e;
+    const int row0 = tl.row0;
+    const int rows = tl.rows;
+    const int col0 = tl.n * kT;
 
     const float* A = (const float*)g.a;
     const float* B = (const float*)g.b;

@@ -12,35 +12,30 @@ oracle, through the C ABI.
   y within a per-token norm-wise error of 2e-2. The quantization itself moves
   y by about 5% on these inputs, so the same comparison against the
   unquantized layer fails: both are checked, on both GEMM paths.
-* 8-bit activations (FLAG_FP8_ACTIVATIONS, fp8 MFMAs): the reference is the
-  oracle's 8-bit activation mode on the dequantized weights, with a tolerance
-  of its own. The fp8 MFMA does not return exact fp32 sums of its exact
-  products: it adds them in groups of 8 k and keeps only about 11 bits below
-  the largest product of a group (measured: 448 + 63 * 2^-6 in one 64-k dot
-  product comes back as 448.875, not 448.984). g and u are therefore off by
-  up to ~1e-3 of their size, and requantizing h turns some of those
-  differences into one-step E4M3 code changes of single h values (a model
-  of the MFMA that truncates each group of 8 products at 11 bits below the
-  group's largest reproduces the GPU's output to bf16 rounding, where the
-  oracle's exact sums differ by up to 4e-2 on single tokens). Measured: mean
-  per-token error ~2.5e-3 on every shape; of 4,000+ tokens, three above 1e-2
-  and the worst at 3.9e-2. Rule: mean over tokens within 5e-3, at most
-  1 + T/200 tokens above 2e-2, every token within 1e-1. Quantizing the
-  activations moves y by about 5% (mean), so the same comparison against the
-  8-bit weight layer without it fails by the mean, and is made too.
+* 8-bit activations (FLAG_FP8_ACTIVATIONS): the token rows enter the gate/up
+  GEMM as E4M3 codes (fp8 MFMA); the down GEMM is the 8-bit weight one. The
+  reference is the oracle's 8-bit activation mode on the dequantized weights
+  under the bf16 rules. The x codes are an exact function of x (the same
+  quantizer as the weights', pinned bit for bit above), so what remains is
+  arithmetic that varies smoothly with its inputs: the fp8 MFMA adds its exact
+  products in groups of 8 k and keeps about 11 bits below a group's largest
+  product (measured: 448 + 63 * 2^-6 in one 64-k dot product comes back as
+  448.875, not 448.984), which puts g and u within ~2^-11 * sqrt(d/8) of the
+  group maxima, below the bf16 rounding of H (2^-9 relative) that the bf16
+  rule already absorbs. Quantizing the token rows moves y by a few percent
+  (mean), so the same comparison against the 8-bit weight layer without it
+  fails by the mean, and is made too.
 """
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from moe_case import compare, make_layer, run_gpu, sample_tokens, to_dev
+from moe_case import compare, make_layer, run_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
 C = synth.LayerConfig
-TOL_Y_Q8 = 1e-1       # every token, 8-bit activations (derivation in the module docstring)
-TOL_Y_Q8_MEAN = 5e-3  # mean over tokens
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -156,24 +151,21 @@ def test_quantize_of_layer_weights_matches_oracle():
         assert np.array_equal(codes, rc) and np.array_equal(scales, rs), name
 
 
-def _layer_case(cfg, inp, tokens_of=None, act_fp8=False):
+def _layer_case(cfg, inp, act_fp8=False):
     import sparse_moe_gemm_amd as cm
 
     flags = cm.FLAG_FP8_WEIGHTS | (cm.FLAG_FP8_ACTIVATIONS if act_fp8 else 0)
     layer = make_layer(cfg, inp, flags=flags)
     g = run_gpu(layer, inp["x"])
     layer.close()
-    toks = None if tokens_of is None else tokens_of(g)
     q = oracle.quantized_expert_weights(inp)
     Lq = oracle.Layer.from_inputs(q, cfg.k)
-    rep = compare(cfg, inp, g, tokens=toks, ref_layer=Lq, act_fp8=act_fp8, tol_y=TOL_Y_Q8 if act_fp8 else None)
-    if act_fp8:
-        assert rep["mean_err"] <= TOL_Y_Q8_MEAN, rep
-        assert rep["over_2e2"] <= 1 + rep["tokens_checked"] // 200, rep
+    rep = compare(cfg, inp, g, ref_layer=Lq, act_fp8=act_fp8)
     # against the layer without the last quantization step the same rule
     # fails: the GPU computed the 8-bit layer, not the bf16 one (weights), or
-    # the 8-bit activation layer, not the 8-bit weight one (activations)
-    t = np.arange(cfg.T) if toks is None else toks
+    # the 8-bit activation layer, not the 8-bit weight one (activations); on
+    # at most 256 tokens (this shows the modes differ; parity is above)
+    t = np.arange(min(cfg.T, 256))
     L0 = Lq if act_fp8 else oracle.Layer.from_inputs(inp, cfg.k)
     y0 = L0.forward(inp["x"], tokens=t, forced_ids=g["topk_ids"])
     den = np.max(np.abs(y0), axis=1)
@@ -215,7 +207,8 @@ def test_fp8_full_size_workload(name):
     cfg = synth.CONFIGS[name]
     print(f"fp8 full-size case {cfg}", flush=True)
     inp = synth.make_inputs(cfg)
-    g, rep = _layer_case(cfg, inp, None if cfg.T <= 64 else (lambda g: sample_tokens(g, cfg.T)))
+    g, rep = _layer_case(cfg, inp)
+    assert rep["tokens_checked"] == cfg.T
     print(name, rep, flush=True)
 
 
@@ -260,7 +253,8 @@ def test_w8a8_full_size_workload(name):
     cfg = synth.CONFIGS[name]
     print(f"w8a8 full-size case {cfg}", flush=True)
     inp = synth.make_inputs(cfg)
-    g, rep = _layer_case(cfg, inp, None if cfg.T <= 64 else (lambda g: sample_tokens(g, cfg.T)), act_fp8=True)
+    g, rep = _layer_case(cfg, inp, act_fp8=True)
+    assert rep["tokens_checked"] == cfg.T
     print(name, rep, flush=True)
 
 

@@ -2,26 +2,33 @@
 
 One step = one full forward of the layer (router, dispatch, gate/up GEMM,
 down GEMM, combine) over one batch of synthetic tokens whose inputs and weights
-are already resident in HBM. Default workload: the Mixtral-8x7B-shaped prefill
-layer (T=4096, d_model=4096, E=8, top-2, d_ff=14336, bf16).
+are already resident in HBM. The headline workload is the Mixtral-8x7B-shaped
+prefill layer (T=4096, d_model=4096, E=8, top-2, d_ff=14336, bf16); by default
+the other four layer shapes (fine-grained 128 experts top-4, decode T=32,
+skewed 64 experts with two hot ones, and the same with 20 masked experts) are
+timed in the same run and reported under "workloads".
 
-Prints one JSON line with the throughput (tokens/s), the roofline position of
-the dominant kernel (measured live with HIP events on the layer's stream), and
-the CPU oracle timed on a bounded sample of the same workload.
+Prints one JSON line: the headline's throughput (tokens/s), the roofline
+position of its dominant kernel (the gate/up GEMM, its average duration
+measured live with the library's HIP events on the layer's stream), the layer's
+MFMA and HBM fractions, one sub-record per workload, and the CPU oracle timed on
+a bounded sample of the headline workload.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--fp8-weights] [--fp8-activations]
-                    [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workloads all|NAME[,NAME...]]
+                    [--fp8-weights] [--fp8-activations] [--no-cpu-baseline]
 
---fp8-weights builds the layer with 8-bit expert weights (E4M3 codes, one
-power-of-two scale per weight row, converted to bf16 in registers): same bf16
-arithmetic, half the expert weight bytes. --fp8-activations (implies
---fp8-weights) also quantizes the expert GEMM inputs per row and runs both
-expert GEMMs on the fp8 MFMA; the roofline peak is then the fp8 one.
+The timed loop runs on a handle without per-stage events; kernel durations come
+from a second handle with COLIBRI_MOE_FLAG_STAGE_TIMING over the same number of
+steps. --fp8-weights builds the layers with 8-bit expert weights (E4M3 codes,
+one power-of-two scale per weight row, converted to bf16 in registers).
+--fp8-activations (implies --fp8-weights) also quantizes the token rows and
+runs the gate/up GEMM on the fp8 MFMA; its roofline peak is then the fp8 one.
 """
 from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -44,7 +51,10 @@ WORKLOAD_NAMES = {
     "skewed": "skewed-64e-top2",
     "skewed-masked": "skewed-64e-top2-20-empty",
     "tiny-f32": "tiny-f32",
+    "dense": "dense-single-expert",
 }
+DEFAULT_WORKLOADS = ("mixtral", "fine-grained", "decode", "skewed", "skewed-masked")
+HEADLINE = "mixtral"
 
 
 def parse():
@@ -52,11 +62,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mixtral", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--workloads", default="all",
+                    help="'all' (the five layer shapes, headline mixtral) or a comma-separated list; "
+                         "the first one listed is the headline")
     ap.add_argument("--fp8-weights", action="store_true",
                     help="8-bit expert weights (bf16 workloads only)")
     ap.add_argument("--fp8-activations", action="store_true",
-                    help="8-bit expert weights and GEMM inputs, fp8 MFMA (bf16 workloads only)")
+                    help="8-bit expert weights and token rows, fp8 MFMA gate/up GEMM (bf16 workloads only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens of the oracle sample (0 = sized to ~15 s of CPU work)")
@@ -105,30 +117,61 @@ def active_weight_bytes(cfg, counts, stage, fp8=False):
     return n_active * per
 
 
-def profiled_traffic(workload: str, kernel: str):
-    """HBM bytes per launch of `kernel` ("gate_up_gemm") from the committed
-    rocprofv3 summary of this workload (FETCH_SIZE and WRITE_SIZE, scaled by a
-    plain copy's readings), or None when that summary is missing, covers another
-    kernel, or was taken on a different version of the kernel's source file."""
-    import hashlib
+def layer_bytes(cfg, counts, fp8=False):
+    """Algorithmic HBM bytes of one forward: the active experts' weights (read
+    once), the router weights and bias, x and y."""
+    es = cfg.elem_bytes()
+    w = active_weight_bytes(cfg, counts, "gate_up_gemm", fp8) + active_weight_bytes(cfg, counts, "down_gemm", fp8)
+    return w + cfg.d * cfg.E * es + cfg.E * 4 + 2 * cfg.T * cfg.d * es
 
+
+def source_digest() -> str:
+    """sha256 over every file of the library's sources (names and contents):
+    a profile taken on other sources says nothing about these kernels."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_moe_gemm_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        h.update(fn.encode())
+        h.update(open(os.path.join(csrc, fn), "rb").read())
+    return h.hexdigest()
+
+
+def profile_fields(workload: str, kernel: str) -> dict:
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_rocprof.md")
     if not os.path.exists(path):
-        return None
+        return {}
     fields = {}
     for line in open(path):
         if ":" in line and not line.startswith("|"):
             key, _, val = line.partition(":")
             fields[key.strip()] = val.strip()
-    for key, val in fields.items():
-        if key.startswith("source_sha256(") and key.endswith(")"):
-            src = os.path.join(ROOT, key[len("source_sha256("):-1])
-            if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != val:
-                return None
+    return fields
+
+
+def profiled_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` ("gate_up_gemm") from the committed
+    rocprofv3 summary of this workload (FETCH_SIZE and WRITE_SIZE, scaled by a
+    plain copy's readings), or None when that summary is missing or was taken
+    on library sources other than the current ones (sha256 of the whole csrc
+    directory, which also covers launch decisions such as tile order and K
+    splits)."""
+    fields = profile_fields(workload, kernel)
+    if fields.get("csrc_sha256") != source_digest():
+        return None
     try:
         return float(fields["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.partition(":")[2].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(cfg, inp, sample_tokens: int, fp8: bool = False, q8: bool = False):
@@ -158,8 +201,111 @@ def cpu_baseline(cfg, inp, sample_tokens: int, fp8: bool = False, q8: bool = Fal
     what = f"first {sample_tokens} tokens of the workload" if reps == 1 else \
         f"all {sample_tokens} tokens of the workload, {reps} times"
     return {"value": reps * sample_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{what} (router, top-k and their {cfg.k} experts' SwiGLU FFN + combine in double), "
                       f"wall {dt:.2f} s"}
+
+
+def run_workload(name: str, args, fp8: bool, q8: bool) -> dict:
+    """Time one workload: K forwards on a handle without stage events (the
+    step time), then K more on a handle with them (per-kernel durations)."""
+    import torch
+
+    import synth
+    import sparse_moe_gemm_amd as cm
+
+    cfg = synth.CONFIGS[name]
+    if fp8 and cfg.dtype != "bf16":
+        raise SystemExit("--fp8-weights / --fp8-activations need bf16 workloads")
+    t_gen = time.perf_counter()
+    inp = synth.make_inputs(cfg)
+    t_gen = time.perf_counter() - t_gen
+    wts = [to_dev(inp[n]) for n in ("w_router", "b_router", "w_gate", "w_up", "w_down")]
+    flags = (cm.FLAG_FP8_WEIGHTS if fp8 else 0) | (cm.FLAG_FP8_ACTIVATIONS if q8 else 0)
+    x = to_dev(inp["x"])
+    y = torch.empty_like(x)
+
+    # 1) step time: K back-to-back forwards, HIP events on the layer's stream
+    layer = cm.MoELayer(*wts, cfg.k, max_tokens=cfg.T, flags=cm.FLAG_ASYNC | flags)
+    rt = layer.routing_buffers(cfg.T)
+    keep = {"expert_counts": rt["expert_counts"]}
+    stream = layer.stream
+    for _ in range(args.warmup):
+        layer.forward(x, y, keep)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    t_wall = time.perf_counter()
+    for _ in range(args.steps):
+        layer.forward(x, y, keep)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    counts = keep["expert_counts"].cpu().numpy()
+    layer.close()
+
+    # 2) per-kernel durations: the library's per-stage events (recorded on
+    # the same stream as the kernels), averaged over K forwards
+    layer = cm.MoELayer(*wts, cfg.k, max_tokens=cfg.T, flags=cm.FLAG_ASYNC | cm.FLAG_STAGE_TIMING | flags)
+    for _ in range(max(1, args.warmup // 2)):
+        layer.forward(x, y)
+    stage_sum = {s: 0.0 for s in cm.STAGES}
+    for _ in range(args.steps):
+        layer.forward(x, y)
+        for s, v in layer.stage_times().items():
+            stage_sum[s] += v
+    stage_ms = {s: v / args.steps for s, v in stage_sum.items()}
+    layer.close()
+    del wts, x, y
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    A = cfg.T * cfg.k
+    t = ms_per_step * 1e-3
+    peak_mm = PEAK_FP8_TFLOPS if q8 else PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
+    layer_tflops = cfg.flops() / t / 1e12
+    layer_gbs = layer_bytes(cfg, counts, fp8) / t / 1e9
+    # The library takes its small-batch (weight streaming) path for bf16 calls
+    # with at most CMOE_DECODE_MAX_A (default 256) assignments: HBM-bound.
+    small_batch = cfg.dtype == "bf16" and A <= int(os.environ.get("CMOE_DECODE_MAX_A", "256"))
+    dom = "gate_up_gemm"  # carries 2/3 of the flops and of the weight bytes
+    prof_key = name + ("-w8a8" if q8 else "-fp8" if fp8 else "")
+    traffic = profiled_traffic(prof_key, dom)
+    if small_batch:
+        achieved = active_weight_bytes(cfg, counts, dom, fp8) / (stage_ms[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                "kernel": ("decode_gemm_q8_kernel<true>" if q8 else "decode_gemm_f8_kernel<true>" if fp8
+                           else "decode_gemm_kernel<true>") + " (gate/up)"}
+    else:
+        achieved = gemm_flops_per_assignment(cfg)[dom] * A / (stage_ms[dom] * 1e-3) / 1e12
+        gu_peak = PEAK_FP8_TFLOPS if q8 else peak_mm
+        roof = {"bound": "mfma", "achieved": achieved, "peak": gu_peak, "unit": "TFLOP/s",
+                "frac": achieved / gu_peak, "traffic": traffic,
+                "kernel": "grouped_gemm_kernel (gate/up" + (", fp8 MFMA" if q8 else "") + ")"}
+    return {
+        "cfg": cfg,
+        "inp": inp,
+        "record": {
+            "workload": WORKLOAD_NAMES[name] + ("-w8a8" if q8 else "-fp8-weights" if fp8 else ""),
+            "T": cfg.T, "d_model": cfg.d, "n_experts": cfg.E, "top_k": cfg.k, "d_ff": cfg.f,
+            "ms_per_step": ms_per_step,
+            "tokens_per_s": cfg.T / t,
+            "bound": "hbm" if small_batch else "mfma",
+            "layer_tflops": layer_tflops,
+            "layer_mfma_frac": layer_tflops / peak_mm,
+            "layer_gbs": layer_gbs,
+            "layer_hbm_frac": layer_gbs / PEAK_HBM_GBS,
+            "kernel_roofline": roof,
+            "stage_ms": stage_ms,
+            "empty_experts": int((counts == 0).sum()),
+            "active_experts": int((counts > 0).sum()),
+            "wall_s_timed": t_wall,
+            "input_gen_s": t_gen,
+        },
+    }
 
 
 def main():
@@ -169,120 +315,59 @@ def main():
               "(--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
 
-    import torch
+    import torch  # noqa: F401
 
-    import synth
-    import sparse_moe_gemm_amd as cm
+    import synth  # noqa: F401
+    import sparse_moe_gemm_amd  # noqa: F401  (fails loudly without the built library)
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
-    cfg = synth.CONFIGS[args.workload]
+    names = list(DEFAULT_WORKLOADS) if args.workloads == "all" else args.workloads.split(",")
+    for n in names:
+        if n not in WORKLOAD_NAMES:
+            raise SystemExit(f"unknown workload {n}; known: {', '.join(WORKLOAD_NAMES)}")
     q8 = bool(args.fp8_activations)
     fp8 = bool(args.fp8_weights) or q8
-    if fp8 and cfg.dtype != "bf16":
-        print("--fp8-weights / --fp8-activations need a bf16 workload", file=sys.stderr)
-        sys.exit(2)
-    t_gen = time.perf_counter()
-    inp = synth.make_inputs(cfg)
-    t_gen = time.perf_counter() - t_gen
 
-    layer = cm.MoELayer(to_dev(inp["w_router"]), to_dev(inp["b_router"]), to_dev(inp["w_gate"]),
-                        to_dev(inp["w_up"]), to_dev(inp["w_down"]), cfg.k, max_tokens=cfg.T,
-                        flags=cm.FLAG_ASYNC | cm.FLAG_STAGE_TIMING | (cm.FLAG_FP8_WEIGHTS if fp8 else 0)
-                        | (cm.FLAG_FP8_ACTIVATIONS if q8 else 0))
-    torch.cuda.synchronize()
-    torch.cuda.empty_cache()
-    x = to_dev(inp["x"])
-    y = torch.empty_like(x)
-    rt = layer.routing_buffers(cfg.T)
-    keep = {"expert_counts": rt["expert_counts"]}
-    stream = layer.stream
-
-    for _ in range(args.warmup):
-        layer.forward(x, y, keep)
-    torch.cuda.synchronize()
-
-    # Timed region: K back-to-back forwards, events on the layer's stream.
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    t_wall = time.perf_counter()
-    for _ in range(args.steps):
-        layer.forward(x, y, keep)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms_total = ev0.elapsed_time(ev1)
-    ms_per_step = ms_total / args.steps
-
-    # Per-kernel durations: the same K forwards again, reading the library's
-    # per-stage HIP events (recorded on the same stream) after each one.
-    stage_sum = {s: 0.0 for s in cm.STAGES}
-    for _ in range(args.steps):
-        layer.forward(x, y, keep)
-        for s, v in layer.stage_times().items():
-            stage_sum[s] += v
-    stage_ms = {s: v / args.steps for s, v in stage_sum.items()}
-    counts = keep["expert_counts"].cpu().numpy()
-    layer.close()
-
-    tokens_per_s = cfg.T / (ms_per_step * 1e-3)
-    A = cfg.T * cfg.k
-    layer_tflops = cfg.flops() / (ms_per_step * 1e-3) / 1e12
-    peak_mm = PEAK_FP8_TFLOPS if q8 else PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
-
-    fpa = gemm_flops_per_assignment(cfg)
-    dom = "gate_up_gemm"  # carries 2/3 of the flops and of the weight bytes
-    # The library takes its small-batch (weight streaming) path for bf16 calls
-    # with at most CMOE_DECODE_MAX_A (default 256) assignments.
-    small_batch = cfg.dtype == "bf16" and A <= int(os.environ.get("CMOE_DECODE_MAX_A", "256"))
-    prof_key = args.workload + ("-w8a8" if q8 else "-fp8" if fp8 else "")
-    if small_batch:
-        # weight streaming bound: algorithmic bytes = the active experts' gate
-        # and up weights, read once
-        achieved = active_weight_bytes(cfg, counts, dom, fp8) / (stage_ms[dom] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "traffic": profiled_traffic(prof_key, dom),
-                "kernel": ("decode_gemm_q8_kernel<true>" if q8 else "decode_gemm_f8_kernel<true>" if fp8
-                           else "decode_gemm_kernel<true>") + " (gate/up)"}
-    else:
-        achieved = fpa[dom] * A / (stage_ms[dom] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": peak_mm, "unit": "TFLOP/s",
-                "frac": achieved / peak_mm, "traffic": profiled_traffic(prof_key, dom),
-                "kernel": "grouped_gemm_kernel<256,256,128,128,true,"
-                          f"{str(fp8 and not q8).lower()},{str(q8).lower()},false> (gate/up)"}
-
+    results = {}
+    for n in names:
+        r = run_workload(n, args, fp8, q8)
+        results[n] = r
+        rec = r["record"]
+        print(f"# {rec['workload']}: {rec['ms_per_step']:.3f} ms/step, {rec['tokens_per_s']:.4g} tokens/s, "
+              f"layer MFMA {rec['layer_mfma_frac']:.3f} HBM {rec['layer_hbm_frac']:.3f}", file=sys.stderr,
+              flush=True)
+        if n != names[0]:
+            del r["inp"]
+    head = results[names[0]]
+    cfg, rec = head["cfg"], head["record"]
     out = {
         "metric": METRIC,
-        "value": tokens_per_s,
+        "value": rec["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": rec["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8" if q8 else cfg.dtype,
         "data": "synthetic (seeded SplitMix64 + Box-Muller, bf16 RNE; no trained weights)",
-        "config": {"workload": WORKLOAD_NAMES[args.workload] + ("-w8a8" if q8 else "-fp8-weights" if fp8 else ""),
-                   "T": cfg.T,
-                   "d_model": cfg.d, "n_experts": cfg.E, "top_k": cfg.k, "d_ff": cfg.f,
-                   "router_bias": cfg.bias or None,
+        "config": {"workload": rec["workload"], "T": cfg.T, "d_model": cfg.d, "n_experts": cfg.E,
+                   "top_k": cfg.k, "d_ff": cfg.f, "router_bias": cfg.bias or None,
                    "expert_weights": "fp8-e4m3, per-row power-of-two scale" if fp8 else cfg.dtype,
-                   "expert_gemm_inputs": "fp8-e4m3, per-row power-of-two scale" if q8 else cfg.dtype},
-        "roofline": roof,
-        "layer_tflops": layer_tflops,
-        "layer_mfma_frac": layer_tflops / peak_mm,
-        "stage_ms": stage_ms,
-        "empty_experts": int((counts == 0).sum()),
-        "wall_s_timed": t_wall,
-        "input_gen_s": t_gen,
+                   "token_rows_for_gate_up": "fp8-e4m3, per-row power-of-two scale" if q8 else cfg.dtype},
+        "roofline": rec["kernel_roofline"],
+        "layer": {"tflops": rec["layer_tflops"], "mfma_frac": rec["layer_mfma_frac"], "gbs": rec["layer_gbs"],
+                  "hbm_frac": rec["layer_hbm_frac"]},
+        "stage_ms": rec["stage_ms"],
+        "workloads": {results[n]["record"]["workload"]: results[n]["record"] for n in names},
+        "csrc_sha256": source_digest(),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens, fp8, q8)
+        out["cpu_baseline"] = cpu_baseline(cfg, head["inp"], args.cpu_sample_tokens, fp8, q8)
     print(json.dumps(out), flush=True)
 
 

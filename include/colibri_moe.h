@@ -82,8 +82,14 @@ typedef enum {
     COLIBRI_MOE_ERR_ALIGNMENT = 3,    /* x, y, a weight or topk_ids not 16-byte aligned, another
                                          routing buffer or b_router not 4-byte aligned */
     COLIBRI_MOE_ERR_OUT_OF_MEMORY = 4,/* init could not allocate its memory */
-    COLIBRI_MOE_ERR_HIP = 5           /* a HIP launch, copy or sync failed */
+    COLIBRI_MOE_ERR_HIP = 5,          /* a HIP launch, copy or sync failed */
+    COLIBRI_MOE_ERR_TOO_LARGE = 6     /* colibri_moe_forward_static: the call's working memory
+                                         exceeds COLIBRI_MOE_STATIC_SCRATCH_BYTES */
 } colibri_moe_status_t;
+
+/* Size of the static working-memory array of colibri_moe_forward_static, one
+ * per GPU the library runs on (64 MiB). */
+#define COLIBRI_MOE_STATIC_SCRATCH_BYTES (64 << 20)
 
 typedef enum { COLIBRI_MOE_F32 = 0, COLIBRI_MOE_BF16 = 1 } colibri_moe_dtype_t;
 
@@ -142,6 +148,25 @@ colibri_moe_status_t colibri_moe_init(colibri_moe_t** out, const colibri_moe_con
  * nothing. routing_out may be NULL. Allocates nothing. */
 colibri_moe_status_t colibri_moe_forward(colibri_moe_t* h, const void* x, int32_t T, void* y,
                                          const colibri_moe_routing_t* routing_out);
+
+/* colibri_moe_forward for callers that cannot allocate device memory at all
+ * (work under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, checks and results (y and every routing
+ * output bit-identical to colibri_moe_forward's), but the call's working
+ * memory (routing buffers the caller does not supply, H, the fp32 partial
+ * sums) lives in one static device array of COLIBRI_MOE_STATIC_SCRATCH_BYTES
+ * in the library, one per GPU, held until the process ends, instead of the
+ * handle's workspace. It allocates nothing and needs no clearing: every kernel
+ * writes what the next one reads. A call whose working memory does not fit
+ * returns COLIBRI_MOE_ERR_TOO_LARGE before enqueueing anything (bf16 layers:
+ * about (k * (2*d_ff + 8*d_model + 16)) bytes per token plus the small-batch
+ * K-slice partials; the Mixtral-shaped layer fits 500 tokens). Every call on
+ * one GPU uses that GPU's array, whichever handle makes it: calls that
+ * overlap on one GPU (several streams, threads or handles) race, and the
+ * caller must order them. The combine always runs as its own kernel here.
+ * ERR_HIP if the array's device address could not be found at init. */
+colibri_moe_status_t colibri_moe_forward_static(colibri_moe_t* h, const void* x, int32_t T, void* y,
+                                                const colibri_moe_routing_t* routing_out);
 
 /* Release everything init allocated (waits for the handle's stream first).
  * NULL is a no-op. The library keeps a registry of live handles: forward and

@@ -14,7 +14,8 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcolibri_moe.so")
 
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_OUT_OF_MEMORY, ERR_HIP = range(6)
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_OUT_OF_MEMORY, ERR_HIP, ERR_TOO_LARGE = range(7)
+STATIC_SCRATCH_BYTES = 64 << 20  # COLIBRI_MOE_STATIC_SCRATCH_BYTES
 F32, BF16 = 0, 1
 FLAG_ASYNC = 1 << 0
 FLAG_STAGE_TIMING = 1 << 1
@@ -40,8 +41,9 @@ class Routing(ctypes.Structure):
                 ("perm", ctypes.c_void_p), ("perm_slot", ctypes.c_void_p), ("inv", ctypes.c_void_p)]
 
 
-EXPORTS = ("colibri_moe_init", "colibri_moe_forward", "colibri_moe_free", "colibri_moe_status_string",
-           "colibri_moe_stage_times", "colibri_moe_stage_name", "colibri_moe_quantize_fp8")
+EXPORTS = ("colibri_moe_init", "colibri_moe_forward", "colibri_moe_forward_static", "colibri_moe_free",
+           "colibri_moe_status_string", "colibri_moe_stage_times", "colibri_moe_stage_name",
+           "colibri_moe_quantize_fp8")
 
 _lib = None
 
@@ -59,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.colibri_moe_init.argtypes = [ctypes.POINTER(P), ctypes.POINTER(Config), ctypes.POINTER(Weights), P]
         L.colibri_moe_forward.restype = ctypes.c_int
         L.colibri_moe_forward.argtypes = [P, P, i32, P, ctypes.POINTER(Routing)]
+        L.colibri_moe_forward_static.restype = ctypes.c_int
+        L.colibri_moe_forward_static.argtypes = [P, P, i32, P, ctypes.POINTER(Routing)]
         L.colibri_moe_free.restype = ctypes.c_int
         L.colibri_moe_free.argtypes = [P]
         L.colibri_moe_status_string.restype = ctypes.c_char_p
@@ -86,6 +90,12 @@ def colibri_moe_init(cfg: Config, weights: Weights, hip_stream: int = 0):
 def colibri_moe_forward(handle, x_ptr: int, T: int, y_ptr: int, routing: Routing | None = None) -> int:
     return lib().colibri_moe_forward(ctypes.c_void_p(handle), ctypes.c_void_p(x_ptr), T, ctypes.c_void_p(y_ptr),
                                      None if routing is None else ctypes.byref(routing))
+
+
+def colibri_moe_forward_static(handle, x_ptr: int, T: int, y_ptr: int, routing: Routing | None = None) -> int:
+    return lib().colibri_moe_forward_static(ctypes.c_void_p(handle), ctypes.c_void_p(x_ptr), T,
+                                            ctypes.c_void_p(y_ptr),
+                                            None if routing is None else ctypes.byref(routing))
 
 
 def colibri_moe_free(handle) -> int:
@@ -188,9 +198,11 @@ class MoELayer:
                     perm_slot=torch.empty(A, dtype=torch.int32, device=dev),
                     inv=torch.empty(A, dtype=torch.int32, device=dev))
 
-    def forward(self, x, y=None, routing: dict | None = None):
+    def forward(self, x, y=None, routing: dict | None = None, static_scratch: bool = False):
         """y [T][d] = layer(x). ``routing`` (from routing_buffers) receives the
-        routing outputs; missing keys are not written."""
+        routing outputs; missing keys are not written. static_scratch: call
+        colibri_moe_forward_static (working memory in the library's fixed
+        per-GPU array instead of the handle's)."""
         torch = self._torch
         if x.dtype != self.dtype or x.dim() != 2 or x.shape[1] != self.d or not x.is_contiguous():
             raise TypeError("x must be a contiguous [T][d] tensor of the layer dtype")
@@ -201,9 +213,10 @@ class MoELayer:
         if routing is not None:
             r = Routing(*[routing[n].data_ptr() if routing.get(n) is not None else None
                           for n, _ in Routing._fields_])
-        st = colibri_moe_forward(self.handle, x.data_ptr(), T, y.data_ptr(), r)
+        fn = colibri_moe_forward_static if static_scratch else colibri_moe_forward
+        st = fn(self.handle, x.data_ptr(), T, y.data_ptr(), r)
         if st != OK:
-            raise ColibriError("colibri_moe_forward", st)
+            raise ColibriError(fn.__name__, st)
         return y
 
     def stage_times(self) -> dict:

@@ -119,6 +119,43 @@ struct Carver {
     }
 };
 
+// Working memory of colibri_moe_forward_static: one fixed array per GPU in
+// the library's code object, so that call allocates nothing. In host code
+// `scratch` names a host-side stand-in, not device memory: kernels and copies
+// get the device address that hipGetSymbolAddress returns for it, looked up
+// once per device (with that device current) and kept here.
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) uint8_t scratch[COLIBRI_MOE_STATIC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+bool g_scratch_done[kMaxDevices];
+
+// Looks up this device's copy of `scratch` (the device must be current).
+// Failure leaves the pointer null: only colibri_moe_forward_static needs it.
+void setup_static_scratch(int device)
+{
+    if (device < 0 || device >= kMaxDevices)
+        return;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_done[device])
+        return;
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess && p != nullptr) {
+        g_scratch_ptr[device] = p;
+        g_scratch_done[device] = true;
+    } else {
+        (void)hipGetLastError();
+    }
+}
+
+void* static_scratch(int device)
+{
+    if (device < 0 || device >= kMaxDevices)
+        return nullptr;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    return g_scratch_ptr[device];
+}
+
 colibri_moe_status_t validate_config(const colibri_moe_config_t* c)
 {
     if (c->dtype != COLIBRI_MOE_F32 && c->dtype != COLIBRI_MOE_BF16)
@@ -330,6 +367,7 @@ colibri_moe_status_t colibri_moe_init(colibri_moe_t** out, const colibri_moe_con
         release(h);
         return COLIBRI_MOE_ERR_HIP;
     }
+    setup_static_scratch(h->device);
     // Small-batch path (bf16): calls with at most CMOE_DECODE_MAX_A
     // assignments (default 256; 0 turns the path off). Results do not depend
     // on the path beyond fp32 summation order.
@@ -495,6 +533,25 @@ colibri_moe_status_t colibri_moe_forward(colibri_moe_t* h, const void* x, int32_
     return forward_impl(h, x, T, y, ro, h->ws, true);
 }
 
+colibri_moe_status_t colibri_moe_forward_static(colibri_moe_t* h, const void* x, int32_t T, void* y,
+                                                const colibri_moe_routing_t* r)
+{
+    colibri_moe_routing_t ro;
+    bool skip;
+    const colibri_moe_status_t st = check_call(h, x, T, y, r, &ro, &skip);
+    if (st != COLIBRI_MOE_OK || skip)
+        return st;
+    if (layout_workspace(h, T, false, nullptr, nullptr) > (size_t)COLIBRI_MOE_STATIC_SCRATCH_BYTES)
+        return COLIBRI_MOE_ERR_TOO_LARGE;
+    uint8_t* base = (uint8_t*)static_scratch(h->device);
+    if (!base)
+        return COLIBRI_MOE_ERR_HIP;
+    Workspace ws;
+    layout_workspace(h, T, false, base, &ws);
+    return forward_impl(h, x, T, y, ro, ws, false);
+}
+
+
 colibri_moe_status_t colibri_moe_free(colibri_moe_t* h)
 {
     if (!h)
@@ -539,6 +596,8 @@ const char* colibri_moe_status_string(colibri_moe_status_t s)
         return "out of device memory";
     case COLIBRI_MOE_ERR_HIP:
         return "HIP runtime error";
+    case COLIBRI_MOE_ERR_TOO_LARGE:
+        return "batch needs more working memory than the static scratch array holds";
     }
     return "unknown status";
 }

@@ -33,8 +33,8 @@ def test_library_exports_every_declared_function():
 
 def test_status_strings_and_stage_names():
     assert cm.colibri_moe_status_string(cm.OK) == "ok"
-    texts = {cm.colibri_moe_status_string(s) for s in range(6)}
-    assert len(texts) == 6
+    texts = {cm.colibri_moe_status_string(s) for s in range(7)}
+    assert len(texts) == 7
     assert cm.colibri_moe_status_string(99) == "unknown status"
     assert [cm.colibri_moe_stage_name(i) for i in range(6)] == list(cm.STAGES)
     assert cm.colibri_moe_stage_name(6) is None
@@ -86,8 +86,16 @@ def test_forward_and_free_reject_unknown_handles():
     assert cm.colibri_moe_free(FAKE) == cm.ERR_INVALID_ARG
     assert cm.colibri_moe_forward(None, FAKE, 4, FAKE) == cm.ERR_INVALID_ARG
     assert cm.colibri_moe_forward(FAKE, FAKE, 4, FAKE) == cm.ERR_INVALID_ARG
+    assert cm.colibri_moe_forward_static(None, FAKE, 4, FAKE) == cm.ERR_INVALID_ARG
+    assert cm.colibri_moe_forward_static(FAKE, FAKE, 4, FAKE) == cm.ERR_INVALID_ARG
     with pytest.raises(RuntimeError):
         cm.colibri_moe_stage_times(FAKE)
+
+
+def test_static_scratch_size_matches_the_header():
+    text = open(os.path.join(ROOT, "include", "colibri_moe.h")).read()
+    m = re.search(r"#define COLIBRI_MOE_STATIC_SCRATCH_BYTES \((\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == cm.STATIC_SCRATCH_BYTES
 
 
 def test_binding_is_marshalling_only():

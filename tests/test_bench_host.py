@@ -77,7 +77,7 @@ def test_committed_summaries_are_complete():
         if not name.endswith("_rocprof.md"):
             continue
         text = open(os.path.join(prof, name)).read()
-        assert ("csrc_sha256:" in text or "source_sha256(" in text) and "rocprofv3" in text, name
+        assert "csrc_sha256:" in text and "rocprofv3" in text, name
         if name.startswith("gate_up_gemm_"):
             assert "traffic_bytes_per_launch:" in text, name
 

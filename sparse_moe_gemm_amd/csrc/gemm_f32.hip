@@ -29,7 +29,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_f32_kernel(GemmArgs g)
     // Every wave derives the block's tile from offsets[] (the same walker as
     // the bf16 GEMMs: one m-tile count per expert, a wave prefix sum, a ballot).
     TileTable tt;
-    const int total = make_table<kT>(g.offsets, g.E, threadIdx.x % kWave, tt) * NT;
+    const int total = make_table<kT>(g.offsets, g.E, threadIdx.x % kWave, NT, tt);
     if ((int)blockIdx.x >= total)
         return;
     const Tile tl = decode<kT>(tt, blockIdx.x, NT, 1, NT, 1);

@@ -3,24 +3,55 @@
 // device from the dispatch's expert offsets, so the host never learns the
 // per-expert row counts. Experts without rows have no m-tiles (their weights
 // are never read).
+//
+// Two classes of experts: those with more than SM rows (class 0) and small
+// ones with 1..SM rows (class 1, one m-tile each; SM = 0: no small class).
+// A small expert's tile does little matrix work but still streams a whole
+// weight panel from HBM, so the small experts' tiles are spread evenly over
+// the big experts' ones instead of running last, all together: the tile
+// sequence is cut into units of 8 consecutive indices (one per XCD, as the
+// workgroups go to the XCDs round robin) and the small units are placed among
+// the big ones in proportion (Bresenham), so within a unit the tile order of
+// each class, and the XCD each tile of a group lands on, stay as they were.
+// Each class keeps the order expert -> K split -> group of GN n-tiles ->
+// m-tile -> n-tile.
 #pragma once
 
 #include "common.hpp"
 
 namespace cmoe {
 
+constexpr int kUnit = 8;  // tiles per interleave unit (XCDs)
+
+// M-tiles of an expert with c rows: c / BM full tiles and a ragged last one.
+template <int BM>
+__device__ __forceinline__ int mtiles_of(int c)
+{
+    return (c + BM - 1) / BM;
+}
+
+// Class of an expert with c > 0 rows.
+template <int SM>
+__device__ __forceinline__ int class_of(int c)
+{
+    return c <= SM ? 1 : 0;
+}
+
 // Per-lane view of the m-tiles: lane l holds experts 4l .. 4l+3 (E <= 256).
 struct TileTable {
-    int off[4];  // segment start offsets[e]
-    int cnt[4];  // rows of the expert
-    int mpre;    // m-tiles of all experts below 4l
-    int msum;    // m-tiles of this lane's experts
+    int off[4];   // segment start offsets[e]
+    int cnt[4];   // rows of the expert
+    int mpre[2];  // per class: m-tiles of that class's experts below 4l
+    int msum[2];  // per class: m-tiles of this lane's experts of that class
+    int tiles[2]; // per class: tiles (m-tiles x tiles per m-tile), uniform
 };
 
-template <int BM>
-__device__ __forceinline__ int make_table(const int32_t* offsets, int E, int lane, TileTable& t)
+// Builds the table; returns the number of tiles (uniform). per_m: tiles per
+// m-tile (n-tiles x K splits).
+template <int BM, int SM = 0>
+__device__ __forceinline__ int make_table(const int32_t* offsets, int E, int lane, int per_m, TileTable& t)
 {
-    int ms = 0;
+    int ms[2] = {0, 0};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int e = lane * 4 + q;
@@ -28,18 +59,27 @@ __device__ __forceinline__ int make_table(const int32_t* offsets, int E, int lan
         const int o1 = e < E ? offsets[e + 1] : 0;
         t.off[q] = o0;
         t.cnt[q] = o1 - o0;
-        ms += (o1 - o0 + BM - 1) / BM;
+        const int m = mtiles_of<BM>(o1 - o0);
+        if (SM == 0 || class_of<SM>(o1 - o0) == 0)
+            ms[0] += m;
+        else
+            ms[1] += m;
     }
-    int incl = ms;
+    t.mpre[1] = t.msum[1] = t.tiles[1] = 0;
 #pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int o = __shfl_up(incl, d, kWave);
-        if (lane >= d)
-            incl += o;
+    for (int c = 0; c < (SM > 0 ? 2 : 1); ++c) {
+        int incl = ms[c];
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int o = __shfl_up(incl, d, kWave);
+            if (lane >= d)
+                incl += o;
+        }
+        t.mpre[c] = incl - ms[c];
+        t.msum[c] = ms[c];
+        t.tiles[c] = __builtin_amdgcn_readfirstlane(__shfl(incl, kWave - 1, kWave)) * per_m;
     }
-    t.mpre = incl - ms;
-    t.msum = ms;
-    return __builtin_amdgcn_readfirstlane(__shfl(incl, kWave - 1, kWave));  // total m-tiles (uniform)
+    return t.tiles[0] + t.tiles[1];
 }
 
 struct Tile {
@@ -48,24 +88,52 @@ struct Tile {
     int kt0, nkt;    // K stages of the split
 };
 
-// Tile behind index L (< total). Tiles of one m-tile are consecutive in the
-// global m-tile order, NT * S of them, so L / (NT * S) is the global m-tile
-// index j; the lane whose experts cover j holds the expert.
-template <int BM>
+// Tile behind index L (< total). First the class and the index inside it
+// (the unit interleave above), then, within the class, tiles of one m-tile are
+// consecutive, NT * S of them, so idx / (NT * S) is the class's m-tile index
+// j; the lane whose experts cover j holds the expert.
+template <int BM, int SM = 0>
 __device__ __forceinline__ Tile decode(const TileTable& t, int L, int NT, int S, int GN, int KT)
 {
+    int cls = 0, idx = L;
+    if constexpr (SM > 0) {
+        const int TA = t.tiles[0], TB = t.tiles[1];
+        const int nb = TA / kUnit, ns = TB / kUnit, nu = nb + ns;
+        if (L < kUnit * nu) {
+            const int u = L / kUnit, r = L - u * kUnit;
+            const int s0 = (int)((int64_t)u * ns / nu), s1 = (int)((int64_t)(u + 1) * ns / nu);
+            if (s1 > s0) {
+                cls = 1;
+                idx = kUnit * s0 + r;
+            } else {
+                idx = kUnit * (u - s0) + r;
+            }
+        } else {
+            const int rem = L - kUnit * nu, ra = TA - kUnit * nb;
+            if (rem < ra) {
+                idx = kUnit * nb + rem;
+            } else {
+                cls = 1;
+                idx = kUnit * ns + rem - ra;
+            }
+        }
+        cls = __builtin_amdgcn_readfirstlane(cls);
+        idx = __builtin_amdgcn_readfirstlane(idx);
+    }
     const int per_m = NT * S;
-    const int j = L / per_m;
-    const uint64_t hit = __ballot(j >= t.mpre && j < t.mpre + t.msum);
+    const int j = idx / per_m;
+    const int mp = SM > 0 && cls ? t.mpre[1] : t.mpre[0];
+    const int msm = SM > 0 && cls ? t.msum[1] : t.msum[0];
+    const uint64_t hit = __ballot(j >= mp && j < mp + msm);
     const int ln = __builtin_ctzll(hit);
-    int base = __builtin_amdgcn_readlane(t.mpre, ln);
+    int base = __builtin_amdgcn_readlane(mp, ln);
     int e = 0, Me = 0, cnt = 0, seg0 = 0;
     bool found = false;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int c = __builtin_amdgcn_readlane(t.cnt[q], ln);
         const int o = __builtin_amdgcn_readlane(t.off[q], ln);
-        const int me = (c + BM - 1) / BM;
+        const int me = SM == 0 || class_of<SM>(c) == cls ? mtiles_of<BM>(c) : 0;
         if (!found) {
             if (j < base + me) {
                 found = true;
@@ -79,15 +147,15 @@ __device__ __forceinline__ Tile decode(const TileTable& t, int L, int NT, int S,
         }
     }
     Tile r;
-    const int local = L - base * per_m;
+    const int local = idx - base * per_m;
     r.s = local / (Me * NT);
     const int rem = local - r.s * Me * NT;
     const int grp = rem / (Me * GN);
     const int gn = min(GN, NT - grp * GN);
-    const int idx = rem - grp * Me * GN;
+    const int id2 = rem - grp * Me * GN;
     r.e = e;
-    r.m = idx / gn;
-    r.n = grp * GN + (idx - r.m * gn);
+    r.m = id2 / gn;
+    r.n = grp * GN + (id2 - r.m * gn);
     r.row0 = seg0 + r.m * BM;
     r.rows = min(BM, cnt - r.m * BM);
     const int per_s = KT / S;

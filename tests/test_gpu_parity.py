@@ -37,6 +37,23 @@ SMALL = [
     # several workgroups; one hot expert takes every token, the other none
     C("hot-expert-split-dispatch", 4608, 128, 2, 1, 128, "bf16", {0: 100.0}),
     C("split-dispatch-k4", 1100, 128, 16, 4, 128, "bf16", {3: 2.0}),
+    # one expert with a ragged last m-tile of 1, 16, 17, 32 and 33 rows past
+    # 256 (the last m-tile's waves: only the first holding rows, the first
+    # two, all); 800 = 3 * 256 + 32 puts the ragged tile after full ones;
+    # d = 384 runs the down GEMM's 128-column tiles
+    C("tail-257", 257, 256, 1, 1, 512, "bf16"),
+    C("tail-272", 272, 256, 1, 1, 512, "bf16"),
+    C("tail-273", 273, 256, 1, 1, 512, "bf16"),
+    C("tail-288", 288, 256, 1, 1, 512, "bf16"),
+    C("tail-289", 289, 256, 1, 1, 512, "bf16"),
+    C("tail-800", 800, 256, 1, 1, 768, "bf16"),
+    C("tail-d384", 270, 384, 1, 1, 256, "bf16"),
+    C("tails-mixed", 1100, 256, 4, 2, 256, "bf16", {0: 0.3, 1: -0.2}),
+    # small experts (at most 64 rows) among big ones: the down GEMM spreads
+    # their tiles over the big experts' tiles in units of 8 (a remainder of
+    # each class at the end); two K splits (K = 2048) and one
+    C("small-among-big", 3000, 256, 32, 2, 2048, "bf16", {0: 3.0, 5: 3.0, 9: 2.0}),
+    C("small-among-big-k1", 2600, 256, 48, 1, 256, "bf16", {2: 4.0, 40: 4.0}),
 ]
 
 

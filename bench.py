@@ -79,7 +79,9 @@ def parse():
 
 def copy_calibration(mib: int):
     """A plain device-to-device copy of known size: its FETCH_SIZE / WRITE_SIZE
-    readings give the factor between those counters and bytes moved."""
+    readings give the factor between those counters and bytes moved. Also
+    reports the copy's rate (bytes read + written per second), an attainable
+    HBM figure next to the 8 TB/s nominal one."""
     import torch
 
     n = mib * (1 << 20) // 4
@@ -88,7 +90,16 @@ def copy_calibration(mib: int):
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 3}), flush=True)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / 10
+    print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 13,
+                      "copy_gbs_read_plus_write": 2 * n * 4 / (ms * 1e-3) / 1e9, "copy_ms": ms}), flush=True)
 
 
 def to_dev(a):
@@ -239,12 +250,41 @@ def run_workload(name: str, args, fp8: bool, q8: bool) -> dict:
     t_wall = time.perf_counter()
     for _ in range(args.steps):
         layer.forward(x, y, keep)
+    t_enq = time.perf_counter() - t_wall  # host time to enqueue the K forwards
     ev1.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
     counts = keep["expert_counts"].cpu().numpy()
     layer.close()
+
+    # 1b) the same forward captured once into a HIP graph and replayed K
+    # times (small batches, where launch gaps matter): the handle runs on the
+    # capturing stream
+    graph_ms = None
+    if cfg.T * cfg.k <= 256 and cfg.dtype == "bf16":
+        gs = torch.cuda.Stream()
+        glayer = cm.MoELayer(*wts, cfg.k, max_tokens=cfg.T, flags=cm.FLAG_ASYNC | flags, stream=gs)
+        with torch.cuda.stream(gs):
+            for _ in range(2):
+                glayer.forward(x, y)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=gs):
+            glayer.forward(x, y)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(gs):
+            ev0.record(gs)
+            for _ in range(args.steps):
+                graph.replay()
+            ev1.record(gs)
+        torch.cuda.synchronize()
+        graph_ms = ev0.elapsed_time(ev1) / args.steps
+        del graph
+        glayer.close()
 
     # 2) per-kernel durations: the library's per-stage events (recorded on
     # the same stream as the kernels), averaged over K forwards
@@ -302,6 +342,8 @@ def run_workload(name: str, args, fp8: bool, q8: bool) -> dict:
             "stage_ms": stage_ms,
             "empty_experts": int((counts == 0).sum()),
             "active_experts": int((counts > 0).sum()),
+            "host_enqueue_us_per_step": t_enq / args.steps * 1e6,
+            "graph_replay_ms_per_step": graph_ms,
             "wall_s_timed": t_wall,
             "input_gen_s": t_gen,
         },

@@ -437,7 +437,8 @@ colibri_moe_status_t forward_impl(colibri_moe* h, const void* x, int32_t T, void
 
     const int A = T * c.top_k;
     int split = 1;
-    bool fused = false;  // combine done by the down GEMM
+    bool fused = false;    // combine done by the down GEMM
+    int ys_bf16 = 0;       // expert outputs stored as bf16
     if (bf && A <= h->dec_max_a) {
         // small-batch path: weight streaming with K slices, then the slice sum
         // and SiLU(g)*u
@@ -471,13 +472,17 @@ colibri_moe_status_t forward_impl(colibri_moe* h, const void* x, int32_t T, void
             dn.y = y;
             fused = true;
         }
+        // Without a K split the expert outputs go to Ys as bf16 rows (bf16
+        // weights).
+        dn.ys_bf16 = bf && !h->fp8 && split == 1 && !fused;
+        ys_bf16 = dn.ys_bf16;
         CMOE_HIP(bf ? launch_down_bf16(dn, s) : launch_down_f32(dn, s));
     }
     if (tm)
         CMOE_HIP(hipEventRecord(h->ev[5], s));
 
     if (!fused) {
-        CombineArgs ca{ws.Ys, inv, topw, y, T, c.top_k, c.d_model, split, bf ? 1 : 0};
+        CombineArgs ca{ws.Ys, inv, topw, y, T, c.top_k, c.d_model, split, bf ? 1 : 0, ys_bf16};
         CMOE_HIP(launch_combine(ca, s));
     }
     if (tm)

@@ -8,7 +8,8 @@
 // the output dtype (round to nearest even for bf16). The down GEMM wrote each
 // expert output at its sorted position p; inv maps assignment t*k+j to it.
 // When the down GEMM split K, Ys holds `split` partial sums per row (at
-// strides of T*k rows), added in split order before the weighting. Each
+// strides of T*k rows), added in split order before the weighting; without a
+// split (tiled path) the rows are bf16, widened exactly here. Each
 // thread handles 4 consecutive outputs with 16-byte loads; the kernel is
 // bound by HBM.
 #include "common.hpp"
@@ -73,6 +74,44 @@ __global__ __launch_bounds__(256) void combine_ks_kernel(CombineArgs g)
     }
 }
 
+// Expert outputs stored as bf16 (no K split), K slots known at compile
+// time: eight consecutive outputs per thread, one 16-byte load per slot, all
+// K in flight together, widened exactly and summed in fp32 in slot order.
+template <int K>
+__global__ __launch_bounds__(256) void combine_b16_kernel(CombineArgs g)
+{
+    const int64_t groups = (int64_t)g.T * (g.d / 8);
+    const uint16_t* yb = (const uint16_t*)g.ys;
+    for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < groups;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t t = idx / (g.d / 8);
+        const int o = (int)(idx % (g.d / 8)) * 8;
+        int pos[K];
+        float wgt[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            pos[j] = g.inv[t * K + j];
+            wgt[j] = g.w[t * K + j];
+        }
+        uint4 v[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j)
+            v[j] = *(const uint4*)(yb + (int64_t)pos[j] * g.d + o);
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const uint32_t w4[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] = fmaf(wgt[j], __uint_as_float(w4[q] << 16), acc[2 * q]);
+                acc[2 * q + 1] = fmaf(wgt[j], __uint_as_float(w4[q] & 0xFFFF0000u), acc[2 * q + 1]);
+            }
+        }
+        store_out(g, t, o, make_float4(acc[0], acc[1], acc[2], acc[3]));
+        store_out(g, t, o + 4, make_float4(acc[4], acc[5], acc[6], acc[7]));
+    }
+}
+
 // Any k and number of partials (the small-batch path's K slices).
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs g)
 {
@@ -108,6 +147,12 @@ bool launch_ks(const CombineArgs& a, dim3 grid, hipStream_t s)
 {
     if (a.k != K || a.split > 2)
         return false;
+    if (a.ys_bf16) {
+        const int64_t groups = (int64_t)a.T * (a.d / 8);
+        const unsigned blocks = (unsigned)std::min<int64_t>((groups + 255) / 256, 8192);
+        hipLaunchKernelGGL((combine_b16_kernel<K>), dim3(blocks), dim3(256), 0, s, a);
+        return true;
+    }
     if (a.split == 1)
         hipLaunchKernelGGL((combine_ks_kernel<K, 1>), grid, dim3(256), 0, s, a);
     else
@@ -124,10 +169,13 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s)
     if (blocks > 8192)
         blocks = 8192;
     const dim3 grid((unsigned)blocks);
-    if (!(launch_ks<1>(a, grid, s) || launch_ks<2>(a, grid, s) || launch_ks<3>(a, grid, s) ||
-          launch_ks<4>(a, grid, s) || launch_ks<5>(a, grid, s) || launch_ks<6>(a, grid, s) ||
-          launch_ks<7>(a, grid, s) || launch_ks<8>(a, grid, s)))
-        hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, a);
+    if (launch_ks<1>(a, grid, s) || launch_ks<2>(a, grid, s) || launch_ks<3>(a, grid, s) ||
+        launch_ks<4>(a, grid, s) || launch_ks<5>(a, grid, s) || launch_ks<6>(a, grid, s) ||
+        launch_ks<7>(a, grid, s) || launch_ks<8>(a, grid, s))
+        return hipGetLastError();
+    if (a.ys_bf16)  // bf16 expert outputs come with k <= 8 and no K split
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

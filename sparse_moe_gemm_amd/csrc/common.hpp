@@ -119,6 +119,9 @@ struct GemmArgs {
     const int32_t* inv;
     const float* topw;
     void* y;
+    // down GEMM with split == 1, without the fused combine: out is [A][d] bf16
+    // (each expert output row rounded to nearest even) instead of fp32
+    int ys_bf16;
 };
 hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t s);
 hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t s);
@@ -172,13 +175,14 @@ hipError_t launch_fp8_encode_rows(const void* w, const float* scales, uint8_t* c
                                   hipStream_t s);
 
 struct CombineArgs {
-    const float* ys;    // split partials, each [A][d] fp32 by sorted position
+    const float* ys;    // split partials, each [A][d] fp32 by sorted position (ys_bf16: one [A][d] bf16)
     const int32_t* inv; // [A]: sorted position of assignment t*k+j
     const float* w;     // [T][k]
     void* y;            // [T][d] dtype
     int T, k, d;
     int split;          // number of partials, at ys + s*T*k*d
     int bf16_out;
+    int ys_bf16;        // the expert outputs are bf16 (split == 1)
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 

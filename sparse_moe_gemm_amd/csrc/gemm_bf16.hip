@@ -535,8 +535,9 @@ __device__ __forceinline__ void stage_q8(const i32x4& ra, const LoadSrc<A_INS>& 
 // completes a count (k assignments times the K splits) finds every partial
 // row of that token and n-tile stored, and its wave computes the token's
 // columns of y exactly as the combine kernel does: partials added in split
-// order, weighted sum over the k slots in slot order (fused multiply-add in
-// fp32), rounded to bf16. Which workgroup does it changes nothing in the
+// order (bf16 weights without a K split: each row rounded to bf16 first, as
+// the unfused path stores it), weighted sum over the k slots in slot order
+// (fused multiply-add in fp32), rounded to bf16. Which workgroup does it changes nothing in the
 // result. Ordering: every wave's stores are released at device scope before
 // the barrier after which the counts are incremented; a wave that completed
 // counts acquires at device scope before it reads the other rows. Lane l of
@@ -592,6 +593,12 @@ __device__ __forceinline__ void fused_combine(const GemmArgs& g, int row0, int r
             if (j < g.k) {
                 const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wgt[j]), b));
                 float4 u = v[j][0];
+                if (g.split == 1 && g.scales == nullptr) {  // bf16 weights: the values the unfused path stores as bf16
+                    u.x = bf16_to_f32(f32_to_bf16_bits(u.x));
+                    u.y = bf16_to_f32(f32_to_bf16_bits(u.y));
+                    u.z = bf16_to_f32(f32_to_bf16_bits(u.z));
+                    u.w = bf16_to_f32(f32_to_bf16_bits(u.w));
+                }
                 if (g.split > 1) {
                     u.x += v[j][1].x;
                     u.y += v[j][1].y;
@@ -777,14 +784,18 @@ __device__ __forceinline__ void load_scales(const float* scales, const Tile& t, 
 // bf16 layout's shape).
 // FC: the down GEMM with the combine fused into its epilogue (a separate
 // instantiation: its epilogue code would cost the plain kernel registers).
+// YB: the down GEMM without a K split stores each expert output row rounded
+// to bf16 (the activation type, like H) instead of fp32: half the bytes to
+// write here and to read in the combine.
 // Tile order (tiles.hpp): the down GEMM spreads the tiles of experts with at
 // most 64 rows over the other experts' tiles (SM = 64): each reads a whole
 // weight panel for little matrix work, and run together at the end they
-// queue on HBM (skewed routing: 6% less time for the down GEMM; no change
+// queue on HBM (skewed routing: 7-11% less time for the down GEMM; no change
 // for the gate/up GEMM, whose tiles are longer, so it keeps the plain order).
-template <int BM, int BN, int WM, int WN, bool GATE_UP, bool F8, bool Q8, bool FC = false>
+template <int BM, int BN, int WM, int WN, bool GATE_UP, bool F8, bool Q8, bool FC = false, bool YB = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void grouped_gemm_kernel(GemmArgs g)
 {
+    static_assert(!YB || (!GATE_UP && !FC), "bf16 expert outputs: plain down GEMM");
     constexpr int SM = GATE_UP ? 0 : 64;
     static_assert(!(F8 && Q8), "one weight mode");
     constexpr int WAVES_N = BN / WN;
@@ -1126,6 +1137,58 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 }
             } else {
                 float* Ys = (float*)g.out + (int64_t)cur.s * g.A_max * g.d;
+                if constexpr (YB) {
+                    // bf16 rows through LDS, as the gate/up epilogue: two
+                    // 32x32 accumulator blocks at a time go into this wave's
+                    // 8 KiB of the free ring slot (rows of 32 fp32, chunk index
+                    // XORed with row%8), then each lane reads back 16
+                    // consecutive values of each block from one row, rounds
+                    // them to bf16 and writes them with 16-byte stores.
+                    static_assert(M16 && NI % 2 == 0, "bf16 outputs: 16x16 MFMA layout, column block pairs");
+                    const int bfree = b == 0 ? kRing - 1 : b - 1;
+                    float* ep = (float*)&ring.st[bfree] + wv * 2048;
+                    const int rr = lane >> 1;       // row read back by this lane
+                    const int rc = (lane & 1) * 4;  // first 16-byte chunk read back
+                    uint16_t* Yb = (uint16_t*)g.out;
+#pragma unroll
+                    for (int i = 0; i < MI; ++i) {
+                        if (PARTIAL && i >= RG)  // padding rows only: nothing to store
+                            continue;
+#pragma unroll
+                        for (int jp = 0; jp < NI; jp += 2) {
+#pragma unroll
+                            for (int c = 0; c < 4; ++c)  // 16x16 block (c/2, c%2) of the region
+#pragma unroll
+                                for (int q = 0; q < 4; ++q) {
+                                    const int r = 16 * (c >> 1) + 4 * (lane >> 4) + q;
+                                    const int cc = 16 * (c & 1) + (lane & 15);
+                                    const int o = r * 32 + (((cc >> 2) ^ (r & 7)) << 2) + (cc & 3);
+                                    ep[o] = acc[i][jp].q[c][q];
+                                    ep[1024 + o] = acc[i][jp + 1].q[c][q];
+                                }
+                            const int row = min(rbase - 4 * (lane >> 4) + i * 32 + rr, cur.rows - 1);
+#pragma unroll
+                            for (int h = 0; h < 2; ++h) {  // the two column blocks
+                                uint32_t hv[8];
+#pragma unroll
+                                for (int t = 0; t < 4; ++t) {
+                                    const int o = h * 1024 + rr * 32 + (((rc + t) ^ (rr & 7)) << 2);
+                                    const floatx4 v = *(const floatx4*)(ep + o);
+                                    hv[2 * t] = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+                                    hv[2 * t + 1] =
+                                        (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+                                }
+                                const int col = cur.n * BN + wn * WN + (jp + h) * 32 + rc * 4;
+                                Vec16* dst = (Vec16*)(Yb + (int64_t)(cur.row0 + row) * g.d + col);
+                                dst[0] = Vec16{hv[0], hv[1], hv[2], hv[3]};
+                                dst[1] = Vec16{hv[4], hv[5], hv[6], hv[7]};
+                            }
+                        }
+                    }
+                    // Every wave is done with the slot before the next stage loads it.
+                    __builtin_amdgcn_s_barrier();
+                    asm volatile("" ::: "memory");
+                } else {
 #pragma unroll
                 for (int i = 0; i < MI; ++i) {
                     if (PARTIAL && i >= RG)  // padding rows only: nothing to store
@@ -1153,6 +1216,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                                 yrow[j * 32] = acc[i][j][q];
                         }
                     }
+                }
                 }
                 if constexpr (FC)
                     fused_combine<BN>(g, cur.row0, cur.rows, cur.n, wv, lane);
@@ -1301,6 +1365,15 @@ hipError_t launch_grouped(const GemmArgs& a, hipStream_t s)
         else
             hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 128, 128, 64, false, F8, Q8, true>), dim3(grid),
                                dim3(kThreads), 0, s, a);
+    } else if (a.ys_bf16) {
+        if constexpr (!Q8 && !F8) {
+            if (BN == 256)
+                hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 256, 128, 128, false, F8, Q8, false, true>), dim3(grid),
+                                   dim3(kThreads), 0, s, a);
+            else
+                hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 128, 128, 64, false, F8, Q8, false, true>), dim3(grid),
+                                   dim3(kThreads), 0, s, a);
+        }
     } else {
         if (BN == 256)
             hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 256, 128, 128, false, F8, Q8>), dim3(grid), dim3(kThreads),

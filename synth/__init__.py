@@ -137,6 +137,9 @@ CONFIGS = {
     "decode": LayerConfig("decode", 32, 4096, 8, 2, 14336, "bf16"),
     "skewed": LayerConfig("skewed", 16384, 4096, 64, 2, 1408, "bf16", _SKEW),
     "skewed-masked": LayerConfig("skewed-masked", 16384, 4096, 64, 2, 1408, "bf16", _SKEW_MASKED),
+    # one expert takes every token: the expert GEMMs are plain dense GEMMs
+    # (gate/up 8192 x 28672 x 4096), a reference point for the grouped kernel
+    "dense": LayerConfig("dense", 8192, 4096, 1, 1, 14336, "bf16"),
 }
 
 

@@ -72,6 +72,7 @@ struct colibri_moe {
     bool timing;
     hipEvent_t ev[kStages + 1];
     int group_n_gu, group_n_dn;  // tile order of the grouped GEMMs (n-tiles per group)
+    int order_m_rows;            // m-tile groups when the mean rows per expert are at most this
     bool fuse_combine;  // bf16 tiled path: combine in the down GEMM's epilogue
     int cus;        // compute units of the device (persistent GEMM grid)
     int dec_max_a;  // bf16 calls with T*k <= dec_max_a take the small-batch path
@@ -352,6 +353,12 @@ colibri_moe_status_t colibri_moe_init(colibri_moe_t** out, const colibri_moe_con
     const int gn = env_int("CMOE_GROUP_N", 0, 0, 1 << 20);
     h->group_n_gu = gn > 0 ? gn : 8;
     h->group_n_dn = gn > 0 ? gn : 64;
+    // Many experts of one or two m-tiles each (fine-grained layers): token
+    // rows are the data read again and again (once per n-tile), weight
+    // panels once or twice; there the tile order keeps an m-tile's n-tiles on
+    // one XCD (groups of 8 m-tiles) instead. Chosen per call from the mean
+    // rows per expert (threshold CMOE_M_ORDER_ROWS, 0 = never).
+    h->order_m_rows = env_int("CMOE_M_ORDER_ROWS", 384, 0, 1 << 30);
     // Combine fused into the down GEMM's epilogue (bf16 layers, tiled path)
     // with CMOE_FUSE_COMBINE=1; the default runs the combine kernel, which is
     // faster here: the fused form needs device-scope release/acquire fences
@@ -455,8 +462,9 @@ colibri_moe_status_t forward_impl(colibri_moe* h, const void* x, int32_t T, void
         CMOE_HIP(launch_decode_gemm(dn, 0, h->cus, s));
         split = h->dec_split_dn;
     } else {
+        const bool order_m = (int64_t)A <= (int64_t)h->order_m_rows * c.n_experts;
         GemmArgs gu{q8 ? (const void*)ws.xq : x, h->w_gu, h->s_gu, q8 ? ws.xsc : nullptr, ws.H, offsets, perm, A,
-                    c.n_experts, c.top_k, c.d_model, c.d_ff, h->group_n_gu, 1, h->cus};
+                    c.n_experts, c.top_k, c.d_model, c.d_ff, order_m ? -8 : h->group_n_gu, 1, h->cus};
         CMOE_HIP(bf ? launch_gate_up_bf16(gu, s) : launch_gate_up_f32(gu, s));
         if (tm) {
             CMOE_HIP(hipEventRecord(h->ev[3], s));
@@ -464,7 +472,7 @@ colibri_moe_status_t forward_impl(colibri_moe* h, const void* x, int32_t T, void
         }
         split = bf ? down_split_bf16(A, c.n_experts, c.d_model, c.d_ff, h->cus, 0) : 1;
         GemmArgs dn{ws.H, h->w_d, h->s_d, nullptr, ws.Ys, offsets, perm, A,
-                    c.n_experts, c.top_k, c.d_model, c.d_ff, h->group_n_dn, split, h->cus};
+                    c.n_experts, c.top_k, c.d_model, c.d_ff, order_m ? -8 : h->group_n_dn, split, h->cus};
         if (bf && h->ccnt && fused_ok) {
             dn.cnt = h->ccnt;
             dn.inv = inv;

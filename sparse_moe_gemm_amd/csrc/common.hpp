@@ -106,7 +106,7 @@ struct GemmArgs {
     const int32_t* perm;      // [A]
     int A_max;                // A = T*k of this call (bounds the tile grid)
     int E, k, d, f;
-    int group_n;              // n-tiles per tile group (tile order), >= 1
+    int group_n;              // tile order (tiles.hpp): > 0 n-tiles per group; -G: groups of G m-tiles
     int split;                // K splits of the down GEMM (1 or 2; gate/up: 1)
     int grid;                 // workgroups of a persistent launch (compute units)
     // Combine fused into the down GEMM (bf16 tiled path, optional; cnt ==

@@ -14,7 +14,12 @@
 // the big ones in proportion (Bresenham), so within a unit the tile order of
 // each class, and the XCD each tile of a group lands on, stay as they were.
 // Each class keeps the order expert -> K split -> group of GN n-tiles ->
-// m-tile -> n-tile.
+// m-tile -> n-tile (GN > 0: within a group every m-tile of one n-tile lands
+// on one XCD, which reads that weight panel into its L2 once), or, with
+// GN = -G, K split -> group of G consecutive m-tiles (across experts) ->
+// n-tile -> m-tile (every n-tile of one m-tile lands on one XCD, which reads
+// that m-tile's token rows once; for experts of one or two m-tiles, whose
+// weight panels are used once or twice anyway).
 #pragma once
 
 #include "common.hpp"
@@ -121,7 +126,23 @@ __device__ __forceinline__ Tile decode(const TileTable& t, int L, int NT, int S,
         idx = __builtin_amdgcn_readfirstlane(idx);
     }
     const int per_m = NT * S;
-    const int j = idx / per_m;
+    int j, ms = 0, mn = 0, mm = 0;  // class m-tile index; m-group order: split, n-tile, m-tile in group
+    if (GN < 0) {
+        const int GM = -GN;
+        const int mtot = (SM > 0 && cls ? t.tiles[1] : t.tiles[0]) / per_m;
+        const int per_split = mtot * NT;
+        ms = idx / per_split;
+        const int rem = idx - ms * per_split;
+        const int grp = rem / (GM * NT);
+        const int gm = min(GM, mtot - grp * GM);
+        const int r2 = rem - grp * GM * NT;
+        mn = r2 / gm;
+        mm = r2 - mn * gm;
+        j = grp * GM + mm;
+    } else {
+        j = idx / per_m;
+    }
+    j = __builtin_amdgcn_readfirstlane(j);
     const int mp = SM > 0 && cls ? t.mpre[1] : t.mpre[0];
     const int msm = SM > 0 && cls ? t.msum[1] : t.msum[0];
     const uint64_t hit = __ballot(j >= mp && j < mp + msm);
@@ -147,15 +168,21 @@ __device__ __forceinline__ Tile decode(const TileTable& t, int L, int NT, int S,
         }
     }
     Tile r;
-    const int local = idx - base * per_m;
-    r.s = local / (Me * NT);
-    const int rem = local - r.s * Me * NT;
-    const int grp = rem / (Me * GN);
-    const int gn = min(GN, NT - grp * GN);
-    const int id2 = rem - grp * Me * GN;
     r.e = e;
-    r.m = id2 / gn;
-    r.n = grp * GN + (id2 - r.m * gn);
+    if (GN < 0) {
+        r.s = ms;
+        r.m = j - base;
+        r.n = mn;
+    } else {
+        const int local = idx - base * per_m;
+        r.s = local / (Me * NT);
+        const int rem = local - r.s * Me * NT;
+        const int grp = rem / (Me * GN);
+        const int gn = min(GN, NT - grp * GN);
+        const int id2 = rem - grp * Me * GN;
+        r.m = id2 / gn;
+        r.n = grp * GN + (id2 - r.m * gn);
+    }
     r.row0 = seg0 + r.m * BM;
     r.rows = min(BM, cnt - r.m * BM);
     const int per_s = KT / S;

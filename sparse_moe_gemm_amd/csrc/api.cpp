@@ -58,7 +58,7 @@ struct colibri_moe {
     void* arena;
     size_t arena_bytes;
     // weights (library copies, repacked)
-    void* w_rt;   // [E][d]
+    void* w_rt;   // router weights in the router kernels' layout
     float* b_r;   // [E]
     void* w_gu;   // [E][2f][d], gate/up interleaved by 32 rows (bf16: blocked MFMA layout;
                   // fp8: E4M3 codes in the fp8 blocked layout)
@@ -73,6 +73,7 @@ struct colibri_moe {
     hipEvent_t ev[kStages + 1];
     int group_n_gu, group_n_dn;  // tile order of the grouped GEMMs (n-tiles per group)
     int order_m_rows;            // m-tile groups when the mean rows per expert are at most this
+    int xcd_map;                 // bit 0: gate/up, bit 1: down GEMM with XCD-contiguous tile placement
     bool fuse_combine;  // bf16 tiled path: combine in the down GEMM's epilogue
     int cus;        // compute units of the device (persistent GEMM grid)
     int dec_max_a;  // bf16 calls with T*k <= dec_max_a take the small-batch path
@@ -258,7 +259,7 @@ colibri_moe_status_t init_impl(colibri_moe* h, const colibri_moe_weights_t* w)
     const size_t d = c.d_model, f = c.d_ff, E = c.n_experts;
 
     Carver cv;
-    const size_t o_wrt = cv.take(E * d * es);
+    const size_t o_wrt = cv.take(router_weight_bytes((int)d, (int)E, (int)es));
     const size_t o_br = cv.take(E * sizeof(float));
     const size_t wes = h->fp8 ? 1 : es;  // bytes per stored expert weight
     const size_t o_wgu = cv.take(E * 2 * f * d * wes);
@@ -359,6 +360,7 @@ colibri_moe_status_t colibri_moe_init(colibri_moe_t** out, const colibri_moe_con
     // one XCD (groups of 8 m-tiles) instead. Chosen per call from the mean
     // rows per expert (threshold CMOE_M_ORDER_ROWS, 0 = never).
     h->order_m_rows = env_int("CMOE_M_ORDER_ROWS", 384, 0, 1 << 30);
+    h->xcd_map = env_int("CMOE_XCD_MAP", 0, 0, 3);
     // Combine fused into the down GEMM's epilogue (bf16 layers, tiled path)
     // with CMOE_FUSE_COMBINE=1; the default runs the combine kernel, which is
     // faster here: the fused form needs device-scope release/acquire fences
@@ -465,6 +467,7 @@ colibri_moe_status_t forward_impl(colibri_moe* h, const void* x, int32_t T, void
         const bool order_m = (int64_t)A <= (int64_t)h->order_m_rows * c.n_experts;
         GemmArgs gu{q8 ? (const void*)ws.xq : x, h->w_gu, h->s_gu, q8 ? ws.xsc : nullptr, ws.H, offsets, perm, A,
                     c.n_experts, c.top_k, c.d_model, c.d_ff, order_m ? -8 : h->group_n_gu, 1, h->cus};
+        gu.xcd_map = h->xcd_map & 1;
         CMOE_HIP(bf ? launch_gate_up_bf16(gu, s) : launch_gate_up_f32(gu, s));
         if (tm) {
             CMOE_HIP(hipEventRecord(h->ev[3], s));
@@ -483,6 +486,7 @@ colibri_moe_status_t forward_impl(colibri_moe* h, const void* x, int32_t T, void
         // Without a K split the expert outputs go to Ys as bf16 rows (bf16
         // weights).
         dn.ys_bf16 = bf && !h->fp8 && split == 1 && !fused;
+        dn.xcd_map = (h->xcd_map >> 1) & 1;
         ys_bf16 = dn.ys_bf16;
         CMOE_HIP(bf ? launch_down_bf16(dn, s) : launch_down_f32(dn, s));
     }

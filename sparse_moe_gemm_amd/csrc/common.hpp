@@ -64,7 +64,7 @@ __device__ __forceinline__ float silu(float z)
 
 struct RouterArgs {
     const void* x;      // [T][d] dtype
-    const void* w_rt;   // router weights transposed: [E][d] dtype
+    const void* w_rt;   // router weights: bf16 blocked (router_weight_bytes), fp32 [E][d]
     const float* b;     // [E] fp32 (never NULL: zeros when the caller gave none)
     int T, d, E, k;
     float* logits;      // [T][E] (may be NULL)
@@ -122,6 +122,10 @@ struct GemmArgs {
     // down GEMM with split == 1, without the fused combine: out is [A][d] bf16
     // (each expert output row rounded to nearest even) instead of fp32
     int ys_bf16;
+    // tile placement (tiles.hpp tile_index): 0 = consecutive tiles to the 8
+    // XCDs in turn; 1 = each XCD runs one contiguous eighth of the tile order
+    // (the launch's grid must then be a multiple of 8)
+    int xcd_map;
 };
 hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t s);
 hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t s);
@@ -187,6 +191,12 @@ struct CombineArgs {
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
 // Init-time weight repacks.
+// Router weights as the router kernels read them, from the caller's [d][E]
+// matrix: fp32 layers [E][d] (transposed); bf16 layers in MFMA operand blocks,
+// for each group of 16 experts and 32-wide K step one 1 KiB block in which
+// lane l's 8 values (expert 16g + l%16, k = 32s + 8(l/16) .. +8) sit at
+// l*16 bytes; experts past E are zero rows.
+size_t router_weight_bytes(int d, int E, int esize);
 hipError_t launch_transpose_router(const void* w_r, void* w_rt, int d, int E, int esize, hipStream_t s);
 hipError_t launch_interleave_gate_up(const void* wg, const void* wu, void* wgu, int E, int f, int d,
                                      int esize, hipStream_t s);

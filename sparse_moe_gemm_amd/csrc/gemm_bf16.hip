@@ -825,9 +825,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     TileTable tt;
     const int total = make_table<BM, SM>(g.offsets, g.E, lane, NT * S, tt);
     int L = blockIdx.x;
-    if (L >= total)
-        return;
     const int GRID = gridDim.x;
+    const bool xm = g.xcd_map != 0;
+    const int t0 = tile_index(L, total, xm);
+    if (t0 < 0)
+        return;
 
     // Per-lane slot rows and swizzled chunk byte offsets of this wave's A loads.
     const uint32_t Kbytes = (uint32_t)K * (Q8 ? 1u : 2u);
@@ -842,14 +844,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const i32x4 ra = make_rsrc(g.a, a_rows * Kbytes);
     const uint32_t lane16 = (uint32_t)lane * 16u;
 
-    Tile cur = decode<BM, SM>(tt, L, NT, S, g.group_n, KT);
+    Tile cur = decode<BM, SM>(tt, t0, NT, S, g.group_n, KT);
     LoadSrc<A_INS> cs;
     cs.rb = panel_rsrc<BN>(g.b, cur, N, KB);
     cs.kt = cur.kt0;
 #pragma unroll
     for (int i = 0; i < A_INS; ++i)
         cs.aoff[i] = (uint32_t)row_src<GATE_UP>(g.perm, cur, slot[i]) * Kbytes + cpart[i];
-    bool has_nxt = L + GRID < total;
+    const int t1 = tile_index(L + GRID, total, xm);
+    bool has_nxt = t1 >= 0;
     Tile nxt = cur;
     i32x4 nrb = cs.rb;
     uint32_t held[A_INS];
@@ -857,7 +860,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     for (int i = 0; i < A_INS; ++i)
         held[i] = 0;
     if (has_nxt) {
-        nxt = decode<BM, SM>(tt, L + GRID, NT, S, g.group_n, KT);
+        nxt = decode<BM, SM>(tt, t1, NT, S, g.group_n, KT);
         nrb = panel_rsrc<BN>(g.b, nxt, N, KB);
 #pragma unroll
         for (int i = 0; i < A_INS; ++i)
@@ -1008,7 +1011,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         // epilogue (below); loads complete in issue order, so the wait the
         // compiler puts there also covers the loads of the next tile's first
         // stages, which have had the whole epilogue to land.
-        const bool has_nn = has_nxt && L + 2 * GRID < total;
+        const int t2 = has_nxt ? tile_index(L + 2 * GRID, total, xm) : -1;
+        const bool has_nn = t2 >= 0;
         Tile nn = nxt;
         i32x4 nnrb = nrb;
         uint32_t nheld[A_INS];
@@ -1016,7 +1020,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         for (int i = 0; i < A_INS; ++i)
             nheld[i] = held[i];
         if (has_nn) {
-            nn = decode<BM, SM>(tt, L + 2 * GRID, NT, S, g.group_n, KT);
+            nn = decode<BM, SM>(tt, t2, NT, S, g.group_n, KT);
             nnrb = panel_rsrc<BN>(g.b, nn, N, KB);
 #pragma unroll
             for (int i = 0; i < A_INS; ++i)
@@ -1350,37 +1354,44 @@ hipError_t launch_grouped(const GemmArgs& a, hipStream_t s)
     const int N = GATE_UP ? 2 * a.f : a.d;
     const int S = GATE_UP ? 1 : a.split;
     const int BN = N % 256 == 0 ? 256 : 128;
-    const int64_t bound = ((int64_t)a.A_max / kBM + a.E) * (N / BN) * S;  // tiles, upper bound
+    int64_t bound = ((int64_t)a.A_max / kBM + a.E) * (N / BN) * S;  // tiles, upper bound
+    // XCD-contiguous placement needs every workgroup's indices on one XCD:
+    // a grid that is a multiple of 8.
+    const bool xm = a.xcd_map != 0 && a.grid % 8 == 0;
+    if (xm)
+        bound = (bound + 7) / 8 * 8;
     const int grid = (int)(bound < a.grid ? bound : a.grid);
     if (grid <= 0)
         return hipSuccess;
+    GemmArgs ga = a;
+    ga.xcd_map = xm ? 1 : 0;
     if constexpr (GATE_UP) {
         // 2 * d_ff is a multiple of 256 (d_ff % 128 == 0 is checked at init)
         hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 256, 128, 128, true, F8, Q8>), dim3(grid), dim3(kThreads), 0,
-                           s, a);
+                           s, ga);
     } else if (a.cnt != nullptr) {
         if (BN == 256)
             hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 256, 128, 128, false, F8, Q8, true>), dim3(grid),
-                               dim3(kThreads), 0, s, a);
+                               dim3(kThreads), 0, s, ga);
         else
             hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 128, 128, 64, false, F8, Q8, true>), dim3(grid),
-                               dim3(kThreads), 0, s, a);
+                               dim3(kThreads), 0, s, ga);
     } else if (a.ys_bf16) {
         if constexpr (!Q8 && !F8) {
             if (BN == 256)
                 hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 256, 128, 128, false, F8, Q8, false, true>), dim3(grid),
-                                   dim3(kThreads), 0, s, a);
+                                   dim3(kThreads), 0, s, ga);
             else
                 hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 128, 128, 64, false, F8, Q8, false, true>), dim3(grid),
-                                   dim3(kThreads), 0, s, a);
+                                   dim3(kThreads), 0, s, ga);
         }
     } else {
         if (BN == 256)
             hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 256, 128, 128, false, F8, Q8>), dim3(grid), dim3(kThreads),
-                               0, s, a);
+                               0, s, ga);
         else
             hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 128, 128, 64, false, F8, Q8>), dim3(grid), dim3(kThreads),
-                               0, s, a);
+                               0, s, ga);
     }
     return hipGetLastError();
 }

@@ -37,12 +37,34 @@ __device__ __forceinline__ uint32_t order_key(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inverse of order_key (a -0 logit comes back as +0, which compares equal).
+__device__ __forceinline__ float key_value(uint32_t key)
+{
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// One step of the wave maximum: v and the value of the lane that the DPP
+// control CTRL names (lanes outside ROW_MASK, or without a source lane, take
+// 0, the smallest key).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v)
+{
+    return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false));
+}
+
+// Largest v over the wave, in a scalar register: within each row of 16 lanes
+// by swaps of neighbours, of quads and of half rows, then across the rows by
+// the row broadcasts of lane 15 and lane 31, so that lane 63 holds the
+// maximum. (DPP moves data between lanes without an LDS round trip.)
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        v = max(v, (uint32_t)__shfl_xor((int)v, off, kWave));
-    return v;
+    v = dpp_max<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+    v = dpp_max<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+    v = dpp_max<0x141, 0xF>(v);  // row_half_mirror
+    v = dpp_max<0x140, 0xF>(v);  // row_mirror: every lane holds its row's maximum
+    v = dpp_max<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v = dpp_max<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // Top-k + softmax for the block's bt tokens, reading logits (bias included)
@@ -78,7 +100,7 @@ __device__ void topk_softmax_epilogue(const float* lg, int ldl, int bt, int t0, 
                     e = q * kWave + __builtin_ctzll(m);
             }
             isel[j] = e;
-            lsel[j] = lg[r * ldl + e];
+            lsel[j] = key_value(best);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 if (lane + q * kWave == e)
@@ -140,10 +162,10 @@ __global__ __launch_bounds__(W * kWave) void router_bf16_kernel(RouterArgs a)
 #pragma unroll
     for (int g = 0; g < TG; ++g)
         xr[g] = (const uint16_t*)a.x + (int64_t)min(t0 + g * kTok + (lane & 15), a.T - 1) * d + kq;
-    const uint16_t* wr[NG];
-#pragma unroll
-    for (int n = 0; n < NG; ++n)
-        wr[n] = (const uint16_t*)a.w_rt + (int64_t)min(n * 16 + (lane & 15), a.E - 1) * d + kq;
+    // Router weights in MFMA operand blocks: the fragment of expert group n at
+    // K step s is the 1 KiB block n * steps + s, lane l's 16 bytes at l*16.
+    const int steps = d / 32;
+    const Vec16* wb = (const Vec16*)a.w_rt + lane;
 
     floatx4 acc[TG][NG];
 #pragma unroll
@@ -159,18 +181,17 @@ __global__ __launch_bounds__(W * kWave) void router_bf16_kernel(RouterArgs a)
     // load is unconditional: a step under a branch lets the compiler move its
     // loads into the branch and wait for each of them there.
     constexpr int U = NG * TG >= 8 ? 1 : 8 / (NG * TG);
-    const int steps = d / 32;
     for (int s0 = wv; s0 < steps; s0 += W * U) {
         Vec16 av[U][TG], bv[U][NG];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int k0 = min(s0 + W * u, steps - 1) * 32;
+            const int st = min(s0 + W * u, steps - 1);
 #pragma unroll
             for (int g = 0; g < TG; ++g)
-                av[u][g] = *(const Vec16*)(xr[g] + k0);
+                av[u][g] = *(const Vec16*)(xr[g] + st * 32);
 #pragma unroll
             for (int n = 0; n < NG; ++n)
-                bv[u][n] = *(const Vec16*)(wr[n] + k0);
+                bv[u][n] = wb[(int64_t)(n * steps + st) * kWave];
         }
         __builtin_amdgcn_sched_barrier(0);  // all loads of the batch first
 #pragma unroll
@@ -267,6 +288,28 @@ __global__ void transpose_router_kernel(const uint8_t* src, uint8_t* dst, int d,
     }
 }
 
+// Groups of 16 experts the bf16 router kernel multiplies (its NG).
+int router_groups(int E)
+{
+    return E <= 16 ? 1 : E <= 32 ? 2 : E <= 64 ? 4 : E <= 128 ? 8 : 16;
+}
+
+// bf16 router weights [d][E] -> MFMA operand blocks for router_groups(E)
+// groups of 16 experts (the layout router_weight_bytes sizes).
+__global__ void block_router_kernel(const uint16_t* src, uint16_t* dst, int d, int E, int groups)
+{
+    const int steps = d / 32;
+    const int64_t n = (int64_t)groups * steps * 512;
+    for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < n;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int j = (int)(idx & 7), lane = (int)((idx >> 3) & 63);
+        const int64_t blk = idx >> 9;
+        const int st = (int)(blk % steps), g = (int)(blk / steps);
+        const int e = g * 16 + (lane & 15), i = st * 32 + (lane >> 4) * 8 + j;
+        dst[idx] = e < E ? src[(int64_t)i * E + e] : (uint16_t)0;
+    }
+}
+
 template <int NG, int TG>
 hipError_t launch_router_tg(const RouterArgs& a, hipStream_t s)
 {
@@ -295,15 +338,19 @@ hipError_t launch_router_ng(const RouterArgs& a, hipStream_t s)
 
 hipError_t launch_router_bf16(const RouterArgs& a, hipStream_t s)
 {
-    if (a.E <= 16)
+    // NG = router_groups(E): the weight blocks hold exactly that many groups
+    switch (router_groups(a.E)) {
+    case 1:
         return launch_router_ng<1>(a, s);
-    if (a.E <= 32)
+    case 2:
         return launch_router_ng<2>(a, s);
-    if (a.E <= 64)
+    case 4:
         return launch_router_ng<4>(a, s);
-    if (a.E <= 128)
+    case 8:
         return launch_router_ng<8>(a, s);
-    return launch_router_ng<16>(a, s);
+    default:
+        return launch_router_ng<16>(a, s);
+    }
 }
 
 hipError_t launch_router_f32(const RouterArgs& a, hipStream_t s)
@@ -312,10 +359,19 @@ hipError_t launch_router_f32(const RouterArgs& a, hipStream_t s)
     return hipGetLastError();
 }
 
+size_t router_weight_bytes(int d, int E, int esize)
+{
+    return esize == 2 ? (size_t)router_groups(E) * 16 * d * 2 : (size_t)E * d * esize;
+}
+
 hipError_t launch_transpose_router(const void* w_r, void* w_rt, int d, int E, int esize, hipStream_t s)
 {
-    hipLaunchKernelGGL(transpose_router_kernel, dim3(256), dim3(256), 0, s, (const uint8_t*)w_r,
-                       (uint8_t*)w_rt, d, E, esize);
+    if (esize == 2)
+        hipLaunchKernelGGL(block_router_kernel, dim3(256), dim3(256), 0, s, (const uint16_t*)w_r, (uint16_t*)w_rt,
+                           d, E, router_groups(E));
+    else
+        hipLaunchKernelGGL(transpose_router_kernel, dim3(256), dim3(256), 0, s, (const uint8_t*)w_r,
+                           (uint8_t*)w_rt, d, E, esize);
     return hipGetLastError();
 }
 

@@ -87,6 +87,25 @@ __device__ __forceinline__ int make_table(const int32_t* offsets, int E, int lan
     return t.tiles[0] + t.tiles[1];
 }
 
+// Tile behind launch index L, or -1 for none. Workgroups go to the 8 XCDs
+// round robin and a persistent workgroup takes indices L, L + grid, ..., so
+// index L runs on XCD L % 8. Plain placement (xm false): tile L, so tiles
+// next to each other in the order run on different XCDs. XCD-contiguous
+// placement (xm true, grid a multiple of 8): XCD x runs the x-th eighth of
+// the tile order, in order, so the tiles that share an m-tile's token rows
+// or an expert's weight panel run on one XCD, close together in time, and
+// read that data into its L2 once. Each workgroup's indices stay on its XCD
+// and map to increasing tiles, so it stops at its first -1.
+__device__ __forceinline__ int tile_index(int L, int total, bool xm)
+{
+    if (!xm)
+        return L < total ? L : -1;
+    const int q = total >> 3, r = total & 7, x = L & 7, i = L >> 3;
+    if (i >= q + (x < r ? 1 : 0))
+        return -1;
+    return x * q + min(x, r) + i;
+}
+
 struct Tile {
     int e, m, n, s;
     int row0, rows;  // first sorted row and valid rows of the m-tile

@@ -52,6 +52,7 @@ WORKLOAD_NAMES = {
     "skewed-masked": "skewed-64e-top2-20-empty",
     "tiny-f32": "tiny-f32",
     "dense": "dense-single-expert",
+    "square": "square-gemm-8192",
 }
 DEFAULT_WORKLOADS = ("mixtral", "fine-grained", "decode", "skewed", "skewed-masked")
 HEADLINE = "mixtral"
@@ -72,34 +73,109 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens of the oracle sample (0 = sized to ~15 s of CPU work)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only measure attainable rates (the library's stream copy, its grouped GEMM on one expert "
+                         "at square and dense shapes, torch.matmul beside it for reference) and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (to scale HBM counters) and exit")
     return ap.parse_args()
 
 
 def copy_calibration(mib: int):
-    """A plain device-to-device copy of known size: its FETCH_SIZE / WRITE_SIZE
-    readings give the factor between those counters and bytes moved. Also
-    reports the copy's rate (bytes read + written per second), an attainable
-    HBM figure next to the 8 TB/s nominal one."""
+    """A device-to-device copy of known size with the library's own streaming
+    copy kernel: its FETCH_SIZE / WRITE_SIZE readings give the factor between
+    those counters and bytes moved, and its rate (bytes read + written per
+    second) is the attainable HBM figure stated next to the 8 TB/s nominal
+    one. torch's own copy is timed beside it."""
     import torch
+    import sparse_moe_gemm_amd as cm
 
     n = mib * (1 << 20) // 4
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for _ in range(10):
-        dst.copy_(src)
-    ev1.record()
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / 10
-    print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 13,
-                      "copy_gbs_read_plus_write": 2 * n * 4 / (ms * 1e-3) / 1e9, "copy_ms": ms}), flush=True)
+
+    def rate(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(10):
+            fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / 10
+
+    ms = rate(lambda: cm.stream_copy(src, dst))
+    ms_torch = rate(lambda: dst.copy_(src))
+    print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 13, "kernel": "stream_copy_kernel",
+                      "copy_gbs_read_plus_write": 2 * n * 4 / (ms * 1e-3) / 1e9, "copy_ms": ms,
+                      "torch_copy_gbs_read_plus_write": 2 * n * 4 / (ms_torch * 1e-3) / 1e9}), flush=True)
+
+
+def peaks(args):
+    """Attainable rates on this GPU next to the nominal peaks: the library's
+    streaming copy (bytes read + written per second, 2 GiB), and its grouped
+    GEMM with every token on one expert, so that the gate/up GEMM is one
+    plain dense product, at M = N = K = 8192 and at 8192 x 28672 x 4096 (the
+    Mixtral gate/up shape with all 8192 rows on one expert). torch.matmul on
+    the same bf16 shapes (a vendor library GEMM, not part of this library) is
+    timed beside it for reference. Kernel times are the layer's own stage
+    events (median of K forwards)."""
+    import torch
+
+    import synth
+    import sparse_moe_gemm_amd as cm
+
+    out = {"nominal": {"bf16_mfma_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}}
+    n = (2 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+
+    def timed(fn, reps=10):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out["stream_copy_gbs"] = 2 * n * 4 / (timed(lambda: cm.stream_copy(src, dst)) * 1e-3) / 1e9
+    out["torch_copy_gbs"] = 2 * n * 4 / (timed(lambda: dst.copy_(src)) * 1e-3) / 1e9
+    del src, dst
+    gemms = {}
+    for name in ("square", "dense"):
+        cfg = synth.CONFIGS[name]
+        inp = synth.make_inputs(cfg)
+        wts = [to_dev(inp[k]) for k in ("w_router", "b_router", "w_gate", "w_up", "w_down")]
+        x = to_dev(inp["x"])
+        y = torch.empty_like(x)
+        layer = cm.MoELayer(*wts, cfg.k, max_tokens=cfg.T, flags=cm.FLAG_ASYNC | cm.FLAG_STAGE_TIMING)
+        for _ in range(args.warmup):
+            layer.forward(x, y)
+        ts = []
+        for _ in range(args.steps):
+            layer.forward(x, y)
+            ts.append(layer.stage_times()["gate_up_gemm"])
+        layer.close()
+        M, N, K = cfg.T, 2 * cfg.f, cfg.d
+        flop = 2.0 * M * N * K
+        ours = float(np.median(ts))
+        a = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+        b = torch.randn(K, N, device="cuda").to(torch.bfloat16)
+        ref = timed(lambda: torch.matmul(a, b))
+        gemms[f"{M}x{N}x{K}"] = {"library_gate_up_ms": ours, "library_tflops": flop / (ours * 1e-3) / 1e12,
+                                 "torch_matmul_ms": ref, "torch_matmul_tflops": flop / (ref * 1e-3) / 1e12}
+        del a, b, x, y, wts
+        torch.cuda.empty_cache()
+    out["gemm_bf16"] = gemms
+    print(json.dumps(out), flush=True)
 
 
 def to_dev(a):
@@ -364,6 +440,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.peaks:
+        peaks(args)
         return
     names = list(DEFAULT_WORKLOADS) if args.workloads == "all" else args.workloads.split(",")
     for n in names:

@@ -186,6 +186,16 @@ colibri_moe_status_t colibri_moe_free(colibri_moe_t* h);
 colibri_moe_status_t colibri_moe_quantize_fp8(const void* w, int64_t rows, int64_t cols, uint8_t* codes,
                                               float* scales, void* hip_stream);
 
+/* Measurement helper, not a step of the layer: copies `bytes` bytes from src
+ * to dst (caller-owned DEVICE buffers, 16-byte aligned, not overlapping;
+ * bytes a multiple of 16, at least 16) with the library's streaming copy
+ * kernel on hip_stream (NULL = default stream), and returns without waiting
+ * (time it with events on that stream). It states the HBM rate the chip
+ * reaches on plain streaming traffic beside the nominal peak, and a copy of
+ * known size scales the rocprofv3 byte counters. INVALID_ARG or ALIGNMENT
+ * otherwise; HIP if the launch fails. Needs no handle. */
+colibri_moe_status_t colibri_moe_stream_copy(const void* src, void* dst, int64_t bytes, void* hip_stream);
+
 /* Static text for a status value. */
 const char* colibri_moe_status_string(colibri_moe_status_t s);
 

@@ -43,7 +43,7 @@ class Routing(ctypes.Structure):
 
 EXPORTS = ("colibri_moe_init", "colibri_moe_forward", "colibri_moe_forward_static", "colibri_moe_free",
            "colibri_moe_status_string", "colibri_moe_stage_times", "colibri_moe_stage_name",
-           "colibri_moe_quantize_fp8")
+           "colibri_moe_quantize_fp8", "colibri_moe_stream_copy")
 
 _lib = None
 
@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.colibri_moe_stage_name.argtypes = [i32]
         L.colibri_moe_quantize_fp8.restype = ctypes.c_int
         L.colibri_moe_quantize_fp8.argtypes = [P, ctypes.c_int64, ctypes.c_int64, P, P, P]
+        L.colibri_moe_stream_copy.restype = ctypes.c_int
+        L.colibri_moe_stream_copy.argtypes = [P, P, ctypes.c_int64, P]
         _lib = L
     return _lib
 
@@ -141,6 +143,27 @@ def quantize_fp8(w, stream=None):
     if st != OK:
         raise ColibriError("colibri_moe_quantize_fp8", st)
     return codes, scales
+
+
+def colibri_moe_stream_copy(src_ptr: int, dst_ptr: int, nbytes: int, hip_stream: int = 0) -> int:
+    return lib().colibri_moe_stream_copy(ctypes.c_void_p(src_ptr), ctypes.c_void_p(dst_ptr), nbytes,
+                                         ctypes.c_void_p(hip_stream))
+
+
+def stream_copy(src, dst, stream=None):
+    """dst <- src with the library's streaming copy kernel (measurement only):
+    contiguous device tensors of the same byte size, a multiple of 16."""
+    import torch
+
+    if not (src.is_cuda and dst.is_cuda and src.is_contiguous() and dst.is_contiguous()):
+        raise TypeError("src and dst must be contiguous device tensors")
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("src and dst differ in size")
+    s = stream if stream is not None else torch.cuda.current_stream()
+    st = colibri_moe_stream_copy(src.data_ptr(), dst.data_ptr(), n, s.cuda_stream)
+    if st != OK:
+        raise ColibriError("colibri_moe_stream_copy", st)
 
 
 class ColibriError(RuntimeError):

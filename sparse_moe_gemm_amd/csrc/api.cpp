@@ -598,6 +598,25 @@ colibri_moe_status_t colibri_moe_quantize_fp8(const void* w, int64_t rows, int64
     return COLIBRI_MOE_OK;
 }
 
+colibri_moe_status_t colibri_moe_stream_copy(const void* src, void* dst, int64_t bytes, void* hip_stream)
+{
+    if (!src || !dst || bytes < 16 || bytes % 16 != 0)
+        return COLIBRI_MOE_ERR_INVALID_ARG;
+    if (!aligned16(src) || !aligned16(dst))
+        return COLIBRI_MOE_ERR_ALIGNMENT;
+    const uint8_t *s0 = (const uint8_t*)src, *d0 = (const uint8_t*)dst;
+    if (s0 < d0 + bytes && d0 < s0 + bytes)
+        return COLIBRI_MOE_ERR_INVALID_ARG;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                hipSuccess || cus <= 0) {
+        (void)hipGetLastError();
+        return COLIBRI_MOE_ERR_HIP;
+    }
+    CMOE_HIP(launch_stream_copy(src, dst, bytes, cus, (hipStream_t)hip_stream));
+    return COLIBRI_MOE_OK;
+}
+
 const char* colibri_moe_status_string(colibri_moe_status_t s)
 {
     switch (s) {

@@ -197,6 +197,8 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 // lane l's 8 values (expert 16g + l%16, k = 32s + 8(l/16) .. +8) sit at
 // l*16 bytes; experts past E are zero rows.
 size_t router_weight_bytes(int d, int E, int esize);
+// Measurement only (stream_copy.hip): dst = src, bytes a multiple of 16.
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, int cus, hipStream_t s);
 hipError_t launch_transpose_router(const void* w_r, void* w_rt, int d, int E, int esize, hipStream_t s);
 hipError_t launch_interleave_gate_up(const void* wg, const void* wu, void* wgu, int E, int f, int d,
                                      int esize, hipStream_t s);

@@ -140,6 +140,8 @@ CONFIGS = {
     # one expert takes every token: the expert GEMMs are plain dense GEMMs
     # (gate/up 8192 x 28672 x 4096), a reference point for the grouped kernel
     "dense": LayerConfig("dense", 8192, 4096, 1, 1, 14336, "bf16"),
+    # square GEMM for the attainable-MFMA record: gate/up is 8192 x 8192 x 8192
+    "square": LayerConfig("square", 8192, 8192, 1, 1, 4096, "bf16"),
 }
 
 

@@ -123,3 +123,18 @@ def test_binding_is_marshalling_only():
 ])
 def test_quantize_fp8_rejects_bad_arguments(args, status):
     assert cm.colibri_moe_quantize_fp8(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, FAKE + 4096, 64), cm.ERR_INVALID_ARG),
+    ((FAKE, None, 64), cm.ERR_INVALID_ARG),
+    ((FAKE, FAKE + 4096, 0), cm.ERR_INVALID_ARG),
+    ((FAKE, FAKE + 4096, 24), cm.ERR_INVALID_ARG),
+    ((FAKE, FAKE + 32, 64), cm.ERR_INVALID_ARG),   # overlapping ranges
+    ((FAKE + 32, FAKE, 64), cm.ERR_INVALID_ARG),
+    ((FAKE + 8, FAKE + 4096, 64), cm.ERR_ALIGNMENT),
+    ((FAKE, FAKE + 4100, 64), cm.ERR_ALIGNMENT),
+])
+def test_stream_copy_rejects_bad_arguments(args, status):
+    # Checked before anything reaches the device (no GPU here).
+    assert cm.colibri_moe_stream_copy(*args) == status

@@ -4,7 +4,7 @@ correct fp32 computations of the logits) and the routing weights of given
 experts (used to check the GPU's weights on every token, whichever experts it
 picked).
 
-The rule (the benchmark spec; reading c3): a token's sorted fp32 logits l_(0) >= l_(1)
+The comparison rule for expert ids: a token's sorted fp32 logits l_(0) >= l_(1)
 >= ... are near-tied at position i when l_(i) - l_(i+1) < 1e-5 * max(|l_(i)|,
 |l_(i+1)|). near_tie_tokens flags a near tie anywhere among the first k+1
 (slot order inside the top k, or the k-th / (k+1)-th boundary);

@@ -261,3 +261,26 @@ def test_full_size_workload(name):
         assert np.all(g["expert_counts"] > 0), "every expert is hit in the decode batch"
     if name == "skewed-masked":
         assert rep["empty_experts"] == 20
+
+
+PLACEMENT = [SMALL[1], SMALL[2], SMALL[5], SMALL[-2]]  # mixtral-, fine-grained-, skewed-masked-small, small-among-big
+
+
+@pytest.mark.parametrize("cfg", PLACEMENT, ids=[c.name for c in PLACEMENT])
+def test_xcd_contiguous_placement(cfg, monkeypatch):
+    """CMOE_XCD_MAP=3 (read at init) gives each XCD one contiguous eighth of
+    both GEMMs' tile orders. Placement changes which workgroup runs a tile,
+    not how a tile sums, so every output is bit-identical to the default
+    placement's, and both match the oracle."""
+    inp = synth.make_inputs(cfg)
+    print(f"xcd placement {cfg}", flush=True)
+    plain = make_layer(cfg, inp)
+    g0 = run_gpu(plain, inp["x"])
+    plain.close()
+    monkeypatch.setenv("CMOE_XCD_MAP", "3")
+    placed = make_layer(cfg, inp)
+    g1 = run_gpu(placed, inp["x"])
+    placed.close()
+    for key in g0:
+        assert np.array_equal(g0[key], g1[key]), key
+    compare(cfg, inp, g1)

@@ -36,7 +36,7 @@ namespace cmoe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kP = 6;  // k-steps of loads in flight per wave
+constexpr int kP = 4;  // k-steps of loads in flight per wave and register set (two sets)
 
 template <bool GATE_UP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_gemm_kernel(DecodeArgs g)

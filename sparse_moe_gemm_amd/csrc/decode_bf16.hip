@@ -20,9 +20,11 @@
 // K slices split every expert's weights into many equal, independent items,
 // which keeps all compute units streaming. Weights are read with
 // non-temporal loads: each is used once per call, and not keeping them in
-// the caches streams them ~5-7% faster. For gate/up a second kernel sums
-// the slices and applies SiLU(g)*u into H; for down the slices are the Ys
-// partials that combine already sums.
+// the caches streams them ~5-7% faster. For gate/up with bf16 weights the
+// items take the whole K (no slices) and apply SiLU(g)*u to their own sums,
+// writing H directly; with 8-bit weights a second kernel sums the slices and
+// applies SiLU(g)*u into H. For down the slices are the Ys partials that
+// combine already sums.
 // With 8-bit expert weights (E4M3 codes in the fp8 blocked layout, one scale
 // per weight row) the same items step through K 32 at a time: per step and
 // weight block one 1 KiB block of codes (one 16-byte load per lane: its B
@@ -111,12 +113,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                         acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1[i]), as_bf16x8(c1[i]), acc1, 0, 0, 0);
                     }
             }
+            if (gate_up && g.h != nullptr) {
+                // whole K in this item (no slices): blocks nb and nb+1 are the
+                // gate and up rows of H columns 16*nb .. +32
+                uint16_t* hcol = g.h + nb * 16 + (lane & 31);
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int row = r0 + 8 * (q / 4) + 4 * (lane >> 5) + (q % 4);
-                if (row < cnt) {
-                    out[(int64_t)(seg0 + row) * N] = acc0[q];
-                    out[(int64_t)(seg0 + row) * N + 32] = acc1[q];
+                for (int q = 0; q < 16; ++q) {
+                    const int row = r0 + 8 * (q / 4) + 4 * (lane >> 5) + (q % 4);
+                    if (row < cnt)
+                        hcol[(int64_t)(seg0 + row) * g.f] = f32_to_bf16_bits(silu(acc0[q]) * acc1[q]);
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int row = r0 + 8 * (q / 4) + 4 * (lane >> 5) + (q % 4);
+                    if (row < cnt) {
+                        out[(int64_t)(seg0 + row) * N] = acc0[q];
+                        out[(int64_t)(seg0 + row) * N + 32] = acc1[q];
+                    }
                 }
             }
         }
@@ -402,11 +416,14 @@ int decode_waves(int cus)
 
 int decode_split(int E, int N, int K, int kstep, int waves, int max_split)
 {
-    // Enough K slices for about two items (of two 32-row blocks) per wave, at
-    // least four k-steps each. (Fewer, longer items stream better than many
-    // short ones; two per wave leave room to balance the last round.)
+    // Enough K slices for about one item (of two 32-row blocks) per two
+    // waves, at least four k-steps each. Long items stream best: on the
+    // 8-expert decode layer (4096 x 14336) the gate/up GEMM without slices
+    // (1.75 items per wave) reads at 6.45 TB/s where two slices gave 6.0,
+    // and the down GEMM takes 146 us with 2 slices (half the waves busy),
+    // 147 with 4, 150 with 8 and 190 with 1.
     const int64_t blocks = (int64_t)E * (N / 64);
-    int64_t s = (2 * (int64_t)waves + blocks - 1) / blocks;
+    int64_t s = ((int64_t)waves + 2 * blocks - 1) / (2 * blocks);
     const int64_t cap = std::min<int64_t>(max_split, std::max(1, K / kstep / 4));
     s = std::max<int64_t>(1, std::min(s, cap));
     return (int)s;

@@ -74,7 +74,7 @@ struct colibri_moe {
     int group_n_gu, group_n_dn;  // tile order of the grouped GEMMs (n-tiles per group)
     int order_m_rows;            // m-tile groups when the mean rows per expert are at most this
     int xcd_map;                 // bit 0: gate/up, bit 1: down GEMM with XCD-contiguous tile placement
-    bool dec_fuse_silu;          // small-batch gate/up writes H itself (bf16 weights, no K slices)
+    bool dec_fuse_silu;          // small-batch gate/up writes H itself (no K slices)
     bool fuse_combine;  // bf16 tiled path: combine in the down GEMM's epilogue
     int cus;        // compute units of the device (persistent GEMM grid)
     int dec_max_a;  // bf16 calls with T*k <= dec_max_a take the small-batch path
@@ -392,10 +392,10 @@ colibri_moe_status_t colibri_moe_init(colibri_moe_t** out, const colibri_moe_con
         const int kstep_dn = h->fp8 ? 32 : 16;
         const int kstep_gu = h->q8 ? 64 : kstep_dn;
         h->dec_split_gu = cmoe::decode_split(cfg->n_experts, 2 * cfg->d_ff, cfg->d_model, kstep_gu, waves, 64);
-        // bf16 weights and no K slices: the gate/up items write H themselves
-        // (SiLU(g)*u in their epilogue) instead of partials for a separate
-        // sum pass (CMOE_DECODE_FUSE_SILU=0 keeps the pass)
-        h->dec_fuse_silu = !h->fp8 && h->dec_split_gu == 1 && env_int("CMOE_DECODE_FUSE_SILU", 1, 0, 1) != 0;
+        // No K slices: the gate/up items write H themselves (SiLU(g)*u in
+        // their epilogue) instead of partials for a separate sum pass
+        // (CMOE_DECODE_FUSE_SILU=0 keeps the pass)
+        h->dec_fuse_silu = h->dec_split_gu == 1 && env_int("CMOE_DECODE_FUSE_SILU", 1, 0, 1) != 0;
         h->dec_split_dn = cmoe::decode_split(cfg->n_experts, cfg->d_model, cfg->d_ff, kstep_dn, waves, 64);
     }
     st = init_impl(h, w);

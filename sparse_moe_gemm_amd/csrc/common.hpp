@@ -150,7 +150,7 @@ struct DecodeArgs {
     int A;                    // T*k of this call
     int E, d, f;
     int split;                // K slices
-    // gate/up, bf16 weights, split == 1: H [A][f] bf16 written directly as
+    // gate/up with split == 1: H [A][f] bf16 written directly as
     // SiLU(g)*u (no partials, no separate slice-sum pass); else null
     uint16_t* h;
 };

@@ -20,11 +20,10 @@
 // K slices split every expert's weights into many equal, independent items,
 // which keeps all compute units streaming. Weights are read with
 // non-temporal loads: each is used once per call, and not keeping them in
-// the caches streams them ~5-7% faster. For gate/up with bf16 weights the
-// items take the whole K (no slices) and apply SiLU(g)*u to their own sums,
-// writing H directly; with 8-bit weights a second kernel sums the slices and
-// applies SiLU(g)*u into H. For down the slices are the Ys partials that
-// combine already sums.
+// the caches streams them ~5-7% faster. A gate/up GEMM without K slices
+// applies SiLU(g)*u to its items' own sums and writes H directly; with slices
+// a second kernel sums them and applies SiLU(g)*u into H. For down the slices
+// are the Ys partials that combine already sums.
 // With 8-bit expert weights (E4M3 codes in the fp8 blocked layout, one scale
 // per weight row) the same items step through K 32 at a time: per step and
 // weight block one 1 KiB block of codes (one 16-byte load per lane: its B
@@ -39,6 +38,37 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kP = 4;  // k-steps of loads in flight per wave and register set (two sets)
+
+// Results of one item for its token group r0 .. r0+31 (32x32 MFMA D layout:
+// lane holds column lane%32 and rows 8*(q/4) + 4*(lane/32) + q%4): the fp32
+// slice partials of its two weight blocks at out (row stride N), or, for a
+// gate/up item that covers the whole K (g.h set, no slices), H itself: blocks
+// nb and nb+1 are the gate and up rows of H columns 16*nb .. +32, and
+// H = bf16(SiLU(g)*u), the same values the slice-sum pass computes from one
+// slice.
+template <bool GATE_UP>
+__device__ __forceinline__ void store_item(const DecodeArgs& g, float* out, int N, int seg0, int r0, int cnt, int nb,
+                                           int lane, const floatx16& acc0, const floatx16& acc1)
+{
+    if (GATE_UP && g.h != nullptr) {
+        uint16_t* hcol = g.h + nb * 16 + (lane & 31);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int row = r0 + 8 * (q / 4) + 4 * (lane >> 5) + (q % 4);
+            if (row < cnt)
+                hcol[(int64_t)(seg0 + row) * g.f] = f32_to_bf16_bits(silu(acc0[q]) * acc1[q]);
+        }
+        return;
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int row = r0 + 8 * (q / 4) + 4 * (lane >> 5) + (q % 4);
+        if (row < cnt) {
+            out[(int64_t)(seg0 + row) * N] = acc0[q];
+            out[(int64_t)(seg0 + row) * N + 32] = acc1[q];
+        }
+    }
+}
 
 template <bool GATE_UP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_gemm_kernel(DecodeArgs g)
@@ -113,26 +143,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                         acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1[i]), as_bf16x8(c1[i]), acc1, 0, 0, 0);
                     }
             }
-            if (gate_up && g.h != nullptr) {
-                // whole K in this item (no slices): blocks nb and nb+1 are the
-                // gate and up rows of H columns 16*nb .. +32
-                uint16_t* hcol = g.h + nb * 16 + (lane & 31);
-#pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int row = r0 + 8 * (q / 4) + 4 * (lane >> 5) + (q % 4);
-                    if (row < cnt)
-                        hcol[(int64_t)(seg0 + row) * g.f] = f32_to_bf16_bits(silu(acc0[q]) * acc1[q]);
-                }
-            } else {
-#pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int row = r0 + 8 * (q / 4) + 4 * (lane >> 5) + (q % 4);
-                    if (row < cnt) {
-                        out[(int64_t)(seg0 + row) * N] = acc0[q];
-                        out[(int64_t)(seg0 + row) * N + 32] = acc1[q];
-                    }
-                }
-            }
+            store_item<gate_up>(g, out, N, seg0, r0, cnt, nb, lane, acc0, acc1);
         }
     }
 }
@@ -237,14 +248,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                         }
                     }
             }
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int row = r0 + 8 * (q / 4) + 4 * (lane >> 5) + (q % 4);
-                if (row < cnt) {
-                    out[(int64_t)(seg0 + row) * N] = acc0[q];
-                    out[(int64_t)(seg0 + row) * N + 32] = acc1[q];
-                }
-            }
+            store_item<gate_up>(g, out, N, seg0, r0, cnt, nb, lane, acc0, acc1);
         }
     }
 }
@@ -360,14 +364,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                                                                                0, sa, 0, sb1);
                     }
             }
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int row = r0 + 8 * (q / 4) + 4 * (lane >> 5) + (q % 4);
-                if (row < cnt) {
-                    out[(int64_t)(seg0 + row) * N] = acc0[q];
-                    out[(int64_t)(seg0 + row) * N + 32] = acc1[q];
-                }
-            }
+            store_item<gate_up>(g, out, N, seg0, r0, cnt, nb, lane, acc0, acc1);
         }
     }
 }

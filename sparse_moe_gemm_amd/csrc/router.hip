@@ -13,7 +13,9 @@
 // the order of the logits, so exponentials are taken for the k winners only.
 //
 // bf16 path: the projection runs on v_mfma_f32_16x16x32_bf16 (16 tokens x 16
-// experts per MFMA); the 16 waves of a block (8 for more than 128 experts)
+// experts per MFMA; init stores the router weights as 1 KiB operand blocks,
+// one per 16 experts and 32-wide K step, so that each B fragment is one
+// contiguous load); the 16 waves of a block (8 for more than 128 experts)
 // split the reduction dimension in interleaved 32-wide steps and add their
 // partial sums through LDS in a fixed order, so results are bit-reproducible
 // and do not depend on the number of tokens in the call.
@@ -155,8 +157,9 @@ __global__ __launch_bounds__(W * kWave) void router_bf16_kernel(RouterArgs a)
     const int t0 = blockIdx.x * BT;
     const int d = a.d;
 
-    // Fragment rows: token rows for A, expert row for B (clamped: padded rows
-    // read valid memory and their results are dropped).
+    // A fragment rows: token rows, clamped (padded rows read valid memory and
+    // their results are dropped); B fragments: whole blocks of the blocked
+    // router weights (experts past E are zero rows there).
     const int kq = (lane >> 4) * 8;
     const uint16_t* xr[TG];
 #pragma unroll

@@ -74,6 +74,7 @@ struct colibri_moe {
     int group_n_gu, group_n_dn;  // tile order of the grouped GEMMs (n-tiles per group)
     int order_m_rows;            // m-tile groups when the mean rows per expert are at most this
     int xcd_map;                 // bit 0: gate/up, bit 1: down GEMM with XCD-contiguous tile placement
+    int k64;                     // bit 0: gate/up, bit 1: down GEMM on 64-wide K stages
     bool dec_fuse_silu;          // small-batch gate/up writes H itself (no K slices)
     bool fuse_combine;  // bf16 tiled path: combine in the down GEMM's epilogue
     int cus;        // compute units of the device (persistent GEMM grid)
@@ -347,13 +348,16 @@ colibri_moe_status_t colibri_moe_init(colibri_moe_t** out, const colibri_moe_con
     h->q8 = (cfg->flags & COLIBRI_MOE_FLAG_FP8_ACTIVATIONS) != 0;
     // Tile order of the grouped GEMMs (tuning only; results do not depend
     // on it): n-tiles per group, CMOE_GROUP_N for both GEMMs.
-    // Consecutive tiles go to the 8 XCDs in turn; with groups of 8 n-tiles
-    // each XCD takes one n-tile of a group for all of its m-tiles, so a weight
-    // panel is read into one XCD's L2 and reused there (gate/up 4-6% faster on
-    // 64 experts x 1408, the same elsewhere). The down GEMM keeps groups of
-    // 64 (measured 1-2% better there).
+    // Consecutive tiles go to the 8 XCDs in turn. With groups of 16 n-tiles
+    // each XCD takes two n-tiles of a group for all of its m-tiles, so a
+    // weight panel is read into one XCD's L2 and reused there, and each
+    // m-tile's token rows serve two tiles running side by side on that XCD.
+    // Measured with the gate/up GEMM's 64-wide K stages: one expert of 8192
+    // rows x 28672 x 4096 1.73 -> 1.47 ms against groups of 8, 4096 rows
+    // 798 -> 785 us, mixtral 1.70 -> 1.69 ms, the skewed shape unchanged.
+    // The down GEMM keeps groups of 64 (1-3% better there than 8 or 16).
     const int gn = env_int("CMOE_GROUP_N", 0, 0, 1 << 20);
-    h->group_n_gu = gn > 0 ? gn : 8;
+    h->group_n_gu = gn > 0 ? gn : 16;
     h->group_n_dn = gn > 0 ? gn : 64;
     // Many experts of one or two m-tiles each (fine-grained layers): token
     // rows are the data read again and again (once per n-tile), weight
@@ -362,6 +366,13 @@ colibri_moe_status_t colibri_moe_init(colibri_moe_t** out, const colibri_moe_con
     // rows per expert (threshold CMOE_M_ORDER_ROWS, 0 = never).
     h->order_m_rows = env_int("CMOE_M_ORDER_ROWS", 384, 0, 1 << 30);
     h->xcd_map = env_int("CMOE_XCD_MAP", 0, 0, 3);
+    // 64-wide K stages (grouped_gemm64_kernel) for the bf16 gate/up GEMM:
+    // 4-6% faster on layers of 512-2048 rows per expert (mixtral gate/up
+    // 1766 -> 1695 us), 4% slower only with 8192 rows on one expert; the down
+    // GEMM keeps 32-wide stages (up to 12% slower with 64). Same sums in the
+    // same order, so outputs are bit-identical either way. CMOE_K64: bit 0
+    // gate/up, bit 1 down.
+    h->k64 = env_int("CMOE_K64", 1, 0, 3);
     // Combine fused into the down GEMM's epilogue (bf16 layers, tiled path)
     // with CMOE_FUSE_COMBINE=1; the default runs the combine kernel, which is
     // faster here: the fused form needs device-scope release/acquire fences
@@ -475,6 +486,7 @@ colibri_moe_status_t forward_impl(colibri_moe* h, const void* x, int32_t T, void
         GemmArgs gu{q8 ? (const void*)ws.xq : x, h->w_gu, h->s_gu, q8 ? ws.xsc : nullptr, ws.H, offsets, perm, A,
                     c.n_experts, c.top_k, c.d_model, c.d_ff, order_m ? -8 : h->group_n_gu, 1, h->cus};
         gu.xcd_map = h->xcd_map & 1;
+        gu.k64 = h->k64 & 1;
         CMOE_HIP(bf ? launch_gate_up_bf16(gu, s) : launch_gate_up_f32(gu, s));
         if (tm) {
             CMOE_HIP(hipEventRecord(h->ev[3], s));
@@ -494,6 +506,7 @@ colibri_moe_status_t forward_impl(colibri_moe* h, const void* x, int32_t T, void
         // weights).
         dn.ys_bf16 = bf && !h->fp8 && split == 1 && !fused;
         dn.xcd_map = (h->xcd_map >> 1) & 1;
+        dn.k64 = (h->k64 >> 1) & 1;
         ys_bf16 = dn.ys_bf16;
         CMOE_HIP(bf ? launch_down_bf16(dn, s) : launch_down_f32(dn, s));
     }

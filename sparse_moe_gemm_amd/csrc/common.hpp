@@ -126,6 +126,9 @@ struct GemmArgs {
     // XCDs in turn; 1 = each XCD runs one contiguous eighth of the tile order
     // (the launch's grid must then be a multiple of 8)
     int xcd_map;
+    // bf16 weights, 256-row weight tiles, no fused combine: 1 runs the
+    // 64-wide K stage kernel (grouped_gemm64_kernel)
+    int k64;
 };
 hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t s);
 hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t s);

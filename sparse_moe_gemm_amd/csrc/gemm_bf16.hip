@@ -1278,6 +1278,402 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the trailing reloads
 }
 
+// ---------------------------------------------------------------------------
+// 64-wide K stages (bf16 weights, 16x16x32 MFMAs; selected with GemmArgs::k64).
+// The same persistent tile walk and 256x256 tiles on 4 waves of 128x128 as
+// grouped_gemm_kernel's M16 path, but each LDS stage holds 64 k: A rows of
+// 128 bytes (whole cache lines; one buffer->LDS load covers 8 rows) and four
+// 16-k weight blocks per 32 weight rows. Two 64 KiB stages form the ring, and
+// the gate/up and bf16-row epilogues stage through a 32 KiB buffer of their
+// own. Per stage and wave: 16 loads, 32 fragment reads, 128 MFMAs, one
+// barrier. Schedule of stage s (slot s%2):
+//   first half:  k-step 0 MFMAs (fragments read in stage s-1), reads of this
+//                stage's k-step 1 fragments;
+//   middle:      wait for every read and every load issued so far (stage
+//                s+1's, issued in stage s-1's second half), barrier;
+//   second half: k-step 1 MFMAs, reads of stage s+1's k-step 0 fragments, and
+//                the loads of stage s+2 into slot s%2, which no wave reads
+//                after the barrier.
+// A chunk c (16 bytes) of tile row r sits at position c ^ ((r >> 1) & 7) of
+// the row: the 16 rows one fragment read covers land in 16 distinct 16-byte
+// bank groups.
+struct Stage64 {
+    Vec16 a[256 * 8];
+    Vec16 b[8 * 4 * 64];
+};
+struct Ring64 {
+    Stage64 st[2];
+    float ep[4 * 2048];
+};
+static_assert(sizeof(Ring64) == 160 * 1024, "LDS");
+
+__device__ __forceinline__ int swz64(int r, int c)
+{
+    return c ^ ((r >> 1) & 7);
+}
+
+struct Src64 {
+    i32x4 rb;          // weight panel
+    uint32_t aoff[8];  // per A load: row byte offset + this lane's chunk
+    int kt;            // 64-wide stage index along K
+};
+
+// Load q (0..15) of this wave's share of a stage at LDS byte address lds:
+// q < 8: tile rows (wv*8 + q)*8 .. +8, 128 bytes each; q >= 8: weight block
+// wv*8 + q - 8 (32-row block /4, 16-k block %4).
+__device__ __forceinline__ void issue64(int q, const i32x4& ra, const Src64& ls, int KB, int wv, uint32_t lane16,
+                                        uint32_t lds)
+{
+    if (q < 8) {
+        dma16(ra, ls.aoff[q], (uint32_t)ls.kt * 128u, lds + (uint32_t)(wv * 8 + q) * 1024u);
+    } else {
+        const int blk = wv * 8 + (q - 8);
+        const uint32_t soff = ((uint32_t)(blk >> 2) * (uint32_t)KB + (uint32_t)ls.kt * 4u + (uint32_t)(blk & 3)) * 1024u;
+        dma16(ls.rb, lane16, soff, lds + (uint32_t)offsetof(Stage64, b) + (uint32_t)blk * 1024u);
+    }
+}
+
+struct Frag64 {
+    const Stage64* st;
+    int wm, wn, lane;
+    // A fragment of the wave's 16-row group i at k-step ks (32 k)
+    __device__ __forceinline__ bf16x8 a(int ks, int i) const
+    {
+        const int r = wm * 128 + i * 16 + (lane & 15);
+        return as_bf16x8(st->a[r * 8 + swz64(r, ks * 4 + (lane >> 4))]);
+    }
+    // B fragment of the wave's 16-row weight group j at k-step ks
+    __device__ __forceinline__ bf16x8 b(int ks, int j) const
+    {
+        const int n = wn * 128 + j * 16 + (lane & 15);
+        const int c = lane >> 4;
+        return as_bf16x8(st->b[((n >> 5) * 4 + ks * 2 + (c >> 1)) * 64 + (n & 31) + 32 * (c & 1)]);
+    }
+};
+
+template <int RG>
+__device__ __forceinline__ void stage64(const i32x4& ra, const Src64& ls, uint32_t ld_lds, int KB, int wv,
+                                        uint32_t lane16, const Stage64* st, const Stage64* st_next, int wm, int wn,
+                                        int lane, bf16x8 (&fa)[8], bf16x8 (&fb)[8], Acc4 (&acc)[4][4])
+{
+    const Frag64 rd{st, wm, wn, lane}, rn{st_next, wm, wn, lane};
+    bf16x8 ga[8], gb[8];
+    int nread = 0;
+#pragma unroll
+    for (int m = 0; m < 64; ++m) {
+        const int j = m / 8, i = m % 8;
+        if ((i >> 1) < RG) {
+            floatx4& c = acc[i >> 1][j >> 1].q[(i & 1) * 2 + (j & 1)];
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], c, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (; nread < 16 && nread < ((m + 1) * 16 + 47) / 48; ++nread) {
+            if (nread < 8)
+                gb[nread] = rd.b(1, nread);
+            else if (((nread - 8) >> 1) < RG)
+                ga[nread - 8] = rd.a(1, nread - 8);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    nread = 0;
+    int nld = 0;
+#pragma unroll
+    for (int m = 0; m < 64; ++m) {
+        const int j = m / 8, i = m % 8;
+        if ((i >> 1) < RG) {
+            floatx4& c = acc[i >> 1][j >> 1].q[(i & 1) * 2 + (j & 1)];
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga[i], gb[j], c, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (; nread < 16 && nread < ((m + 1) * 16 + 47) / 48; ++nread) {
+            if (nread < 8)
+                fb[nread] = rn.b(0, nread);
+            else
+                fa[nread - 8] = rn.a(0, nread - 8);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (; nld < ((m + 1) * 16) / 64; ++nld) {
+            issue64(nld, ra, ls, KB, wv, lane16, ld_lds);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// The K stages of one tile, continuing the stream: stage j multiplies slot b
+// and loads stream stage j + 2 (this tile's, the next tile's first two, or,
+// past the last tile, a reload of this tile's last stage that nobody reads).
+template <int RG>
+__device__ __forceinline__ void tile_stages64(const i32x4& ra, const Src64& cs, int nkt, bool has_nxt,
+                                              const i32x4& nrb, int nkt0, const uint32_t (&cpart)[2],
+                                              uint32_t Kbytes, int KB, int wv, uint32_t lane16, Ring64& ring,
+                                              uint32_t ring0, int& b, int wm, int wn, int lane, bf16x8 (&fa)[8],
+                                              bf16x8 (&fb)[8], const uint32_t (&held)[8], Acc4 (&acc)[4][4])
+{
+    int j = 0;
+    do {
+        const int ja = j + 2;
+        Src64 ls = cs;
+        if (ja < nkt) {
+            ls.kt = cs.kt + ja;
+        } else if (has_nxt) {
+            ls.rb = nrb;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                ls.aoff[i] = held[i] * Kbytes + cpart[i & 1];
+            ls.kt = nkt0 + (ja - nkt);
+        } else {
+            ls.kt = cs.kt + nkt - 1;
+        }
+        stage64<RG>(ra, ls, ring0 + (uint32_t)b * (uint32_t)sizeof(Stage64), KB, wv, lane16, &ring.st[b],
+                    &ring.st[b ^ 1], wm, wn, lane, fa, fb, acc);
+        b ^= 1;
+    } while (++j < nkt);
+}
+
+template <bool GATE_UP, bool YB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void grouped_gemm64_kernel(GemmArgs g)
+{
+    constexpr int BM = 256, BN = 256, WM = 128, WN = 128, MI = 4, NI = 4;
+    constexpr int SM = GATE_UP ? 0 : 64;
+    __shared__ Ring64 ring;
+
+    const int N = GATE_UP ? 2 * g.f : g.d;
+    const int K = GATE_UP ? g.d : g.f;
+    const int NT = N / BN;
+    const int KB = K / 16;
+    const int KT = K / 64;
+    const int S = GATE_UP ? 1 : g.split;
+    const int lane = threadIdx.x % kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int wm = wv / 2, wn = wv % 2;
+
+    TileTable tt;
+    const int total = make_table<BM, SM>(g.offsets, g.E, lane, NT * S, tt);
+    int L = blockIdx.x;
+    const int GRID = gridDim.x;
+    const bool xm = g.xcd_map != 0;
+    const int t0 = tile_index(L, total, xm);
+    if (t0 < 0)
+        return;
+
+    // A loads: load q covers tile rows (wv*8 + q)*8 + lane/8; this lane's
+    // chunk position is lane%8, holding global chunk (lane%8) ^ ((row >> 1) & 7),
+    // which depends on q only through its parity.
+    const uint32_t Kbytes = (uint32_t)K * 2u;
+    int slot[8];
+    uint32_t cpart[2];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        slot[q] = (wv * 8 + q) * 8 + (lane >> 3);
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+        cpart[p] = (uint32_t)swz64(slot[p], lane & 7) * 16u;
+    const uint32_t a_rows = GATE_UP ? (uint32_t)(g.A_max / g.k) : (uint32_t)g.A_max;
+    const i32x4 ra = make_rsrc(g.a, a_rows * Kbytes);
+    const uint32_t lane16 = (uint32_t)lane * 16u;
+
+    Tile cur = decode<BM, SM>(tt, t0, NT, S, g.group_n, KT);
+    Src64 cs;
+    cs.rb = panel_rsrc<BN>(g.b, cur, N, KB);
+    cs.kt = cur.kt0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        cs.aoff[q] = (uint32_t)row_src<GATE_UP>(g.perm, cur, slot[q]) * Kbytes + cpart[q & 1];
+    const int t1 = tile_index(L + GRID, total, xm);
+    bool has_nxt = t1 >= 0;
+    Tile nxt = cur;
+    i32x4 nrb = cs.rb;
+    uint32_t held[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        held[q] = 0;
+    if (has_nxt) {
+        nxt = decode<BM, SM>(tt, t1, NT, S, g.group_n, KT);
+        nrb = panel_rsrc<BN>(g.b, nxt, N, KB);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            held[q] = (uint32_t)row_src<GATE_UP>(g.perm, nxt, slot[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        asm volatile("" : "+v"(held[q]) : : "memory");
+
+    Acc4 acc[MI][NI];
+    auto zero_acc = [&]() {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    acc[i][j].q[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+    };
+    zero_acc();
+
+    // Prologue: stream stages 0 and 1 (the first tile has at least 2), then
+    // stage 0's k-step 0 fragments.
+    const uint32_t ring0 = lds_addr(&ring);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        Src64 ls = cs;
+        ls.kt = cs.kt + p;
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            issue64(q, ra, ls, KB, wv, lane16, ring0 + (uint32_t)p * (uint32_t)sizeof(Stage64));
+    }
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    bf16x8 fa[8], fb[8];
+    {
+        const Frag64 r0{&ring.st[0], wm, wn, lane};
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            fb[j] = r0.b(0, j);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            fa[i] = r0.a(0, i);
+    }
+    int b = 0;
+
+    for (;;) {
+        const int wrows = cur.rows - wm * WM;
+        const int RG = wrows <= 0 ? 0 : wrows <= 32 ? 1 : wrows <= 64 ? 2 : MI;
+        auto run = [&](auto g_const) {
+            constexpr int GG = decltype(g_const)::value;
+            tile_stages64<GG>(ra, cs, cur.nkt, has_nxt, nrb, nxt.kt0, cpart, Kbytes, KB, wv, lane16, ring, ring0, b,
+                              wm, wn, lane, fa, fb, held, acc);
+        };
+        if (RG == MI)
+            run(std::integral_constant<int, MI>{});
+        else if (RG == 2)
+            run(std::integral_constant<int, 2>{});
+        else if (RG == 1)
+            run(std::integral_constant<int, 1>{});
+        else
+            run(std::integral_constant<int, 0>{});
+
+        // The tile after next: its token rows, fetched during the epilogue.
+        const int t2 = has_nxt ? tile_index(L + 2 * GRID, total, xm) : -1;
+        const bool has_nn = t2 >= 0;
+        Tile nn = nxt;
+        i32x4 nnrb = nrb;
+        uint32_t nheld[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            nheld[q] = held[q];
+        if (has_nn) {
+            nn = decode<BM, SM>(tt, t2, NT, S, g.group_n, KT);
+            nnrb = panel_rsrc<BN>(g.b, nn, N, KB);
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                nheld[q] = (uint32_t)row_src<GATE_UP>(g.perm, nn, slot[q]);
+        }
+
+        // Epilogue through this wave's 8 KiB of ring.ep (no other wave uses
+        // it, so no barrier), as grouped_gemm_kernel's M16 epilogues.
+        {
+            const int lq = lane >> 4;
+            int rbase = wm * WM + 4 * lq;
+            asm volatile("" : "+v"(rbase));
+            float* ep = ring.ep + wv * 2048;
+            const int rr = lane >> 1;
+            const int rc = (lane & 1) * 4;
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                if (i >= RG)
+                    continue;
+#pragma unroll
+                for (int jp = 0; jp < NI; jp += 2) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int r = 16 * (c >> 1) + 4 * (lane >> 4) + q;
+                            const int cc = 16 * (c & 1) + (lane & 15);
+                            const int o = r * 32 + (((cc >> 2) ^ (r & 7)) << 2) + (cc & 3);
+                            ep[o] = acc[i][jp].q[c][q];
+                            ep[1024 + o] = acc[i][jp + 1].q[c][q];
+                        }
+                    const int row = min(rbase - 4 * lq + i * 32 + rr, cur.rows - 1);
+                    if constexpr (GATE_UP) {
+                        uint32_t hv[8];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            const int o = rr * 32 + (((rc + t) ^ (rr & 7)) << 2);
+                            const floatx4 gv = *(const floatx4*)(ep + o);
+                            const floatx4 uv = *(const floatx4*)(ep + 1024 + o);
+                            hv[2 * t] = (uint32_t)f32_to_bf16_bits(silu_rcp(gv[0]) * uv[0]) |
+                                        ((uint32_t)f32_to_bf16_bits(silu_rcp(gv[1]) * uv[1]) << 16);
+                            hv[2 * t + 1] = (uint32_t)f32_to_bf16_bits(silu_rcp(gv[2]) * uv[2]) |
+                                            ((uint32_t)f32_to_bf16_bits(silu_rcp(gv[3]) * uv[3]) << 16);
+                        }
+                        const int col = (cur.n * BN + wn * WN + jp * 32) / 2 + rc * 4;
+                        Vec16* dst = (Vec16*)((uint16_t*)g.out + (int64_t)(cur.row0 + row) * g.f + col);
+                        dst[0] = Vec16{hv[0], hv[1], hv[2], hv[3]};
+                        dst[1] = Vec16{hv[4], hv[5], hv[6], hv[7]};
+                    } else if constexpr (YB) {
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            uint32_t hv[8];
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) {
+                                const int o = h * 1024 + rr * 32 + (((rc + t) ^ (rr & 7)) << 2);
+                                const floatx4 v = *(const floatx4*)(ep + o);
+                                hv[2 * t] = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+                                hv[2 * t + 1] =
+                                    (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+                            }
+                            const int col = cur.n * BN + wn * WN + (jp + h) * 32 + rc * 4;
+                            Vec16* dst = (Vec16*)((uint16_t*)g.out + (int64_t)(cur.row0 + row) * g.d + col);
+                            dst[0] = Vec16{hv[0], hv[1], hv[2], hv[3]};
+                            dst[1] = Vec16{hv[4], hv[5], hv[6], hv[7]};
+                        }
+                    } else {
+                        float* Ys = (float*)g.out + (int64_t)cur.s * g.A_max * g.d;
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) {
+                                const int o = h * 1024 + rr * 32 + (((rc + t) ^ (rr & 7)) << 2);
+                                const floatx4 v = *(const floatx4*)(ep + o);
+                                const int col = cur.n * BN + wn * WN + (jp + h) * 32 + (rc + t) * 4;
+                                *(floatx4*)(Ys + (int64_t)(cur.row0 + row) * g.d + col) = v;
+                            }
+                    }
+                }
+            }
+            zero_acc();
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                asm volatile("" : "+v"(nheld[q]) : : "memory");
+        }
+        if (!has_nxt)
+            break;
+        cur = nxt;
+        cs.rb = nrb;
+        cs.kt = cur.kt0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            cs.aoff[q] = held[q] * Kbytes + cpart[q & 1];
+        L += GRID;
+        has_nxt = has_nn;
+        nxt = nn;
+        nrb = nnrb;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            held[q] = nheld[q];
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // Init-time weight repack into the blocked MFMA operand layout: for expert e,
 // row block nb (32 weight rows) and k block kb (16 k), one 1 KiB block in lane
 // order, lane l holding row nb*32 + l%32, k = kb*16 + 8*(l/32) .. +8. With
@@ -1365,6 +1761,17 @@ hipError_t launch_grouped(const GemmArgs& a, hipStream_t s)
         return hipSuccess;
     GemmArgs ga = a;
     ga.xcd_map = xm ? 1 : 0;
+    if constexpr (!F8 && !Q8) {
+        if (a.k64 && a.cnt == nullptr && N % 256 == 0) {
+            if constexpr (GATE_UP)
+                hipLaunchKernelGGL((grouped_gemm64_kernel<true, false>), dim3(grid), dim3(kThreads), 0, s, ga);
+            else if (a.ys_bf16)
+                hipLaunchKernelGGL((grouped_gemm64_kernel<false, true>), dim3(grid), dim3(kThreads), 0, s, ga);
+            else
+                hipLaunchKernelGGL((grouped_gemm64_kernel<false, false>), dim3(grid), dim3(kThreads), 0, s, ga);
+            return hipGetLastError();
+        }
+    }
     if constexpr (GATE_UP) {
         // 2 * d_ff is a multiple of 256 (d_ff % 128 == 0 is checked at init)
         hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 256, 128, 128, true, F8, Q8>), dim3(grid), dim3(kThreads), 0,

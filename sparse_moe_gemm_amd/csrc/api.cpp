@@ -366,13 +366,13 @@ colibri_moe_status_t colibri_moe_init(colibri_moe_t** out, const colibri_moe_con
     // rows per expert (threshold CMOE_M_ORDER_ROWS, 0 = never).
     h->order_m_rows = env_int("CMOE_M_ORDER_ROWS", 384, 0, 1 << 30);
     h->xcd_map = env_int("CMOE_XCD_MAP", 0, 0, 3);
-    // 64-wide K stages (grouped_gemm64_kernel) for the bf16 gate/up GEMM:
-    // 4-6% faster on layers of 512-2048 rows per expert (mixtral gate/up
-    // 1766 -> 1695 us), 4% slower only with 8192 rows on one expert; the down
-    // GEMM keeps 32-wide stages (up to 12% slower with 64). Same sums in the
-    // same order, so outputs are bit-identical either way. CMOE_K64: bit 0
-    // gate/up, bit 1 down.
-    h->k64 = env_int("CMOE_K64", 1, 0, 3);
+    // 64-wide K stages (grouped_gemm64_kernel) for the bf16 gate/up GEMM
+    // (with tile groups of 16 n-tiles): mixtral gate/up 1.76 -> 1.68 ms, one
+    // expert of 8192 rows 1.66 -> 1.44 ms; the down GEMM keeps 32-wide stages
+    // (up to 12% slower with 64). Same sums in the same order, so outputs are
+    // bit-identical either way. CMOE_K64: bit 0 gate/up, bit 1 down, bit 2
+    // gate/up whatever the rows per expert.
+    h->k64 = env_int("CMOE_K64", 1, 0, 7);
     // Combine fused into the down GEMM's epilogue (bf16 layers, tiled path)
     // with CMOE_FUSE_COMBINE=1; the default runs the combine kernel, which is
     // faster here: the fused form needs device-scope release/acquire fences
@@ -486,7 +486,11 @@ colibri_moe_status_t forward_impl(colibri_moe* h, const void* x, int32_t T, void
         GemmArgs gu{q8 ? (const void*)ws.xq : x, h->w_gu, h->s_gu, q8 ? ws.xsc : nullptr, ws.H, offsets, perm, A,
                     c.n_experts, c.top_k, c.d_model, c.d_ff, order_m ? -8 : h->group_n_gu, 1, h->cus};
         gu.xcd_map = h->xcd_map & 1;
-        gu.k64 = h->k64 & 1;
+        // 64-wide K stages for layers of at least three m-tiles per expert on
+        // average (mixtral, one big expert); with fewer (fine-grained 256
+        // rows, skewed 512) they measured 0-4% slower than 32-wide stages
+        // (CMOE_K64 bit 2 drops this condition)
+        gu.k64 = (h->k64 & 1) && ((h->k64 & 4) || (int64_t)A >= (int64_t)768 * c.n_experts);
         CMOE_HIP(bf ? launch_gate_up_bf16(gu, s) : launch_gate_up_f32(gu, s));
         if (tm) {
             CMOE_HIP(hipEventRecord(h->ev[3], s));

@@ -235,6 +235,17 @@ def profile_fields(workload: str, kernel: str) -> dict:
     return fields
 
 
+def gate_up_kernel_name(cfg, A: int, fp8: bool, q8: bool) -> str:
+    """The tiled gate/up kernel the library picks for a call (the rule in
+    api.cpp): 64-wide K stages for bf16 weights when the layer has at least
+    768 rows per expert on average (CMOE_K64 bit 0; bit 2 drops the row
+    condition), else the 32-wide kernel."""
+    k64 = int(os.environ.get("CMOE_K64", "1"))
+    if not fp8 and not q8 and (k64 & 1) and ((k64 & 4) or A >= 768 * cfg.E):
+        return "grouped_gemm64_kernel<true, false> (gate/up, 64-wide K stages)"
+    return "grouped_gemm_kernel (gate/up" + (", fp8 MFMA" if q8 else "") + ")"
+
+
 def profiled_traffic(workload: str, kernel: str):
     """HBM bytes per launch of `kernel` ("gate_up_gemm") from the committed
     rocprofv3 summary of this workload (FETCH_SIZE and WRITE_SIZE, scaled by a
@@ -400,7 +411,7 @@ def run_workload(name: str, args, fp8: bool, q8: bool) -> dict:
         gu_peak = PEAK_FP8_TFLOPS if q8 else peak_mm
         roof = {"bound": "mfma", "achieved": achieved, "peak": gu_peak, "unit": "TFLOP/s",
                 "frac": achieved / gu_peak, "traffic": traffic,
-                "kernel": "grouped_gemm_kernel (gate/up" + (", fp8 MFMA" if q8 else "") + ")"}
+                "kernel": gate_up_kernel_name(cfg, A, fp8, q8)}
     return {
         "cfg": cfg,
         "inp": inp,

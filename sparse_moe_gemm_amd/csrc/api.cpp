@@ -506,9 +506,9 @@ colibri_moe_status_t forward_impl(colibri_moe* h, const void* x, int32_t T, void
             dn.y = y;
             fused = true;
         }
-        // Without a K split the expert outputs go to Ys as bf16 rows (bf16
-        // weights).
-        dn.ys_bf16 = bf && !h->fp8 && split == 1 && !fused;
+        // Without a K split the expert outputs go to Ys as bf16 rows (any
+        // weight precision of a bf16 layer).
+        dn.ys_bf16 = bf && split == 1 && !fused;
         dn.xcd_map = (h->xcd_map >> 1) & 1;
         dn.k64 = (h->k64 >> 1) & 1;
         ys_bf16 = dn.ys_bf16;

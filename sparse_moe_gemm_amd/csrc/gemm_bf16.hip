@@ -79,8 +79,9 @@ struct Stage {
     Vec16 a[BM * kCH];
     Vec16 b[(BN / 32) * (F8 ? 1 : 2) * 64];
 };
-// The ring of stages; with fp8 weights the gate/up epilogue has a buffer of
-// its own (a 24 KiB slot is too small for it).
+// The ring of stages; with fp8 weights the epilogues that stage bf16 rows
+// (gate/up, and the down GEMM's bf16 outputs) have a buffer of their own (a
+// 24 KiB slot is too small for them).
 template <int BM, int BN, bool F8, bool EPBUF>
 struct Ring {
     Stage<BM, BN, F8> st[kRing];
@@ -803,7 +804,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     constexpr int A_INS = BM * kCH / 64 / 4;             // A loads per wave per stage
     constexpr int B_INS = (BN / 32) * (F8 ? 1 : 2) / 4;  // weight blocks per wave per stage
     constexpr int NLD = A_INS + B_INS;
-    constexpr bool EPBUF = GATE_UP && F8;                // gate/up epilogue outside the ring
+    constexpr bool EPBUF = (GATE_UP || YB) && F8;        // bf16 epilogue outside the ring
     static_assert((BM / WM) * WAVES_N == kThreads / kWave, "4 waves");
     static_assert(A_INS * 4 * 16 == BM && B_INS * 4 == (BN / 32) * (F8 ? 1 : 2), "stage split over 4 waves");
     static_assert(!GATE_UP || (NI % 2 == 0 && WN % 64 == 0), "gate/up pairs per wave");
@@ -1144,13 +1145,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 if constexpr (YB) {
                     // bf16 rows through LDS, as the gate/up epilogue: two
                     // 32x32 accumulator blocks at a time go into this wave's
-                    // 8 KiB of the free ring slot (rows of 32 fp32, chunk index
-                    // XORed with row%8), then each lane reads back 16
-                    // consecutive values of each block from one row, rounds
-                    // them to bf16 and writes them with 16-byte stores.
-                    static_assert(M16 && NI % 2 == 0, "bf16 outputs: 16x16 MFMA layout, column block pairs");
-                    const int bfree = b == 0 ? kRing - 1 : b - 1;
-                    float* ep = (float*)&ring.st[bfree] + wv * 2048;
+                    // 8 KiB of the free ring slot (8-bit weights: of the
+                    // epilogue buffer; rows of 32 fp32, chunk index XORed with
+                    // row%8), then each lane reads back 16 consecutive values
+                    // of each block from one row, rounds them to bf16 and
+                    // writes them with 16-byte stores.
+                    static_assert(NI % 2 == 0, "bf16 outputs: column block pairs");
+                    float* ep;
+                    if constexpr (EPBUF) {
+                        ep = ring.ep + wv * 2048;
+                    } else {
+                        const int bfree = b == 0 ? kRing - 1 : b - 1;
+                        ep = (float*)&ring.st[bfree] + wv * 2048;
+                    }
+                    const int wr = 4 * (lane >> 5);  // 32x32 layout: row of q = 0 inside the group
+                    const int wc = lane & 31;
                     const int rr = lane >> 1;       // row read back by this lane
                     const int rc = (lane & 1) * 4;  // first 16-byte chunk read back
                     uint16_t* Yb = (uint16_t*)g.out;
@@ -1160,17 +1169,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                             continue;
 #pragma unroll
                         for (int jp = 0; jp < NI; jp += 2) {
+                            if constexpr (M16) {
 #pragma unroll
-                            for (int c = 0; c < 4; ++c)  // 16x16 block (c/2, c%2) of the region
+                                for (int c = 0; c < 4; ++c)  // 16x16 block (c/2, c%2) of the region
 #pragma unroll
-                                for (int q = 0; q < 4; ++q) {
-                                    const int r = 16 * (c >> 1) + 4 * (lane >> 4) + q;
-                                    const int cc = 16 * (c & 1) + (lane & 15);
-                                    const int o = r * 32 + (((cc >> 2) ^ (r & 7)) << 2) + (cc & 3);
-                                    ep[o] = acc[i][jp].q[c][q];
-                                    ep[1024 + o] = acc[i][jp + 1].q[c][q];
+                                    for (int q = 0; q < 4; ++q) {
+                                        const int r = 16 * (c >> 1) + 4 * (lane >> 4) + q;
+                                        const int cc = 16 * (c & 1) + (lane & 15);
+                                        const int o = r * 32 + (((cc >> 2) ^ (r & 7)) << 2) + (cc & 3);
+                                        ep[o] = acc[i][jp].q[c][q];
+                                        ep[1024 + o] = acc[i][jp + 1].q[c][q];
+                                    }
+                            } else {
+#pragma unroll
+                                for (int q = 0; q < 16; ++q) {
+                                    const int r = wr + 8 * (q / 4) + (q % 4);
+                                    const int o = r * 32 + (((wc >> 2) ^ (r & 7)) << 2) + (wc & 3);
+                                    ep[o] = acc[i][jp][q];
+                                    ep[1024 + o] = acc[i][jp + 1][q];
                                 }
-                            const int row = min(rbase - 4 * (lane >> 4) + i * 32 + rr, cur.rows - 1);
+                            }
+                            const int row = min(rbase - 4 * lq + i * 32 + rr, cur.rows - 1);
 #pragma unroll
                             for (int h = 0; h < 2; ++h) {  // the two column blocks
                                 uint32_t hv[8];
@@ -1189,9 +1208,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                             }
                         }
                     }
-                    // Every wave is done with the slot before the next stage loads it.
-                    __builtin_amdgcn_s_barrier();
-                    asm volatile("" ::: "memory");
+                    // Every wave is done with the slot before the next stage
+                    // loads it (a wave's own epilogue buffer needs no barrier).
+                    if constexpr (!EPBUF) {
+                        __builtin_amdgcn_s_barrier();
+                        asm volatile("" ::: "memory");
+                    }
                 } else {
 #pragma unroll
                 for (int i = 0; i < MI; ++i) {
@@ -1784,7 +1806,9 @@ hipError_t launch_grouped(const GemmArgs& a, hipStream_t s)
             hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 128, 128, 64, false, F8, Q8, true>), dim3(grid),
                                dim3(kThreads), 0, s, ga);
     } else if (a.ys_bf16) {
-        if constexpr (!Q8 && !F8) {
+        if constexpr (Q8) {  // 8-bit A rows feed the gate/up GEMM only
+            return hipErrorInvalidValue;
+        } else {
             if (BN == 256)
                 hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 256, 128, 128, false, F8, Q8, false, true>), dim3(grid),
                                    dim3(kThreads), 0, s, ga);

@@ -202,7 +202,7 @@ def test_fp8_layer_parity(cfg, path, monkeypatch):
         assert np.all(g["expert_counts"][44:] == 0)
 
 
-@pytest.mark.parametrize("name", ["decode", "mixtral"])
+@pytest.mark.parametrize("name", ["decode", "mixtral", "fine-grained"])
 def test_fp8_full_size_workload(name):
     cfg = synth.CONFIGS[name]
     print(f"fp8 full-size case {cfg}", flush=True)

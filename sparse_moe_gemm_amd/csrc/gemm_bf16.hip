@@ -594,7 +594,7 @@ __device__ __forceinline__ void fused_combine(const GemmArgs& g, int row0, int r
             if (j < g.k) {
                 const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wgt[j]), b));
                 float4 u = v[j][0];
-                if (g.split == 1 && g.scales == nullptr) {  // bf16 weights: the values the unfused path stores as bf16
+                if (g.split == 1) {  // the values the unfused path stores as bf16 (no K split)
                     u.x = bf16_to_f32(f32_to_bf16_bits(u.x));
                     u.y = bf16_to_f32(f32_to_bf16_bits(u.y));
                     u.z = bf16_to_f32(f32_to_bf16_bits(u.z));

@@ -70,7 +70,11 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 }
 
 // Top-k + softmax for the block's bt tokens, reading logits (bias included)
-// from LDS `lg` laid out [bt][ldl]. Wave w of W handles tokens w, w+W, ...
+// from LDS `lg` laid out [bt][ldl]. Wave w of W handles tokens w, w+W, ...;
+// lane l holds the keys of experts l + 64q (q < NQ, NQ = ceil(E / 64) at
+// most) and, once they are chosen, slot l's expert and logit (l < k), so
+// that the k softmax weights are computed and stored by k lanes at once.
+template <int NQ>
 __device__ void topk_softmax_epilogue(const float* lg, int ldl, int bt, int t0, int T, int E, int k,
                                       int32_t* ids, float* wout)
 {
@@ -83,44 +87,47 @@ __device__ void topk_softmax_epilogue(const float* lg, int ldl, int bt, int t0, 
         // Order keys of the token's logits (expert e = lane + 64q); an expert
         // not present, or already taken, has key 0, below every logit's key.
         // The largest key wins; among equal keys the lowest expert index.
-        uint32_t key[4];
+        uint32_t key[NQ];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < NQ; ++q) {
             const int e = lane + q * kWave;
             key[q] = e < E ? order_key(lg[r * ldl + e]) : 0u;
         }
-        float lsel[kMaxTopK];
-        int isel[kMaxTopK];
+        int my_id = 0;
+        float my_l = 0.0f;
         for (int j = 0; j < k; ++j) {
-            uint32_t best = max(max(key[0], key[1]), max(key[2], key[3]));
+            uint32_t best = key[0];
+#pragma unroll
+            for (int q = 1; q < NQ; ++q)
+                best = max(best, key[q]);
             best = wave_max_u32(best);
             int e = E - 1;
 #pragma unroll
-            for (int q = 3; q >= 0; --q) {
+            for (int q = NQ - 1; q >= 0; --q) {
                 const uint64_t m = __ballot(key[q] == best && lane + q * kWave < E);
                 if (m != 0)
                     e = q * kWave + __builtin_ctzll(m);
             }
-            isel[j] = e;
-            lsel[j] = key_value(best);
+            if (lane == j) {
+                my_id = e;
+                my_l = key_value(best);
+            }
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < NQ; ++q)
                 if (lane + q * kWave == e)
                     key[q] = 0u;
         }
-        if (lane == 0) {
-            const float l0 = lsel[0];
-            float ex[kMaxTopK];
-            float s = 0.0f;
-            for (int j = 0; j < k; ++j) {
-                ex[j] = __expf(lsel[j] - l0);
-                s += ex[j];
-            }
-            const float inv = 1.0f / s;
-            for (int j = 0; j < k; ++j) {
-                ids[(int64_t)t * k + j] = isel[j];
-                wout[(int64_t)t * k + j] = ex[j] * inv;
-            }
+        // w_j = exp(l_j - l_0) / sum_j' exp(l_j' - l_0), the sum taken in slot
+        // order (the same value in every lane).
+        const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_l), 0));
+        const float ex = __expf(my_l - l0);
+        float sum = 0.0f;
+        for (int j = 0; j < k; ++j)
+            sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
+        const float inv = 1.0f / sum;
+        if (lane < k) {
+            ids[(int64_t)t * k + lane] = my_id;
+            wout[(int64_t)t * k + lane] = ex * inv;
         }
     }
 }
@@ -253,7 +260,7 @@ __global__ __launch_bounds__(W * kWave) void router_bf16_kernel(RouterArgs a)
     }
     __syncthreads();
     store_logits(&part[0][0], LDL, BT, t0, a.T, a.E, a.logits);
-    topk_softmax_epilogue(&part[0][0], LDL, BT, t0, a.T, a.E, a.k, a.ids, a.w);
+    topk_softmax_epilogue<(EP + kWave - 1) / kWave>(&part[0][0], LDL, BT, t0, a.T, a.E, a.k, a.ids, a.w);
 }
 
 __global__ __launch_bounds__(kThreads) void router_f32_kernel(RouterArgs a)
@@ -274,7 +281,7 @@ __global__ __launch_bounds__(kThreads) void router_f32_kernel(RouterArgs a)
     }
     __syncthreads();
     store_logits(&lg[0][0], kMaxExperts + 1, kTok, t0, a.T, a.E, a.logits);
-    topk_softmax_epilogue(&lg[0][0], kMaxExperts + 1, kTok, t0, a.T, a.E, a.k, a.ids, a.w);
+    topk_softmax_epilogue<kMaxExperts / kWave>(&lg[0][0], kMaxExperts + 1, kTok, t0, a.T, a.E, a.k, a.ids, a.w);
 }
 
 __global__ void transpose_router_kernel(const uint8_t* src, uint8_t* dst, int d, int E, int esize)

@@ -16,7 +16,10 @@
 // (no atomics, no histogram contention on hot experts). Ranks inside the
 // segment come from a block-wide exclusive scan over threads that own
 // consecutive runs of assignments, so the order is the (t, j) order and the
-// result is exact and reproducible. A block covers 4096 assignments per
+// result is exact and reproducible. The three counts need only block totals
+// (one shuffle reduction per wave and one LDS exchange), and when the ids fit
+// one block iteration each thread keeps its run in registers for the second
+// pass. A block covers 4096 assignments per
 // iteration up to 8192 assignments (256 threads, runs of 16), else 32768
 // (1024 threads, runs of 32), so most calls need one or two loads and scans
 // per pass: the loop over chunks is a chain of dependent loads and block
@@ -76,12 +79,41 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int& tot
     return before + incl - v;
 }
 
+// Block-wide sums of NV ints per thread (NT threads): each wave adds its
+// lanes' values with butterfly shuffles, then every thread adds the waves'
+// sums from LDS (one barrier pair for all NV values).
+template <int NT, int NV>
+__device__ __forceinline__ void block_sums(int (&v)[NV], int (*s_red)[NV])
+{
+    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int off = kWave / 2; off > 0; off >>= 1)
+            v[i] += __shfl_xor(v[i], off, kWave);
+    if (lane == 0)
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            s_red[wv][i] = v[i];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        int t = 0;
+#pragma unroll
+        for (int w = 0; w < NT / kWave; ++w)
+            t += s_red[w][i];
+        v[i] = t;
+    }
+    __syncthreads();
+}
+
 // NT threads, kRun consecutive assignments per thread.
 template <int NT, int kRun>
 __global__ __launch_bounds__(NT) void dispatch_kernel(DispatchArgs g, int parts)
 {
     constexpr int kChunk = NT * kRun;  // assignments per block iteration
     __shared__ int s_wave[NT / kWave];
+    __shared__ int s_red[NT / kWave][3];
     const int e = blockIdx.x / parts;
     const int part = blockIdx.x % parts;
     const int A = g.T * g.k;
@@ -93,11 +125,12 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(DispatchArgs g, int parts)
     const int r0 = min(part * rpp, runs) * kRun;
     const int r1 = min((part + 1) * rpp, runs) * kRun;
 
-    // Pass 1: count ids below e, equal to e, and equal to e before r0.
+    // Pass 1: count ids below e, equal to e, and equal to e before r0. When
+    // the ids fit one chunk, this thread's run stays in v for pass 2.
     int below = 0, equal = 0, before = 0;
+    int v[kRun];
     for (int c = 0; c < A; c += kChunk) {
         const int a0 = c + threadIdx.x * kRun;
-        int v[kRun];
         load_run(g.ids, a0, A, v);
         int eq = 0;
 #pragma unroll
@@ -108,11 +141,9 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(DispatchArgs g, int parts)
         equal += eq;
         before += a0 < r0 ? eq : 0;  // r0 is a run boundary
     }
-    int tot_below, tot_equal, tot_before = 0;
-    (void)block_exclusive_scan<NT>(below, s_wave, tot_below);
-    (void)block_exclusive_scan<NT>(equal, s_wave, tot_equal);
-    if (parts > 1)
-        (void)block_exclusive_scan<NT>(before, s_wave, tot_before);
+    int tot[3] = {below, equal, before};
+    block_sums<NT, 3>(tot, s_red);
+    const int tot_below = tot[0], tot_equal = tot[1], tot_before = tot[2];
     if (part == 0 && threadIdx.x == 0) {
         g.counts[e] = tot_equal;
         g.offsets[e] = tot_below;
@@ -122,21 +153,25 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(DispatchArgs g, int parts)
     if (tot_equal == tot_before)  // none of this expert's assignments in [r0, r1)
         return;
 
-    // Pass 2: stable compaction of this expert's assignments in [r0, r1).
+    // Pass 2: stable compaction of this expert's assignments in [r0, r1),
+    // over the chunks of pass 1 that meet that range (runs outside it count
+    // none of this block's assignments).
     int base = tot_below + tot_before;
-    for (int c = r0; c < r1; c += kChunk) {
+    const bool one = A <= kChunk;  // v still holds this thread's run
+    for (int c = (r0 / kChunk) * kChunk; c < r1; c += kChunk) {
         const int a0 = c + threadIdx.x * kRun;
-        int v[kRun];
-        load_run(g.ids, a0, A, v);
+        if (!one)
+            load_run(g.ids, a0, A, v);
+        const bool in = a0 >= r0 && a0 < r1;  // runs are whole: r0, r1 are run boundaries
         int mine = 0;
-        if (a0 < r1) {
+        if (in) {
 #pragma unroll
             for (int q = 0; q < kRun; ++q)
                 mine += v[q] == e;
         }
         int chunk_total;
         int p = base + block_exclusive_scan<NT>(mine, s_wave, chunk_total);
-        if (a0 < r1) {
+        if (in) {
 #pragma unroll
             for (int q = 0; q < kRun; ++q) {
                 if (v[q] == e) {

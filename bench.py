@@ -121,7 +121,9 @@ def peaks(args):
     plain dense product, at M = N = K = 8192 and at 8192 x 28672 x 4096 (the
     Mixtral gate/up shape with all 8192 rows on one expert). torch.matmul on
     the same bf16 shapes (a vendor library GEMM, not part of this library) is
-    timed beside it for reference. Kernel times are the layer's own stage
+    timed beside it for reference, and, on the mixtral, fine-grained and
+    skewed layers' own routing, one torch.matmul per active expert beside the
+    library's grouped gate/up GEMM. Kernel times are the layer's own stage
     events (median of K forwards)."""
     import torch
 
@@ -175,7 +177,58 @@ def peaks(args):
         del a, b, x, y, wts
         torch.cuda.empty_cache()
     out["gemm_bf16"] = gemms
+    out["grouped_gate_up"] = {name: grouped_reference(name, args, timed) for name in ("mixtral", "fine-grained", "skewed")}
     print(json.dumps(out), flush=True)
+
+
+def grouped_reference(name, args, timed):
+    """The gate/up GEMM of a layer shape on its own routing: the library's
+    grouped kernel (stage event; it also gathers the token rows through perm
+    and applies SiLU(g)*u) against one torch.matmul (hipBLASLt) per active
+    expert on token rows already gathered into expert order (a vendor library
+    reference, not part of this library; gathering and weight transposes are
+    outside its timed region)."""
+    import torch
+
+    import synth
+    import sparse_moe_gemm_amd as cm
+
+    cfg = synth.CONFIGS[name]
+    inp = synth.make_inputs(cfg)
+    wts = [to_dev(inp[k]) for k in ("w_router", "b_router", "w_gate", "w_up", "w_down")]
+    x = to_dev(inp["x"])
+    y = torch.empty_like(x)
+    layer = cm.MoELayer(*wts, cfg.k, max_tokens=cfg.T, flags=cm.FLAG_ASYNC | cm.FLAG_STAGE_TIMING)
+    rt = layer.routing_buffers(cfg.T)
+    for _ in range(args.warmup):
+        layer.forward(x, y, routing=rt)
+    ts = []
+    for _ in range(args.steps):
+        layer.forward(x, y, routing=rt)
+        ts.append(layer.stage_times()["gate_up_gemm"])
+    layer.close()
+    torch.cuda.synchronize()
+    ours = float(np.median(ts))
+    counts = rt["expert_counts"].cpu().tolist()
+    offs = rt["expert_offsets"].cpu().tolist()
+    a_sorted = x[rt["perm"].long()].contiguous()
+    # [E][d][2f] contiguous right operands (gate rows then up rows of each expert)
+    w_gu = torch.cat([wts[2], wts[3]], dim=1).transpose(1, 2).contiguous()
+    del wts, x, y, rt
+    active = [e for e in range(cfg.E) if counts[e] > 0]
+    outs = {e: torch.empty(counts[e], 2 * cfg.f, dtype=torch.bfloat16, device="cuda") for e in active}
+
+    def per_expert():
+        for e in active:
+            torch.matmul(a_sorted[offs[e]:offs[e + 1]], w_gu[e], out=outs[e])
+
+    ref = timed(per_expert)
+    flop = 4.0 * cfg.d * cfg.f * cfg.T * cfg.k
+    del a_sorted, w_gu, outs
+    torch.cuda.empty_cache()
+    return {"workload": WORKLOAD_NAMES.get(name, name), "active_experts": len(active),
+            "library_gate_up_ms": ours, "library_tflops": flop / (ours * 1e-3) / 1e12,
+            "torch_matmul_per_expert_ms": ref, "torch_matmul_per_expert_tflops": flop / (ref * 1e-3) / 1e12}
 
 
 def to_dev(a):

@@ -123,7 +123,7 @@ def peaks(args):
     the same bf16 shapes (a vendor library GEMM, not part of this library) is
     timed beside it for reference, and, on the mixtral, fine-grained and
     skewed layers' own routing, one torch.matmul per active expert beside the
-    library's grouped gate/up GEMM. Kernel times are the layer's own stage
+    library's grouped gate/up and down GEMMs. Kernel times are the layer's own stage
     events (median of K forwards)."""
     import torch
 
@@ -182,12 +182,12 @@ def peaks(args):
 
 
 def grouped_reference(name, args, timed):
-    """The gate/up GEMM of a layer shape on its own routing: the library's
-    grouped kernel (stage event; it also gathers the token rows through perm
-    and applies SiLU(g)*u) against one torch.matmul (hipBLASLt) per active
-    expert on token rows already gathered into expert order (a vendor library
-    reference, not part of this library; gathering and weight transposes are
-    outside its timed region)."""
+    """The expert GEMMs of a layer shape on its own routing: the library's
+    grouped kernels (stage events; gate/up also gathers the token rows through
+    perm and applies SiLU(g)*u) against one torch.matmul (hipBLASLt) per
+    active expert on rows already in expert order (a vendor library reference,
+    not part of this library; gathering and weight transposes are outside its
+    timed region, and the down products take random bf16 rows of h)."""
     import torch
 
     import synth
@@ -202,33 +202,44 @@ def grouped_reference(name, args, timed):
     rt = layer.routing_buffers(cfg.T)
     for _ in range(args.warmup):
         layer.forward(x, y, routing=rt)
-    ts = []
+    ts, td = [], []
     for _ in range(args.steps):
         layer.forward(x, y, routing=rt)
-        ts.append(layer.stage_times()["gate_up_gemm"])
+        st = layer.stage_times()
+        ts.append(st["gate_up_gemm"])
+        td.append(st["down_gemm"])
     layer.close()
     torch.cuda.synchronize()
-    ours = float(np.median(ts))
+    ours, ours_dn = float(np.median(ts)), float(np.median(td))
     counts = rt["expert_counts"].cpu().tolist()
     offs = rt["expert_offsets"].cpu().tolist()
     a_sorted = x[rt["perm"].long()].contiguous()
     # [E][d][2f] contiguous right operands (gate rows then up rows of each expert)
     w_gu = torch.cat([wts[2], wts[3]], dim=1).transpose(1, 2).contiguous()
+    w_dn = wts[4].transpose(1, 2).contiguous()  # [E][f][d]
+    h_sorted = torch.randn(cfg.T * cfg.k, cfg.f, device="cuda").to(torch.bfloat16)
     del wts, x, y, rt
     active = [e for e in range(cfg.E) if counts[e] > 0]
     outs = {e: torch.empty(counts[e], 2 * cfg.f, dtype=torch.bfloat16, device="cuda") for e in active}
+    outs_dn = {e: torch.empty(counts[e], cfg.d, dtype=torch.bfloat16, device="cuda") for e in active}
 
     def per_expert():
         for e in active:
             torch.matmul(a_sorted[offs[e]:offs[e + 1]], w_gu[e], out=outs[e])
 
+    def per_expert_dn():
+        for e in active:
+            torch.matmul(h_sorted[offs[e]:offs[e + 1]], w_dn[e], out=outs_dn[e])
+
     ref = timed(per_expert)
+    ref_dn = timed(per_expert_dn)
     flop = 4.0 * cfg.d * cfg.f * cfg.T * cfg.k
-    del a_sorted, w_gu, outs
+    del a_sorted, w_gu, outs, h_sorted, w_dn, outs_dn
     torch.cuda.empty_cache()
     return {"workload": WORKLOAD_NAMES.get(name, name), "active_experts": len(active),
             "library_gate_up_ms": ours, "library_tflops": flop / (ours * 1e-3) / 1e12,
-            "torch_matmul_per_expert_ms": ref, "torch_matmul_per_expert_tflops": flop / (ref * 1e-3) / 1e12}
+            "torch_matmul_per_expert_ms": ref, "torch_matmul_per_expert_tflops": flop / (ref * 1e-3) / 1e12,
+            "library_down_ms": ours_dn, "torch_matmul_per_expert_down_ms": ref_dn}
 
 
 def to_dev(a):

@@ -437,6 +437,36 @@ def run_workload(name: str, args, fp8: bool, q8: bool) -> dict:
         del graph
         glayer.close()
 
+    # 1c) layers back to back (small batches): NB handles (each with its own
+    # copy of the weights in its arena, so every layer streams its weights
+    # from HBM) chained on one stream, x -> y0 -> y1 -> ..., as consecutive
+    # MoE layers of a decode step would run; per-layer time of the chain
+    chain_ms = None
+    NB = 4
+    if cfg.T * cfg.k <= 256 and cfg.dtype == "bf16":
+        layers = [cm.MoELayer(*wts, cfg.k, max_tokens=cfg.T, flags=cm.FLAG_ASYNC | flags) for _ in range(NB)]
+        cs = layers[0].stream
+        ys = [torch.empty_like(x) for _ in range(NB)]
+
+        def chain():
+            src = x
+            for L, dst in zip(layers, ys):
+                L.forward(src, dst)
+                src = dst
+
+        for _ in range(args.warmup):
+            chain()
+        torch.cuda.synchronize()
+        ev0.record(cs)
+        for _ in range(args.steps):
+            chain()
+        ev1.record(cs)
+        torch.cuda.synchronize()
+        chain_ms = ev0.elapsed_time(ev1) / args.steps / NB
+        for L in layers:
+            L.close()
+        del layers, ys
+
     # 2) per-kernel durations: the library's per-stage events (recorded on
     # the same stream as the kernels), averaged over K forwards
     layer = cm.MoELayer(*wts, cfg.k, max_tokens=cfg.T, flags=cm.FLAG_ASYNC | cm.FLAG_STAGE_TIMING | flags)
@@ -495,6 +525,8 @@ def run_workload(name: str, args, fp8: bool, q8: bool) -> dict:
             "active_experts": int((counts > 0).sum()),
             "host_enqueue_us_per_step": t_enq / args.steps * 1e6,
             "graph_replay_ms_per_step": graph_ms,
+            "back_to_back_layers": NB if chain_ms is not None else None,
+            "back_to_back_ms_per_layer": chain_ms,
             "wall_s_timed": t_wall,
             "input_gen_s": t_gen,
         },

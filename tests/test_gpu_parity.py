@@ -54,6 +54,11 @@ SMALL = [
     # each class at the end); two K splits (K = 2048) and one
     C("small-among-big", 3000, 256, 32, 2, 2048, "bf16", {0: 3.0, 5: 3.0, 9: 2.0}),
     C("small-among-big-k1", 2600, 256, 48, 1, 256, "bf16", {2: 4.0, 40: 4.0}),
+    # at least 4096 tokens with 64 or 128 experts: router blocks of 64 or 32
+    # tokens, the last one ragged (4 tokens, 1 token: its other rows are
+    # clamped repeats whose results are dropped)
+    C("router-64-token-blocks-ragged", 4100, 256, 64, 2, 128, "bf16", {7: 0.5}),
+    C("router-32-token-blocks-ragged", 4097, 256, 128, 4, 128, "bf16"),
 ]
 
 

@@ -268,7 +268,8 @@ def test_full_size_workload(name):
         assert rep["empty_experts"] == 20
 
 
-PLACEMENT = [SMALL[1], SMALL[2], SMALL[5], SMALL[-2]]  # mixtral-, fine-grained-, skewed-masked-small, small-among-big
+BY_NAME = {c.name: c for c in SMALL}
+PLACEMENT = [BY_NAME[n] for n in ("mixtral-small", "fine-grained-small", "skewed-masked-small", "small-among-big")]
 
 
 @pytest.mark.parametrize("cfg", PLACEMENT, ids=[c.name for c in PLACEMENT])
@@ -291,7 +292,8 @@ def test_xcd_contiguous_placement(cfg, monkeypatch):
     compare(cfg, inp, g1)
 
 
-STAGES64 = [SMALL[1], SMALL[2], SMALL[5], SMALL[13], SMALL[19], SMALL[-2]]
+STAGES64 = [BY_NAME[n] for n in ("mixtral-small", "fine-grained-small", "skewed-masked-small", "last-tile-padding",
+                                  "tail-288", "small-among-big")]
 
 
 @pytest.mark.parametrize("cfg", STAGES64, ids=[c.name for c in STAGES64])

@@ -309,14 +309,61 @@ __device__ __forceinline__ void stage(const i32x4& ra, const LoadSrc<A_INS>& ls,
 // bf16 weights on v_mfma_f32_16x16x32_bf16 (M16 path): one MFMA k step per
 // 32-wide K stage. A wave's 128 x 128 block is 8 x 8 MFMA blocks of 16 x 16;
 // Acc4 holds the four 16x16 blocks of one 32x32 region, q[2*ri + cj] for
-// rows 16*ri .. and columns 16*cj ... Operand lanes: A lane l holds row l%16
-// and k 8*(l/16) .. +8 (chunk l/16 of the stage's A row), B lane l the same
-// k of weight row l%16; D lane l holds column l%16, rows 4*(l/16) + q. Per
+// rows 16*ri .. and columns 16*cj ... Fragment lanes: a token-row fragment's
+// lane l holds row l%16 and k 8*(l/16) .. +8 (chunk l/16 of the stage's A
+// row), a weight fragment's lane l the same k of weight row l%16. With the
+// token fragment as the MFMA's first operand (SW false) lane l of a result
+// block holds output column l%16 of token rows 4*(l/16) + q; with the weight
+// fragment first (SW true) the block is transposed: token row l%16, output
+// columns 4*(l/16) + q. The products and their order are the same either
+// way, and so are the results, bit for bit. Per
 // element of work this shape moves half the accumulator registers of the
 // 32x32x16 shape, which saves power in a power-bound loop.
 struct Acc4 {
     floatx4 q[4];
 };
+
+// Epilogues of the M16 path on transposed blocks (SW): lane l holds token row
+// l%16 and the four consecutive output columns 4*(l/16) .. +3 of each 16x16
+// block, so it can store its own row segment without a trip through LDS.
+// bf16_pair: two fp32 values as two bf16 in one register, first in the low half.
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b)
+{
+    return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+}
+
+// Row segment of 8 bf16 from the two 16x16 blocks of a 32-column block (c0:
+// columns 0..15, c1: 16..31; lo/hi: the lane's columns 0,1 and 2,3 of its
+// four). One v_permlane16_swap per register pair trades the odd 16-lane rows
+// of c0 for the even rows of c1: afterwards lanes of an even row group g hold
+// columns 4g .. 4g+7 (their own four of c0, then those of lane l+16), lanes of
+// an odd group columns 16 + 4(g-1) .. +7 (lane l-16's four of c1, then their
+// own), i.e. 8 consecutive columns starting at row8_col(lane).
+__device__ __forceinline__ Vec16 row8(uint32_t c0lo, uint32_t c0hi, uint32_t c1lo, uint32_t c1hi)
+{
+    const auto lo = __builtin_amdgcn_permlane16_swap(c0lo, c1lo, false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap(c0hi, c1hi, false, false);
+    return Vec16{lo[0], hi[0], lo[1], hi[1]};
+}
+
+// An accumulator block read out of its AGPRs where the epilogue uses it (the
+// vector ALU cannot take AGPR operands; left to itself the compiler copies
+// every accumulator to VGPRs at the start of the epilogue, which spills).
+__device__ __forceinline__ floatx4 acc_read(const floatx4& a)
+{
+    floatx4 r;
+    asm volatile("v_accvgpr_read_b32 %0, %4\n\tv_accvgpr_read_b32 %1, %5\n\t"
+                 "v_accvgpr_read_b32 %2, %6\n\tv_accvgpr_read_b32 %3, %7"
+                 : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3])
+                 : "a"(a[0]), "a"(a[1]), "a"(a[2]), "a"(a[3]));
+    return r;
+}
+
+__device__ __forceinline__ int row8_col(int lane)
+{
+    const int g = lane >> 4;
+    return 8 * (g >> 1) + 16 * (g & 1);
+}
 
 template <int BM, int BN, int WM, int WN>
 struct FragReader16 {
@@ -355,7 +402,7 @@ struct FragReader16 {
 // with RG = 0, its B fragments; only the tile's last stage (`last`, whose
 // next stage starts the next tile) reads them all. An expert's ragged last
 // m-tile then costs far fewer LDS reads than a full one.
-template <int BM, int BN, int WM, int WN, int A_INS, int B_INS, int RG>
+template <int BM, int BN, int WM, int WN, int A_INS, int B_INS, int RG, bool SW>
 __device__ __forceinline__ void stage16(const i32x4& ra, const LoadSrc<A_INS>& ls, uint32_t ld_lds, int KB, int wv,
                                         uint32_t lane16, const Stage<BM, BN, false>* st,
                                         const Stage<BM, BN, false>* st_next, int wm, int wn, int lane,
@@ -377,7 +424,8 @@ __device__ __forceinline__ void stage16(const i32x4& ra, const LoadSrc<A_INS>& l
         const int j = m / MH, i = m % MH;
         if ((i >> 1) < RG) {
             floatx4& c = acc[i >> 1][j >> 1].q[(i & 1) * 2 + (j & 1)];
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], c, 0, 0, 0);
+            c = SW ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], c, 0, 0, 0)
+                   : __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], c, 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -402,7 +450,8 @@ __device__ __forceinline__ void stage16(const i32x4& ra, const LoadSrc<A_INS>& l
         const int j = m / MH, i = MH + m % MH;
         if ((i >> 1) < RG) {
             floatx4& c = acc[i >> 1][j >> 1].q[(i & 1) * 2 + (j & 1)];
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], c, 0, 0, 0);
+            c = SW ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], c, 0, 0, 0)
+                   : __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], c, 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
         if (m < MH && (FULL || (m >> 1) < RG || last)) {  // the upper-row A fragments are free after the first half
@@ -673,7 +722,7 @@ __device__ __forceinline__ void tile_stages(const i32x4& ra, const LoadSrc<A_INS
 }
 
 // tile_stages for the M16 path (stage16 per stage).
-template <int BM, int BN, int WM, int WN, int A_INS, int B_INS, int RG>
+template <int BM, int BN, int WM, int WN, int A_INS, int B_INS, int RG, bool SW>
 __device__ __forceinline__ void tile_stages16(const i32x4& ra, const LoadSrc<A_INS>& cs, int nkt, bool has_nxt,
                                               const i32x4& nrb, int nkt0, const uint32_t (&cpart)[A_INS],
                                               uint32_t Kbytes, int KB, int wv, uint32_t lane16,
@@ -699,7 +748,7 @@ __device__ __forceinline__ void tile_stages16(const i32x4& ra, const LoadSrc<A_I
         }
         const int bl = b + kAhead >= kRing ? b + kAhead - kRing : b + kAhead;
         const int bn = b + 1 >= kRing ? 0 : b + 1;
-        stage16<BM, BN, WM, WN, A_INS, B_INS, RG>(ra, ls, ring0 + (uint32_t)bl * kStageBytes, KB, wv, lane16,
+        stage16<BM, BN, WM, WN, A_INS, B_INS, RG, SW>(ra, ls, ring0 + (uint32_t)bl * kStageBytes, KB, wv, lane16,
                                                  &ring.st[b], &ring.st[bn], wm, wn, lane, fa, fb, acc, j == nkt - 1);
         b = bn;
     } while (++j < nkt);
@@ -805,6 +854,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     constexpr int B_INS = (BN / 32) * (F8 ? 1 : 2) / 4;  // weight blocks per wave per stage
     constexpr int NLD = A_INS + B_INS;
     constexpr bool EPBUF = (GATE_UP || YB) && F8;        // bf16 epilogue outside the ring
+    // M16 path: transposed accumulator blocks (weight fragment as the MFMA's
+    // first operand) for the epilogues that store bf16 rows straight from the
+    // accumulators; the fp32 partial sums keep the plain layout (their 4-byte
+    // stores measured faster than 16-byte ones of the transposed blocks).
+    constexpr bool SW = GATE_UP || YB;
     static_assert((BM / WM) * WAVES_N == kThreads / kWave, "4 waves");
     static_assert(A_INS * 4 * 16 == BM && B_INS * 4 == (BN / 32) * (F8 ? 1 : 2), "stage split over 4 waves");
     static_assert(!GATE_UP || (NI % 2 == 0 && WN % 64 == 0), "gate/up pairs per wave");
@@ -989,7 +1043,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                                                                  Kbytes, KB, wv, lane16, ring, ring0, b, wm, wn,
                                                                  lane, qa, qb, sa, sb, held, acc);
             else if constexpr (M16)
-                tile_stages16<BM, BN, WM, WN, A_INS, B_INS, GG>(ra, cs, cur.nkt, has_nxt, nrb, nxt.kt0, cpart, Kbytes,
+                tile_stages16<BM, BN, WM, WN, A_INS, B_INS, GG, SW>(ra, cs, cur.nkt, has_nxt, nrb, nxt.kt0, cpart, Kbytes,
                                                                 KB, wv, lane16, ring, ring0, b, wm, wn, lane, fa16,
                                                                 fb16, held, acc);
             else
@@ -1066,7 +1120,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             const int lq = M16 ? (lane >> 4) : (lane >> 5);
             int rbase = wm * WM + 4 * lq;
             asm volatile("" : "+v"(rbase));
-            if constexpr (GATE_UP) {
+            if constexpr (GATE_UP && M16) {
+                // Straight from the accumulators (transposed blocks): per
+                // 32-row group, gate/up block pair and 16-row half, each lane
+                // applies SiLU(g)*u to its four columns of both 16x16 blocks,
+                // rounds them to bf16, and after one register swap between
+                // neighbouring 16-lane groups stores 8 consecutive values of
+                // its row with one 16-byte store.
+                static_assert(BN == 256 && WN == 128 && NI == 4, "gate/up epilogue layout");
+                uint16_t* H = (uint16_t*)g.out;
+                int rl = wm * WM + (lane & 15);
+                asm volatile("" : "+v"(rl));
+                const int c8 = row8_col(lane);
+#pragma unroll
+                for (int i = 0; i < MI; ++i) {
+                    if (PARTIAL && i >= RG)  // padding rows only: nothing to store
+                        continue;
+#pragma unroll
+                    for (int jp = 0; jp < NI; jp += 2) {
+#pragma unroll
+                        for (int ri = 0; ri < 2; ++ri) {
+                            uint32_t d[2][2];
+#pragma unroll
+                            for (int cj = 0; cj < 2; ++cj) {
+                                const floatx4 gv = acc_read(acc[i][jp].q[2 * ri + cj]);
+                                const floatx4 uv = acc_read(acc[i][jp + 1].q[2 * ri + cj]);
+                                d[cj][0] = bf16_pair(silu_rcp(gv[0]) * uv[0], silu_rcp(gv[1]) * uv[1]);
+                                d[cj][1] = bf16_pair(silu_rcp(gv[2]) * uv[2], silu_rcp(gv[3]) * uv[3]);
+                            }
+                            const Vec16 v = row8(d[0][0], d[0][1], d[1][0], d[1][1]);
+                            const int row = min(rl + i * 32 + ri * 16, cur.rows - 1);
+                            const int col = (cur.n * BN + wn * WN + jp * 32) / 2 + c8;
+                            *(Vec16*)(H + (int64_t)(cur.row0 + row) * g.f + col) = v;
+                            __builtin_amdgcn_sched_barrier(0);  // one segment at a time
+                        }
+                    }
+                }
+            } else if constexpr (GATE_UP) {
                 // Through LDS, one (32-row group, gate/up block pair) at a time:
                 // the accumulators go from AGPRs straight into this wave's 8 KiB
                 // of the ring slot the tile's last stage used (free until the
@@ -1096,25 +1186,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                         continue;
 #pragma unroll
                     for (int jp = 0; jp < NI; jp += 2) {
-                        if constexpr (M16) {
 #pragma unroll
-                            for (int c = 0; c < 4; ++c)  // 16x16 block (c/2, c%2) of the region
-#pragma unroll
-                                for (int q = 0; q < 4; ++q) {
-                                    const int r = 16 * (c >> 1) + 4 * (lane >> 4) + q;
-                                    const int cc = 16 * (c & 1) + (lane & 15);
-                                    const int o = r * 32 + (((cc >> 2) ^ (r & 7)) << 2) + (cc & 3);
-                                    ep[o] = acc[i][jp].q[c][q];
-                                    ep[1024 + o] = acc[i][jp + 1].q[c][q];
-                                }
-                        } else {
-#pragma unroll
-                            for (int q = 0; q < 16; ++q) {
-                                const int r = wr + 8 * (q / 4) + (q % 4);
-                                const int o = r * 32 + (((wc >> 2) ^ (r & 7)) << 2) + (wc & 3);
-                                ep[o] = acc[i][jp][q];
-                                ep[1024 + o] = acc[i][jp + 1][q];
-                            }
+                        for (int q = 0; q < 16; ++q) {
+                            const int r = wr + 8 * (q / 4) + (q % 4);
+                            const int o = r * 32 + (((wc >> 2) ^ (r & 7)) << 2) + (wc & 3);
+                            ep[o] = acc[i][jp][q];
+                            ep[1024 + o] = acc[i][jp + 1][q];
                         }
                         uint32_t hv[8];
 #pragma unroll
@@ -1142,7 +1219,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 }
             } else {
                 float* Ys = (float*)g.out + (int64_t)cur.s * g.A_max * g.d;
-                if constexpr (YB) {
+                if constexpr (YB && M16) {
+                    // bf16 rows straight from the accumulators, as the M16
+                    // gate/up epilogue: per 32-row group, 32-column block and
+                    // 16-row half one register swap and one 16-byte store of 8
+                    // consecutive values of the lane's row.
+                    static_assert(NI % 2 == 0, "bf16 outputs: column block pairs");
+                    uint16_t* Yb = (uint16_t*)g.out;
+                    int rl = wm * WM + (lane & 15);
+                    asm volatile("" : "+v"(rl));
+                    const int c8 = row8_col(lane);
+#pragma unroll
+                    for (int i = 0; i < MI; ++i) {
+                        if (PARTIAL && i >= RG)  // padding rows only: nothing to store
+                            continue;
+#pragma unroll
+                        for (int j = 0; j < NI; ++j)
+#pragma unroll
+                            for (int ri = 0; ri < 2; ++ri) {
+                                const floatx4 v0 = acc_read(acc[i][j].q[2 * ri]);
+                                const floatx4 v1 = acc_read(acc[i][j].q[2 * ri + 1]);
+                                const Vec16 v = row8(bf16_pair(v0[0], v0[1]), bf16_pair(v0[2], v0[3]),
+                                                     bf16_pair(v1[0], v1[1]), bf16_pair(v1[2], v1[3]));
+                                const int row = min(rl + i * 32 + ri * 16, cur.rows - 1);
+                                const int col = cur.n * BN + wn * WN + j * 32 + c8;
+                                *(Vec16*)(Yb + (int64_t)(cur.row0 + row) * g.d + col) = v;
+                                __builtin_amdgcn_sched_barrier(0);  // one segment at a time
+                            }
+                    }
+                } else if constexpr (YB) {
                     // bf16 rows through LDS, as the gate/up epilogue: two
                     // 32x32 accumulator blocks at a time go into this wave's
                     // 8 KiB of the free ring slot (8-bit weights: of the
@@ -1169,25 +1274,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                             continue;
 #pragma unroll
                         for (int jp = 0; jp < NI; jp += 2) {
-                            if constexpr (M16) {
 #pragma unroll
-                                for (int c = 0; c < 4; ++c)  // 16x16 block (c/2, c%2) of the region
-#pragma unroll
-                                    for (int q = 0; q < 4; ++q) {
-                                        const int r = 16 * (c >> 1) + 4 * (lane >> 4) + q;
-                                        const int cc = 16 * (c & 1) + (lane & 15);
-                                        const int o = r * 32 + (((cc >> 2) ^ (r & 7)) << 2) + (cc & 3);
-                                        ep[o] = acc[i][jp].q[c][q];
-                                        ep[1024 + o] = acc[i][jp + 1].q[c][q];
-                                    }
-                            } else {
-#pragma unroll
-                                for (int q = 0; q < 16; ++q) {
-                                    const int r = wr + 8 * (q / 4) + (q % 4);
-                                    const int o = r * 32 + (((wc >> 2) ^ (r & 7)) << 2) + (wc & 3);
-                                    ep[o] = acc[i][jp][q];
-                                    ep[1024 + o] = acc[i][jp + 1][q];
-                                }
+                            for (int q = 0; q < 16; ++q) {
+                                const int r = wr + 8 * (q / 4) + (q % 4);
+                                const int o = r * 32 + (((wc >> 2) ^ (r & 7)) << 2) + (wc & 3);
+                                ep[o] = acc[i][jp][q];
+                                ep[1024 + o] = acc[i][jp + 1][q];
                             }
                             const int row = min(rbase - 4 * lq + i * 32 + rr, cur.rows - 1);
 #pragma unroll
@@ -1219,7 +1311,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 for (int i = 0; i < MI; ++i) {
                     if (PARTIAL && i >= RG)  // padding rows only: nothing to store
                         continue;
-                    if constexpr (M16) {
+                    if constexpr (M16) {  // plain (not transposed) blocks: lane l holds column l%16
 #pragma unroll
                         for (int ri = 0; ri < 2; ++ri)
 #pragma unroll
@@ -1305,9 +1397,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 // The same persistent tile walk and 256x256 tiles on 4 waves of 128x128 as
 // grouped_gemm_kernel's M16 path, but each LDS stage holds 64 k: A rows of
 // 128 bytes (whole cache lines; one buffer->LDS load covers 8 rows) and four
-// 16-k weight blocks per 32 weight rows. Two 64 KiB stages form the ring, and
-// the gate/up and bf16-row epilogues stage through a 32 KiB buffer of their
-// own. Per stage and wave: 16 loads, 32 fragment reads, 128 MFMAs, one
+// 16-k weight blocks per 32 weight rows. Two 64 KiB stages form the ring;
+// the accumulator blocks are transposed (SW) and the epilogues store straight
+// from them, without LDS. Per stage and wave: 16 loads, 32 fragment reads, 128 MFMAs, one
 // barrier. Schedule of stage s (slot s%2):
 //   first half:  k-step 0 MFMAs (fragments read in stage s-1), reads of this
 //                stage's k-step 1 fragments;
@@ -1325,9 +1417,8 @@ struct Stage64 {
 };
 struct Ring64 {
     Stage64 st[2];
-    float ep[4 * 2048];
 };
-static_assert(sizeof(Ring64) == 160 * 1024, "LDS");
+static_assert(sizeof(Ring64) == 128 * 1024, "LDS");
 
 __device__ __forceinline__ int swz64(int r, int c)
 {
@@ -1373,7 +1464,7 @@ struct Frag64 {
     }
 };
 
-template <int RG>
+template <int RG, bool SW>
 __device__ __forceinline__ void stage64(const i32x4& ra, const Src64& ls, uint32_t ld_lds, int KB, int wv,
                                         uint32_t lane16, const Stage64* st, const Stage64* st_next, int wm, int wn,
                                         int lane, bf16x8 (&fa)[8], bf16x8 (&fb)[8], Acc4 (&acc)[4][4])
@@ -1386,7 +1477,8 @@ __device__ __forceinline__ void stage64(const i32x4& ra, const Src64& ls, uint32
         const int j = m / 8, i = m % 8;
         if ((i >> 1) < RG) {
             floatx4& c = acc[i >> 1][j >> 1].q[(i & 1) * 2 + (j & 1)];
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], c, 0, 0, 0);
+            c = SW ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], c, 0, 0, 0)
+                   : __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], c, 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -1409,7 +1501,8 @@ __device__ __forceinline__ void stage64(const i32x4& ra, const Src64& ls, uint32
         const int j = m / 8, i = m % 8;
         if ((i >> 1) < RG) {
             floatx4& c = acc[i >> 1][j >> 1].q[(i & 1) * 2 + (j & 1)];
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga[i], gb[j], c, 0, 0, 0);
+            c = SW ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(gb[j], ga[i], c, 0, 0, 0)
+                   : __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga[i], gb[j], c, 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -1431,7 +1524,7 @@ __device__ __forceinline__ void stage64(const i32x4& ra, const Src64& ls, uint32
 // The K stages of one tile, continuing the stream: stage j multiplies slot b
 // and loads stream stage j + 2 (this tile's, the next tile's first two, or,
 // past the last tile, a reload of this tile's last stage that nobody reads).
-template <int RG>
+template <int RG, bool SW>
 __device__ __forceinline__ void tile_stages64(const i32x4& ra, const Src64& cs, int nkt, bool has_nxt,
                                               const i32x4& nrb, int nkt0, const uint32_t (&cpart)[2],
                                               uint32_t Kbytes, int KB, int wv, uint32_t lane16, Ring64& ring,
@@ -1453,7 +1546,7 @@ __device__ __forceinline__ void tile_stages64(const i32x4& ra, const Src64& cs, 
         } else {
             ls.kt = cs.kt + nkt - 1;
         }
-        stage64<RG>(ra, ls, ring0 + (uint32_t)b * (uint32_t)sizeof(Stage64), KB, wv, lane16, &ring.st[b],
+        stage64<RG, SW>(ra, ls, ring0 + (uint32_t)b * (uint32_t)sizeof(Stage64), KB, wv, lane16, &ring.st[b],
                     &ring.st[b ^ 1], wm, wn, lane, fa, fb, acc);
         b ^= 1;
     } while (++j < nkt);
@@ -1463,6 +1556,7 @@ template <bool GATE_UP, bool YB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void grouped_gemm64_kernel(GemmArgs g)
 {
     constexpr int BM = 256, BN = 256, WM = 128, WN = 128, MI = 4, NI = 4;
+    constexpr bool SW = true;  // transposed accumulator blocks (the epilogue below)
     constexpr int SM = GATE_UP ? 0 : 64;
     __shared__ Ring64 ring;
 
@@ -1570,7 +1664,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         const int RG = wrows <= 0 ? 0 : wrows <= 32 ? 1 : wrows <= 64 ? 2 : MI;
         auto run = [&](auto g_const) {
             constexpr int GG = decltype(g_const)::value;
-            tile_stages64<GG>(ra, cs, cur.nkt, has_nxt, nrb, nxt.kt0, cpart, Kbytes, KB, wv, lane16, ring, ring0, b,
+            tile_stages64<GG, SW>(ra, cs, cur.nkt, has_nxt, nrb, nxt.kt0, cpart, Kbytes, KB, wv, lane16, ring, ring0, b,
                               wm, wn, lane, fa, fb, held, acc);
         };
         if (RG == MI)
@@ -1599,76 +1693,57 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 nheld[q] = (uint32_t)row_src<GATE_UP>(g.perm, nn, slot[q]);
         }
 
-        // Epilogue through this wave's 8 KiB of ring.ep (no other wave uses
-        // it, so no barrier), as grouped_gemm_kernel's M16 epilogues.
+        // Epilogue straight from the accumulators (transposed 16x16 blocks:
+        // lane l holds token row l%16 and four consecutive output columns),
+        // as grouped_gemm_kernel's M16 epilogues: SiLU(g)*u or bf16 rows as
+        // 8 consecutive values per lane and 16-byte store after one register
+        // swap, fp32 partial sums as the lane's four columns per store.
         {
-            const int lq = lane >> 4;
-            int rbase = wm * WM + 4 * lq;
-            asm volatile("" : "+v"(rbase));
-            float* ep = ring.ep + wv * 2048;
-            const int rr = lane >> 1;
-            const int rc = (lane & 1) * 4;
+            int rl = wm * WM + (lane & 15);
+            asm volatile("" : "+v"(rl));
+            const int c8 = row8_col(lane);
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
                 if (i >= RG)
                     continue;
 #pragma unroll
-                for (int jp = 0; jp < NI; jp += 2) {
-#pragma unroll
-                    for (int c = 0; c < 4; ++c)
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const int r = 16 * (c >> 1) + 4 * (lane >> 4) + q;
-                            const int cc = 16 * (c & 1) + (lane & 15);
-                            const int o = r * 32 + (((cc >> 2) ^ (r & 7)) << 2) + (cc & 3);
-                            ep[o] = acc[i][jp].q[c][q];
-                            ep[1024 + o] = acc[i][jp + 1].q[c][q];
-                        }
-                    const int row = min(rbase - 4 * lq + i * 32 + rr, cur.rows - 1);
+                for (int ri = 0; ri < 2; ++ri) {
+                    const int row = min(rl + i * 32 + ri * 16, cur.rows - 1);
                     if constexpr (GATE_UP) {
-                        uint32_t hv[8];
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) {
-                            const int o = rr * 32 + (((rc + t) ^ (rr & 7)) << 2);
-                            const floatx4 gv = *(const floatx4*)(ep + o);
-                            const floatx4 uv = *(const floatx4*)(ep + 1024 + o);
-                            hv[2 * t] = (uint32_t)f32_to_bf16_bits(silu_rcp(gv[0]) * uv[0]) |
-                                        ((uint32_t)f32_to_bf16_bits(silu_rcp(gv[1]) * uv[1]) << 16);
-                            hv[2 * t + 1] = (uint32_t)f32_to_bf16_bits(silu_rcp(gv[2]) * uv[2]) |
-                                            ((uint32_t)f32_to_bf16_bits(silu_rcp(gv[3]) * uv[3]) << 16);
+                        for (int jp = 0; jp < NI; jp += 2) {
+                            uint32_t d[2][2];
+#pragma unroll
+                            for (int cj = 0; cj < 2; ++cj) {
+                                const floatx4 gv = acc_read(acc[i][jp].q[2 * ri + cj]);
+                                const floatx4 uv = acc_read(acc[i][jp + 1].q[2 * ri + cj]);
+                                d[cj][0] = bf16_pair(silu_rcp(gv[0]) * uv[0], silu_rcp(gv[1]) * uv[1]);
+                                d[cj][1] = bf16_pair(silu_rcp(gv[2]) * uv[2], silu_rcp(gv[3]) * uv[3]);
+                            }
+                            const int col = (cur.n * BN + wn * WN + jp * 32) / 2 + c8;
+                            *(Vec16*)((uint16_t*)g.out + (int64_t)(cur.row0 + row) * g.f + col) =
+                                row8(d[0][0], d[0][1], d[1][0], d[1][1]);
+                            __builtin_amdgcn_sched_barrier(0);  // one segment at a time
                         }
-                        const int col = (cur.n * BN + wn * WN + jp * 32) / 2 + rc * 4;
-                        Vec16* dst = (Vec16*)((uint16_t*)g.out + (int64_t)(cur.row0 + row) * g.f + col);
-                        dst[0] = Vec16{hv[0], hv[1], hv[2], hv[3]};
-                        dst[1] = Vec16{hv[4], hv[5], hv[6], hv[7]};
                     } else if constexpr (YB) {
 #pragma unroll
-                        for (int h = 0; h < 2; ++h) {
-                            uint32_t hv[8];
-#pragma unroll
-                            for (int t = 0; t < 4; ++t) {
-                                const int o = h * 1024 + rr * 32 + (((rc + t) ^ (rr & 7)) << 2);
-                                const floatx4 v = *(const floatx4*)(ep + o);
-                                hv[2 * t] = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
-                                hv[2 * t + 1] =
-                                    (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
-                            }
-                            const int col = cur.n * BN + wn * WN + (jp + h) * 32 + rc * 4;
-                            Vec16* dst = (Vec16*)((uint16_t*)g.out + (int64_t)(cur.row0 + row) * g.d + col);
-                            dst[0] = Vec16{hv[0], hv[1], hv[2], hv[3]};
-                            dst[1] = Vec16{hv[4], hv[5], hv[6], hv[7]};
+                        for (int j = 0; j < NI; ++j) {
+                            const floatx4 v0 = acc_read(acc[i][j].q[2 * ri]);
+                            const floatx4 v1 = acc_read(acc[i][j].q[2 * ri + 1]);
+                            const int col = cur.n * BN + wn * WN + j * 32 + c8;
+                            *(Vec16*)((uint16_t*)g.out + (int64_t)(cur.row0 + row) * g.d + col) =
+                                row8(bf16_pair(v0[0], v0[1]), bf16_pair(v0[2], v0[3]), bf16_pair(v1[0], v1[1]),
+                                     bf16_pair(v1[2], v1[3]));
+                            __builtin_amdgcn_sched_barrier(0);  // one segment at a time
                         }
                     } else {
-                        float* Ys = (float*)g.out + (int64_t)cur.s * g.A_max * g.d;
+                        float* yrow = (float*)g.out + (int64_t)cur.s * g.A_max * g.d +
+                                      (int64_t)(cur.row0 + row) * g.d + cur.n * BN + wn * WN + 4 * (lane >> 4);
 #pragma unroll
-                        for (int h = 0; h < 2; ++h)
+                        for (int j = 0; j < NI; ++j)
 #pragma unroll
-                            for (int t = 0; t < 4; ++t) {
-                                const int o = h * 1024 + rr * 32 + (((rc + t) ^ (rr & 7)) << 2);
-                                const floatx4 v = *(const floatx4*)(ep + o);
-                                const int col = cur.n * BN + wn * WN + (jp + h) * 32 + (rc + t) * 4;
-                                *(floatx4*)(Ys + (int64_t)(cur.row0 + row) * g.d + col) = v;
-                            }
+                            for (int cj = 0; cj < 2; ++cj)
+                                *(floatx4*)(yrow + j * 32 + 16 * cj) = acc[i][j].q[2 * ri + cj];
                     }
                 }
             }

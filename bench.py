@@ -302,10 +302,12 @@ def profile_fields(workload: str, kernel: str) -> dict:
 def gate_up_kernel_name(cfg, A: int, fp8: bool, q8: bool) -> str:
     """The tiled gate/up kernel the library picks for a call (the rule in
     api.cpp): 64-wide K stages for bf16 weights when the layer has at least
-    768 rows per expert on average (CMOE_K64 bit 0; bit 2 drops the row
-    condition), else the 32-wide kernel."""
+    768 rows per expert on average, or at most CMOE_M_ORDER_ROWS (384; the
+    layers in m-tile order) (CMOE_K64 bit 0; bit 2 drops the row condition),
+    else the 32-wide kernel."""
     k64 = int(os.environ.get("CMOE_K64", "1"))
-    if not fp8 and not q8 and (k64 & 1) and ((k64 & 4) or A >= 768 * cfg.E):
+    order_m = A <= int(os.environ.get("CMOE_M_ORDER_ROWS", "384")) * cfg.E
+    if not fp8 and not q8 and (k64 & 1) and ((k64 & 4) or order_m or A >= 768 * cfg.E):
         return "grouped_gemm64_kernel<true, false> (gate/up, 64-wide K stages)"
     return "grouped_gemm_kernel (gate/up" + (", fp8 MFMA" if q8 else "") + ")"
 

@@ -487,10 +487,12 @@ colibri_moe_status_t forward_impl(colibri_moe* h, const void* x, int32_t T, void
                     c.n_experts, c.top_k, c.d_model, c.d_ff, order_m ? -8 : h->group_n_gu, 1, h->cus};
         gu.xcd_map = h->xcd_map & 1;
         // 64-wide K stages for layers of at least three m-tiles per expert on
-        // average (mixtral, one big expert); with fewer (fine-grained 256
-        // rows, skewed 512) they measured 0-4% slower than 32-wide stages
-        // (CMOE_K64 bit 2 drops this condition)
-        gu.k64 = (h->k64 & 1) && ((h->k64 & 4) || (int64_t)A >= (int64_t)768 * c.n_experts);
+        // average (mixtral, one big expert) and for layers in m-tile order
+        // (many experts of one or two m-tiles: fine-grained, 1.8% less layer
+        // time); in between (skewed, 512 rows on average but two experts of
+        // ~15 k rows and 62 of at most 56) they measured 2% slower than
+        // 32-wide stages (CMOE_K64 bit 2 drops this condition)
+        gu.k64 = (h->k64 & 1) && ((h->k64 & 4) || order_m || (int64_t)A >= (int64_t)768 * c.n_experts);
         CMOE_HIP(bf ? launch_gate_up_bf16(gu, s) : launch_gate_up_f32(gu, s));
         if (tm) {
             CMOE_HIP(hipEventRecord(h->ev[3], s));

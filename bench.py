@@ -491,8 +491,12 @@ def run_workload(name: str, args, fp8: bool, q8: bool) -> dict:
     layer_tflops = cfg.flops() / t / 1e12
     layer_gbs = layer_bytes(cfg, counts, fp8) / t / 1e9
     # The library takes its small-batch (weight streaming) path for bf16 calls
-    # with at most CMOE_DECODE_MAX_A (default 256) assignments: HBM-bound.
-    small_batch = cfg.dtype == "bf16" and A <= int(os.environ.get("CMOE_DECODE_MAX_A", "256"))
+    # with at most CMOE_DECODE_MAX_A (default 2048) assignments when no expert
+    # holds more than CMOE_DECODE_MAX_ROWS rows (default 48, 32 with 8-bit
+    # weights; 0: no such test): HBM-bound.
+    max_rows = int(os.environ.get("CMOE_DECODE_MAX_ROWS", "32" if fp8 else "48"))
+    small_batch = (cfg.dtype == "bf16" and A <= int(os.environ.get("CMOE_DECODE_MAX_A", "2048"))
+                   and (max_rows == 0 or int(np.max(counts)) <= max_rows))
     dom = "gate_up_gemm"  # carries 2/3 of the flops and of the weight bytes
     prof_key = name + ("-w8a8" if q8 else "-fp8" if fp8 else "")
     traffic = profiled_traffic(prof_key, dom)
@@ -501,7 +505,7 @@ def run_workload(name: str, args, fp8: bool, q8: bool) -> dict:
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                 "kernel": ("decode_gemm_q8_kernel<true>" if q8 else "decode_gemm_f8_kernel<true>" if fp8
-                           else "decode_gemm_kernel<true>") + " (gate/up)"}
+                           else f"decode_gemm_kernel<true, {1 if cfg.T <= 32 else 2}>") + " (gate/up)"}
     else:
         achieved = gemm_flops_per_assignment(cfg)[dom] * A / (stage_ms[dom] * 1e-3) / 1e12
         gu_peak = PEAK_FP8_TFLOPS if q8 else peak_mm

@@ -79,6 +79,7 @@ struct colibri_moe {
     bool fuse_combine;  // bf16 tiled path: combine in the down GEMM's epilogue
     int cus;        // compute units of the device (persistent GEMM grid)
     int dec_max_a;  // bf16 calls with T*k <= dec_max_a take the small-batch path
+    int dec_gate_rows;  // ... when no expert holds more rows (0: always; see create)
     int dec_split_gu, dec_split_dn;  // its K slices (gate/up, down)
 };
 
@@ -234,7 +235,8 @@ size_t layout_workspace(const colibri_moe* h, int64_t T, bool up_to, uint8_t* ba
     // (a call takes the small-batch path when A <= dec_max_a)
     if (c.dtype == COLIBRI_MOE_BF16 && h->dec_max_a > 0 && (up_to || A <= (size_t)h->dec_max_a)) {
         const size_t ad = std::min(A, (size_t)h->dec_max_a);
-        ys_floats = std::max(ys_floats, (size_t)h->dec_split_gu * ad * 2 * f);
+        if (!h->dec_fuse_silu)  // else the gate/up kernel writes H itself
+            ys_floats = std::max(ys_floats, (size_t)h->dec_split_gu * ad * 2 * f);
         ys_floats = std::max(ys_floats, (size_t)h->dec_split_dn * ad * d);
     }
     const size_t o_ys = cv.take(ys_floats * sizeof(float));
@@ -390,13 +392,18 @@ colibri_moe_status_t colibri_moe_init(colibri_moe_t** out, const colibri_moe_con
     }
     setup_static_scratch(h->device);
     // Small-batch path (bf16): calls with at most CMOE_DECODE_MAX_A
-    // assignments (default 256; 0 turns the path off). Results do not depend
-    // on the path beyond fp32 summation order.
+    // assignments (default 2048; 0 turns the path off) and, for calls of
+    // more than CMOE_DECODE_MAX_ROWS tokens (default 48, 32 with 8-bit
+    // weights, whose kernels take 32 rows per weight pass; 0: no such test),
+    // only when no expert holds more rows than that (decided on the device).
+    // Results do not depend on the path beyond fp32 summation order.
     h->dec_max_a = 0;
+    h->dec_gate_rows = 0;
     h->dec_split_gu = h->dec_split_dn = 1;
     if (cfg->dtype == COLIBRI_MOE_BF16) {
         const int64_t amax = (int64_t)cfg->max_tokens * cfg->top_k;
-        h->dec_max_a = (int)std::min<int64_t>(amax, env_int("CMOE_DECODE_MAX_A", 256, 0, 1 << 16));
+        h->dec_max_a = (int)std::min<int64_t>(amax, env_int("CMOE_DECODE_MAX_A", 2048, 0, 1 << 16));
+        h->dec_gate_rows = env_int("CMOE_DECODE_MAX_ROWS", h->fp8 ? 32 : 48, 0, 1 << 16);
         const int waves = cmoe::decode_waves(h->cus);
         // k step of the small-batch kernels: 16 (bf16 weights), 32 (8-bit
         // weights), 64 (8-bit token rows, gate/up only)
@@ -461,28 +468,26 @@ colibri_moe_status_t forward_impl(colibri_moe* h, const void* x, int32_t T, void
         CMOE_HIP(hipEventRecord(h->ev[2], s));
 
     const int A = T * c.top_k;
-    int split = 1;
-    bool fused = false;    // combine done by the down GEMM
-    int ys_bf16 = 0;       // expert outputs stored as bf16
-    if (bf && A <= h->dec_max_a) {
-        // small-batch path: weight streaming with K slices, then the slice sum
-        // and SiLU(g)*u
+    // Path choice. Calls with A <= dec_max_a go to the small-batch kernels
+    // (weight streaming: K slices, then the slice sum and SiLU(g)*u), the
+    // others to the tiled grouped GEMMs. The small-batch kernels win while
+    // every expert holds few rows, which the host cannot see (skewed routing
+    // puts most tokens on a few experts): a call that may hold an expert with
+    // more than dec_gate_rows rows (T > dec_gate_rows) enqueues both paths,
+    // and each kernel takes or leaves the call from offsets on the device.
+    const bool small = bf && A <= h->dec_max_a;
+    const int gate = small && h->dec_gate_rows > 0 && T > h->dec_gate_rows ? h->dec_gate_rows : 0;
+    const bool tiled = !small || gate > 0;
+    const bool order_m = (int64_t)A <= (int64_t)h->order_m_rows * c.n_experts;
+    if (small) {
         DecodeArgs gu{q8 ? (const void*)ws.xq : x, h->w_gu, h->s_gu, q8 ? ws.xsc : nullptr, ws.Ys, offsets, perm,
                       A, c.n_experts, c.d_model, c.d_ff, h->dec_split_gu};
         gu.h = h->dec_fuse_silu ? (uint16_t*)ws.H : nullptr;
+        gu.max_rows = T;
+        gu.gate_rows = gate;
         CMOE_HIP(launch_decode_gemm(gu, 1, h->cus, s));
-        if (tm)
-            CMOE_HIP(hipEventRecord(h->ev[3], s));
-        if (!h->dec_fuse_silu)
-            CMOE_HIP(launch_decode_silu(ws.Ys, ws.H, A, c.d_ff, h->dec_split_gu, s));
-        if (tm)
-            CMOE_HIP(hipEventRecord(h->ev[4], s));
-        DecodeArgs dn{ws.H, h->w_d, h->s_d, nullptr, ws.Ys, offsets, perm,
-                      A, c.n_experts, c.d_model, c.d_ff, h->dec_split_dn};
-        CMOE_HIP(launch_decode_gemm(dn, 0, h->cus, s));
-        split = h->dec_split_dn;
-    } else {
-        const bool order_m = (int64_t)A <= (int64_t)h->order_m_rows * c.n_experts;
+    }
+    if (tiled) {
         GemmArgs gu{q8 ? (const void*)ws.xq : x, h->w_gu, h->s_gu, q8 ? ws.xsc : nullptr, ws.H, offsets, perm, A,
                     c.n_experts, c.top_k, c.d_model, c.d_ff, order_m ? -8 : h->group_n_gu, 1, h->cus};
         gu.xcd_map = h->xcd_map & 1;
@@ -493,15 +498,32 @@ colibri_moe_status_t forward_impl(colibri_moe* h, const void* x, int32_t T, void
         // ~15 k rows and 62 of at most 56) they measured 2% slower than
         // 32-wide stages (CMOE_K64 bit 2 drops this condition)
         gu.k64 = (h->k64 & 1) && ((h->k64 & 4) || order_m || (int64_t)A >= (int64_t)768 * c.n_experts);
+        gu.skip_rows = gate;
         CMOE_HIP(bf ? launch_gate_up_bf16(gu, s) : launch_gate_up_f32(gu, s));
-        if (tm) {
-            CMOE_HIP(hipEventRecord(h->ev[3], s));
-            CMOE_HIP(hipEventRecord(h->ev[4], s));
-        }
+    }
+    if (tm)
+        CMOE_HIP(hipEventRecord(h->ev[3], s));
+    if (small && !h->dec_fuse_silu)
+        CMOE_HIP(launch_decode_silu(ws.Ys, ws.H, A, c.d_ff, h->dec_split_gu, offsets, c.n_experts, gate, s));
+    if (tm)
+        CMOE_HIP(hipEventRecord(h->ev[4], s));
+
+    int split = 1;
+    bool fused = false;    // combine done by the down GEMM
+    int ys_bf16 = 0;       // expert outputs stored as bf16
+    if (small) {
+        DecodeArgs dn{ws.H, h->w_d, h->s_d, nullptr, ws.Ys, offsets, perm,
+                      A, c.n_experts, c.d_model, c.d_ff, h->dec_split_dn};
+        dn.max_rows = T;
+        dn.gate_rows = gate;
+        CMOE_HIP(launch_decode_gemm(dn, 0, h->cus, s));
+        split = h->dec_split_dn;
+    }
+    if (tiled) {
         split = bf ? down_split_bf16(A, c.n_experts, c.d_model, c.d_ff, h->cus, 0) : 1;
         GemmArgs dn{ws.H, h->w_d, h->s_d, nullptr, ws.Ys, offsets, perm, A,
                     c.n_experts, c.top_k, c.d_model, c.d_ff, order_m ? -8 : h->group_n_dn, split, h->cus};
-        if (bf && h->ccnt && fused_ok) {
+        if (bf && h->ccnt && fused_ok && gate == 0) {
             dn.cnt = h->ccnt;
             dn.inv = inv;
             dn.topw = topw;
@@ -513,6 +535,7 @@ colibri_moe_status_t forward_impl(colibri_moe* h, const void* x, int32_t T, void
         dn.ys_bf16 = bf && split == 1 && !fused;
         dn.xcd_map = (h->xcd_map >> 1) & 1;
         dn.k64 = (h->k64 >> 1) & 1;
+        dn.skip_rows = gate;
         ys_bf16 = dn.ys_bf16;
         CMOE_HIP(bf ? launch_down_bf16(dn, s) : launch_down_f32(dn, s));
     }
@@ -521,6 +544,12 @@ colibri_moe_status_t forward_impl(colibri_moe* h, const void* x, int32_t T, void
 
     if (!fused) {
         CombineArgs ca{ws.Ys, inv, topw, y, T, c.top_k, c.d_model, split, bf ? 1 : 0, ys_bf16};
+        if (gate > 0) {
+            ca.offsets = offsets;
+            ca.E = c.n_experts;
+            ca.gate_rows = gate;
+            ca.small_split = h->dec_split_dn;
+        }
         CMOE_HIP(launch_combine(ca, s));
     }
     if (tm)

@@ -112,11 +112,20 @@ __global__ __launch_bounds__(256) void combine_b16_kernel(CombineArgs g)
     }
 }
 
-// Any k and number of partials (the small-batch path's K slices).
+// Any k and number of partials (the small-batch path's K slices), and calls
+// that enqueued both GEMM paths: the Ys format of the path the device chose
+// (bf16 rows widened exactly, or fp32 partials added in order). The same
+// arithmetic as the kernels above, so the same results bit for bit.
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs g)
 {
     const int64_t groups = (int64_t)g.T * (g.d / 4);
     const int64_t stride = (int64_t)g.T * g.k * g.d;
+    int split = g.split;
+    bool ysb = g.ys_bf16 != 0;
+    if (g.gate_rows > 0 && max_expert_rows(g.offsets, g.E) <= g.gate_rows) {
+        split = g.small_split;
+        ysb = false;
+    }
     for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < groups;
          idx += (int64_t)gridDim.x * blockDim.x) {
         const int64_t t = idx / (g.d / 4);
@@ -124,14 +133,22 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs g)
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int j = 0; j < g.k; ++j) {
             const float wj = g.w[t * g.k + j];
-            const float* row = g.ys + (int64_t)g.inv[t * g.k + j] * g.d + o;
-            float4 v = *(const float4*)row;
-            for (int s = 1; s < g.split; ++s) {
-                const float4 u = *(const float4*)(row + s * stride);
-                v.x += u.x;
-                v.y += u.y;
-                v.z += u.z;
-                v.w += u.w;
+            const int64_t pos = (int64_t)g.inv[t * g.k + j] * g.d + o;
+            float4 v;
+            if (ysb) {
+                const uint2 b = *(const uint2*)((const uint16_t*)g.ys + pos);
+                v = make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u),
+                                __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xFFFF0000u));
+            } else {
+                const float* row = g.ys + pos;
+                v = *(const float4*)row;
+                for (int s = 1; s < split; ++s) {
+                    const float4 u = *(const float4*)(row + s * stride);
+                    v.x += u.x;
+                    v.y += u.y;
+                    v.z += u.z;
+                    v.w += u.w;
+                }
             }
             acc.x = fmaf(wj, v.x, acc.x);
             acc.y = fmaf(wj, v.y, acc.y);
@@ -169,6 +186,10 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s)
     if (blocks > 8192)
         blocks = 8192;
     const dim3 grid((unsigned)blocks);
+    if (a.gate_rows > 0) {  // format known on the device only
+        hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
     if (launch_ks<1>(a, grid, s) || launch_ks<2>(a, grid, s) || launch_ks<3>(a, grid, s) ||
         launch_ks<4>(a, grid, s) || launch_ks<5>(a, grid, s) || launch_ks<6>(a, grid, s) ||
         launch_ks<7>(a, grid, s) || launch_ks<8>(a, grid, s))

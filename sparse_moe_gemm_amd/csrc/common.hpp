@@ -57,6 +57,21 @@ __device__ __forceinline__ float silu(float z)
     return z / (1.0f + __expf(-z));
 }
 
+// Most rows any expert holds in this call (offsets [E+1]), the same value in
+// every lane of the wave. Calls that enqueue both GEMM paths let each kernel
+// decide from it, on the device, whether the call is its own.
+__device__ __forceinline__ int max_expert_rows(const int32_t* offsets, int E)
+{
+    const int lane = threadIdx.x % kWave;
+    int m = 0;
+    for (int e = lane; e < E; e += kWave)
+        m = max(m, offsets[e + 1] - offsets[e]);
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d >>= 1)
+        m = max(m, __shfl_xor(m, d, kWave));
+    return __builtin_amdgcn_readfirstlane(m);
+}
+
 // ---------------------------------------------------------------------------
 // Host-side launchers (each defined in the .hip file of its kernel).
 // All enqueue on `s` and return the launch status.
@@ -129,6 +144,10 @@ struct GemmArgs {
     // bf16 weights, 256-row weight tiles, no fused combine: 1 runs the
     // 64-wide K stage kernel (grouped_gemm64_kernel)
     int k64;
+    // > 0: the call also went to the small-batch kernels, which take it when
+    // no expert holds more than skip_rows rows; the tiled kernel then does
+    // nothing (0: always run)
+    int skip_rows;
 };
 hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t s);
 hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t s);
@@ -156,6 +175,14 @@ struct DecodeArgs {
     // gate/up with split == 1: H [A][f] bf16 written directly as
     // SiLU(g)*u (no partials, no separate slice-sum pass); else null
     uint16_t* h;
+    // most rows one expert can hold in this call (T: a token picks an
+    // expert at most once); 1..32 lets the bf16 kernel skip its code for
+    // token-group pairs, 0 means not known
+    int max_rows;
+    // > 0: the call also went to the tiled kernels, which take it when some
+    // expert holds more than gate_rows rows; this kernel then does nothing
+    // (0: always run)
+    int gate_rows;
 };
 // Waves a decode launch runs on `cus` compute units.
 int decode_waves(int cus);
@@ -163,8 +190,10 @@ int decode_waves(int cus);
 // that steps through K in kstep-wide steps (16 for bf16 weights, 32 for fp8).
 int decode_split(int E, int N, int K, int kstep, int waves, int max_split);
 hipError_t launch_decode_gemm(const DecodeArgs& a, int gate_up, int cus, hipStream_t s);
-// H = SiLU(sum of gate slices) * (sum of up slices), bf16.
-hipError_t launch_decode_silu(const float* part, void* H, int A, int f, int S, hipStream_t s);
+// H = SiLU(sum of gate slices) * (sum of up slices), bf16; gate_rows as in
+// DecodeArgs (offsets [E+1]).
+hipError_t launch_decode_silu(const float* part, void* H, int A, int f, int S, const int32_t* offsets, int E,
+                              int gate_rows, hipStream_t s);
 
 // 8-bit expert weights (quant_fp8.hip). Row scales of bf16 weight rows: rows
 // of [rows][cols], or with w1 != null the interleaved gate/up rows of
@@ -193,6 +222,14 @@ struct CombineArgs {
     int split;          // number of partials, at ys + s*T*k*d
     int bf16_out;
     int ys_bf16;        // the expert outputs are bf16 (split == 1)
+    // Calls that enqueue both GEMM paths (gate_rows > 0): when no expert
+    // holds more than gate_rows rows (offsets [E+1]) the small-batch kernels
+    // wrote Ys, as small_split fp32 partials; otherwise the tiled ones, as
+    // split and ys_bf16 say.
+    const int32_t* offsets;
+    int E;
+    int gate_rows;
+    int small_split;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 

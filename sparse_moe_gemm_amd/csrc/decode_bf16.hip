@@ -10,12 +10,14 @@
 //   - a work item is (expert e, two 32-row weight blocks nb and nb+1, K
 //     slice s); every wave takes items w, w + W, ... (W = waves in the grid)
 //     on its own;
-//   - for each 32-token group of the expert it multiplies the tokens' K slice
-//     (A fragments, through perm for gate/up; each one feeds both blocks)
-//     with the two weight blocks (B fragments, fetched straight into
-//     registers from the blocked MFMA layout) with v_mfma_f32_32x32x16_bf16,
-//     P k-steps of loads in flight ahead of the MFMAs (plain loads, so the
-//     compiler's wait counts are exact);
+//   - for the expert's tokens, 32-row groups taken two at a time, it
+//     multiplies the tokens' K slice (A fragments, through perm for gate/up;
+//     each one feeds both blocks) with the two weight blocks (B fragments,
+//     fetched straight into registers from the blocked MFMA layout, each one
+//     feeding both token groups) with v_mfma_f32_32x32x16_bf16, P k-steps of
+//     loads in flight ahead of the MFMAs (plain loads, so the compiler's wait
+//     counts are exact); an expert with up to 64 rows streams its weights
+//     once;
 //   - it writes the fp32 partial sums of its slice: P[s][p][nb*32 + j].
 // K slices split every expert's weights into many equal, independent items,
 // which keeps all compute units streaming. Weights are read with
@@ -70,10 +72,88 @@ __device__ __forceinline__ void store_item(const DecodeArgs& g, float* out, int 
     }
 }
 
-template <bool GATE_UP>
+// One pass of an item's K slice over G consecutive 32-token groups of the
+// expert, from row r0 on: every weight fragment fetched feeds the MFMAs of
+// all G groups, so an expert with up to 32*G rows streams its weight blocks
+// once. Each group's accumulators see the same MFMA sequence as in a pass of
+// its own (the results do not depend on G).
+template <bool GATE_UP, int G>
+__device__ __forceinline__ void decode_pass(const DecodeArgs& g, const Vec16* bp, int64_t bst, float* out, int N, int K,
+                                            int seg0, int r0, int cnt, int nb, int kb0, int kb1, int lane)
+{
+    static_assert(G == 1 || G == 2, "one or two token groups per pass");
+    const Vec16* ap[G];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+        const int r = min(r0 + 32 * gi + (lane & 31), cnt - 1);
+        const int src = GATE_UP ? g.perm[seg0 + r] : seg0 + r;
+        ap[gi] = (const Vec16*)((const uint16_t*)g.a + (int64_t)src * K) + (lane >> 5);
+    }
+    // accumulators as named values (group, weight block): the conditional
+    // MFMAs below then update them in place, with no copies between blocks
+    floatx16 acc00, acc01, acc10, acc11;
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+        acc00[q] = acc01[q] = acc10[q] = acc11[q] = 0.f;
+    Vec16 a0[G][kP], b0[kP], c0[kP], a1[G][kP], b1[kP], c1[kP];
+    auto mfma4 = [&](const Vec16 (&a)[G][kP], const Vec16& b, const Vec16& c, int i) {
+        acc00 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[0][i]), as_bf16x8(b), acc00, 0, 0, 0);
+        acc01 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[0][i]), as_bf16x8(c), acc01, 0, 0, 0);
+        if constexpr (G == 2) {
+            acc10 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[G - 1][i]), as_bf16x8(b), acc10, 0, 0, 0);
+            acc11 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[G - 1][i]), as_bf16x8(c), acc11, 0, 0, 0);
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < kP; ++i) {
+        const int kb = min(kb0 + i, kb1 - 1);
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi)
+            a0[gi][i] = ap[gi][kb * 2];
+        b0[i] = __builtin_nontemporal_load(&bp[(int64_t)kb * kWave]);
+        c0[i] = __builtin_nontemporal_load(&bp[bst + (int64_t)kb * kWave]);
+    }
+    for (int kb = kb0; kb < kb1; kb += 2 * kP) {
+#pragma unroll
+        for (int i = 0; i < kP; ++i) {
+            const int kk = min(kb + kP + i, kb1 - 1);
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi)
+                a1[gi][i] = ap[gi][kk * 2];
+            b1[i] = __builtin_nontemporal_load(&bp[(int64_t)kk * kWave]);
+            c1[i] = __builtin_nontemporal_load(&bp[bst + (int64_t)kk * kWave]);
+        }
+#pragma unroll
+        for (int i = 0; i < kP; ++i)
+            if (kb + i < kb1)
+                mfma4(a0, b0[i], c0[i], i);
+#pragma unroll
+        for (int i = 0; i < kP; ++i) {
+            const int kk = min(kb + 2 * kP + i, kb1 - 1);
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi)
+                a0[gi][i] = ap[gi][kk * 2];
+            b0[i] = __builtin_nontemporal_load(&bp[(int64_t)kk * kWave]);
+            c0[i] = __builtin_nontemporal_load(&bp[bst + (int64_t)kk * kWave]);
+        }
+#pragma unroll
+        for (int i = 0; i < kP; ++i)
+            if (kb + kP + i < kb1)
+                mfma4(a1, b1[i], c1[i], i);
+    }
+    store_item<GATE_UP>(g, out, N, seg0, r0, cnt, nb, lane, acc00, acc01);
+    if constexpr (G == 2)
+        store_item<GATE_UP>(g, out, N, seg0, r0 + 32, cnt, nb, lane, acc10, acc11);
+}
+
+// GMAX: token groups per weight pass, at most (1 for calls whose experts
+// hold at most 32 rows each, where the pair code would only cost)
+template <bool GATE_UP, int GMAX>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_gemm_kernel(DecodeArgs g)
 {
     constexpr bool gate_up = GATE_UP;
+    if (g.gate_rows > 0 && max_expert_rows(g.offsets, g.E) > g.gate_rows)
+        return;  // the tiled kernels take this call
     const int lane = threadIdx.x % kWave;
     const int W = gridDim.x * (kThreads / kWave);
     const int w0 = blockIdx.x * (kThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -83,7 +163,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int NB2 = NB / 2;  // items cover two weight blocks
     const int items = g.E * NB2 * S;
     const Vec16* B = (const Vec16*)g.b;
-    const uint16_t* Abase = (const uint16_t*)g.a;
 
     for (int it = w0; it < items; it += W) {
         const int s = it % S;
@@ -99,51 +178,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         const int64_t bst = (int64_t)KB * kWave;  // next weight block
         float* out = g.part + (int64_t)s * g.A * N + nb * 32 + (lane & 31);
 
-        for (int r0 = 0; r0 < cnt; r0 += 32) {
-            const int r = min(r0 + (lane & 31), cnt - 1);
-            const int src = gate_up ? g.perm[seg0 + r] : seg0 + r;
-            const Vec16* ap = (const Vec16*)(Abase + (int64_t)src * K) + (lane >> 5);
-            floatx16 acc0, acc1;
-#pragma unroll
-            for (int q = 0; q < 16; ++q)
-                acc0[q] = acc1[q] = 0.f;
-            Vec16 a0[kP], b0[kP], c0[kP], a1[kP], b1[kP], c1[kP];
-#pragma unroll
-            for (int i = 0; i < kP; ++i) {
-                const int kb = min(kb0 + i, kb1 - 1);
-                a0[i] = ap[kb * 2];
-                b0[i] = __builtin_nontemporal_load(&bp[(int64_t)kb * kWave]);
-                c0[i] = __builtin_nontemporal_load(&bp[bst + (int64_t)kb * kWave]);
-            }
-            for (int kb = kb0; kb < kb1; kb += 2 * kP) {
-#pragma unroll
-                for (int i = 0; i < kP; ++i) {
-                    const int kk = min(kb + kP + i, kb1 - 1);
-                    a1[i] = ap[kk * 2];
-                    b1[i] = __builtin_nontemporal_load(&bp[(int64_t)kk * kWave]);
-                    c1[i] = __builtin_nontemporal_load(&bp[bst + (int64_t)kk * kWave]);
+        // token groups in pairs (one weight pass per 64 rows), a last single
+        // group where at most 32 rows remain
+        for (int r0 = 0; r0 < cnt; r0 += 32 * GMAX) {
+            if constexpr (GMAX == 2) {
+                if (cnt - r0 > 32) {
+                    decode_pass<gate_up, 2>(g, bp, bst, out, N, K, seg0, r0, cnt, nb, kb0, kb1, lane);
+                    continue;
                 }
-#pragma unroll
-                for (int i = 0; i < kP; ++i)
-                    if (kb + i < kb1) {
-                        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0[i]), as_bf16x8(b0[i]), acc0, 0, 0, 0);
-                        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0[i]), as_bf16x8(c0[i]), acc1, 0, 0, 0);
-                    }
-#pragma unroll
-                for (int i = 0; i < kP; ++i) {
-                    const int kk = min(kb + 2 * kP + i, kb1 - 1);
-                    a0[i] = ap[kk * 2];
-                    b0[i] = __builtin_nontemporal_load(&bp[(int64_t)kk * kWave]);
-                    c0[i] = __builtin_nontemporal_load(&bp[bst + (int64_t)kk * kWave]);
-                }
-#pragma unroll
-                for (int i = 0; i < kP; ++i)
-                    if (kb + kP + i < kb1) {
-                        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1[i]), as_bf16x8(b1[i]), acc0, 0, 0, 0);
-                        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1[i]), as_bf16x8(c1[i]), acc1, 0, 0, 0);
-                    }
             }
-            store_item<gate_up>(g, out, N, seg0, r0, cnt, nb, lane, acc0, acc1);
+            decode_pass<gate_up, 1>(g, bp, bst, out, N, K, seg0, r0, cnt, nb, kb0, kb1, lane);
         }
     }
 }
@@ -153,6 +197,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 {
     constexpr bool gate_up = GATE_UP;
     constexpr int kQ = 4;  // 32-wide k steps of loads in flight per wave (two sets)
+    if (g.gate_rows > 0 && max_expert_rows(g.offsets, g.E) > g.gate_rows)
+        return;  // the tiled kernels take this call
     const int lane = threadIdx.x % kWave;
     const int W = gridDim.x * (kThreads / kWave);
     const int w0 = blockIdx.x * (kThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -275,6 +321,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 {
     constexpr bool gate_up = GATE_UP;
     constexpr int kQ = 3;  // 64-wide k steps of loads in flight per wave (two sets)
+    if (g.gate_rows > 0 && max_expert_rows(g.offsets, g.E) > g.gate_rows)
+        return;  // the tiled kernels take this call
     const int lane = threadIdx.x % kWave;
     const int W = gridDim.x * (kThreads / kWave);
     const int w0 = blockIdx.x * (kThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -373,8 +421,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // with gate/up interleaved by 32 rows: h column c is gate row (c/32)*64 + c%32
 // and up row (c/32)*64 + 32 + c%32 of the combined [2f] weight rows. Four
 // consecutive columns per thread, slices summed in order.
-__global__ __launch_bounds__(256) void decode_silu_kernel(const float* part, uint16_t* H, int A, int f, int S)
+__global__ __launch_bounds__(256) void decode_silu_kernel(const float* part, uint16_t* H, int A, int f, int S,
+                                                          const int32_t* offsets, int E, int gate_rows)
 {
+    if (gate_rows > 0 && max_expert_rows(offsets, E) > gate_rows)
+        return;  // the tiled gate/up GEMM wrote H
     const int64_t groups = (int64_t)A * (f / 4);
     const int64_t sstride = (int64_t)A * 2 * f;
     for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < groups;
@@ -437,14 +488,17 @@ hipError_t launch_decode_gemm(const DecodeArgs& a, int gate_up, int cus, hipStre
             hipLaunchKernelGGL(decode_gemm_f8_kernel<true>, dim3(cus * 2), dim3(kThreads), 0, s, a);
         else
             hipLaunchKernelGGL(decode_gemm_f8_kernel<false>, dim3(cus * 2), dim3(kThreads), 0, s, a);
-    } else if (gate_up)
-        hipLaunchKernelGGL(decode_gemm_kernel<true>, dim3(cus * 2), dim3(kThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL(decode_gemm_kernel<false>, dim3(cus * 2), dim3(kThreads), 0, s, a);
+    } else {
+        const bool single = a.max_rows >= 1 && a.max_rows <= 32;
+        auto k = gate_up ? (single ? decode_gemm_kernel<true, 1> : decode_gemm_kernel<true, 2>)
+                         : (single ? decode_gemm_kernel<false, 1> : decode_gemm_kernel<false, 2>);
+        hipLaunchKernelGGL(k, dim3(cus * 2), dim3(kThreads), 0, s, a);
+    }
     return hipGetLastError();
 }
 
-hipError_t launch_decode_silu(const float* part, void* H, int A, int f, int S, hipStream_t s)
+hipError_t launch_decode_silu(const float* part, void* H, int A, int f, int S, const int32_t* offsets, int E,
+                              int gate_rows, hipStream_t s)
 {
     const int64_t groups = (int64_t)A * (f / 4);
     int64_t blocks = (groups + 255) / 256;
@@ -452,7 +506,8 @@ hipError_t launch_decode_silu(const float* part, void* H, int A, int f, int S, h
         blocks = 4096;
     if (blocks < 1)
         return hipSuccess;
-    hipLaunchKernelGGL(decode_silu_kernel, dim3((unsigned)blocks), dim3(256), 0, s, part, (uint16_t*)H, A, f, S);
+    hipLaunchKernelGGL(decode_silu_kernel, dim3((unsigned)blocks), dim3(256), 0, s, part, (uint16_t*)H, A, f, S,
+                       offsets, E, gate_rows);
     return hipGetLastError();
 }
 

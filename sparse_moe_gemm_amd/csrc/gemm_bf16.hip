@@ -879,6 +879,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
     TileTable tt;
     const int total = make_table<BM, SM>(g.offsets, g.E, lane, NT * S, tt);
+    if (g.skip_rows > 0 && table_max_rows(tt) <= g.skip_rows)
+        return;  // the small-batch kernels take this call
     int L = blockIdx.x;
     const int GRID = gridDim.x;
     const bool xm = g.xcd_map != 0;
@@ -1572,6 +1574,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
     TileTable tt;
     const int total = make_table<BM, SM>(g.offsets, g.E, lane, NT * S, tt);
+    if (g.skip_rows > 0 && table_max_rows(tt) <= g.skip_rows)
+        return;  // the small-batch kernels take this call
     int L = blockIdx.x;
     const int GRID = gridDim.x;
     const bool xm = g.xcd_map != 0;

@@ -87,6 +87,17 @@ __device__ __forceinline__ int make_table(const int32_t* offsets, int E, int lan
     return t.tiles[0] + t.tiles[1];
 }
 
+// Most rows any expert holds, from a table make_table filled (every lane of
+// the wave gets the same value).
+__device__ __forceinline__ int table_max_rows(const TileTable& t)
+{
+    int m = max(max(t.cnt[0], t.cnt[1]), max(t.cnt[2], t.cnt[3]));
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d >>= 1)
+        m = max(m, __shfl_xor(m, d, kWave));
+    return __builtin_amdgcn_readfirstlane(m);
+}
+
 // Tile behind launch index L, or -1 for none. Workgroups go to the 8 XCDs
 // round robin and a persistent workgroup takes indices L, L + grid, ..., so
 // index L runs on XCD L % 8. Plain placement (xm false): tile L, so tiles

@@ -175,7 +175,10 @@ def _layer_case(cfg, inp, act_fp8=False):
     return g, rep
 
 
-PATHS = {"tiled": "0", "small-batch": "65536"}
+# the small-batch path forced: every call within CMOE_DECODE_MAX_A, and no
+# per-expert row test on the device (CMOE_DECODE_MAX_ROWS=0)
+PATHS = {"tiled": {"CMOE_DECODE_MAX_A": "0"},
+         "small-batch": {"CMOE_DECODE_MAX_A": "65536", "CMOE_DECODE_MAX_ROWS": "0"}}
 CASES = [
     C("decode-small", 32, 512, 8, 2, 1024, "bf16"),
     C("one-token", 1, 128, 8, 2, 128, "bf16"),
@@ -193,7 +196,8 @@ CASES = [
 @pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("cfg", CASES, ids=[c.name for c in CASES])
 def test_fp8_layer_parity(cfg, path, monkeypatch):
-    monkeypatch.setenv("CMOE_DECODE_MAX_A", PATHS[path])
+    for key, val in PATHS[path].items():
+        monkeypatch.setenv(key, val)
     print(f"fp8 case {cfg} path {path}", flush=True)
     inp = synth.make_inputs(cfg)
     g, rep = _layer_case(cfg, inp)
@@ -239,7 +243,8 @@ Q8_CASES = [
 @pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("cfg", Q8_CASES, ids=[c.name for c in Q8_CASES])
 def test_w8a8_layer_parity(cfg, path, monkeypatch):
-    monkeypatch.setenv("CMOE_DECODE_MAX_A", PATHS[path])
+    for key, val in PATHS[path].items():
+        monkeypatch.setenv(key, val)
     print(f"w8a8 case {cfg} path {path}", flush=True)
     inp = synth.make_inputs(cfg)
     g, rep = _layer_case(cfg, inp, act_fp8=True)

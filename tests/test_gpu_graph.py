@@ -1,8 +1,9 @@
 """The forward captured into a HIP graph (torch.cuda.graph on the stream the
 handle was created with) and replayed: every replay must give the eager
 forward's outputs bit for bit, with eager forwards of other inputs and
-synchronizations between the replays. Both GEMM paths (small-batch and tiled)
-and the static-scratch entry point's kernels are covered; the forward enqueues
+synchronizations between the replays. Both GEMM paths (small-batch and tiled,
+also enqueued together with the choice made on the device) and the
+static-scratch entry point's kernels are covered; the forward enqueues
 kernels only (no memset, no allocation, no synchronization in ASYNC mode)."""
 import numpy as np
 import pytest
@@ -17,6 +18,8 @@ CASES = [
     C("decode-small", 32, 512, 8, 2, 1024, "bf16"),
     C("mixtral-small", 700, 256, 8, 2, 512, "bf16", {1: 0.5}),
     C("fine-grained-small", 1000, 256, 128, 4, 256, "bf16"),
+    # both GEMM paths enqueued, the device picks the small-batch kernels
+    C("both-paths-small", 200, 256, 64, 2, 256, "bf16"),
 ]
 
 

@@ -83,13 +83,20 @@ def test_small_layer_parity(cfg):
 # small-batch (weight streaming) path, forced through the init-time threshold
 # CMOE_DECODE_MAX_A. The small-batch path is taken here also for batches far
 # larger than it is meant for (several 32-token groups per expert, hot
-# experts), which exercises its row-group loop and its K slices.
-PATHS = {"tiled": "0", "small-batch": "65536"}
+# experts), which exercises its row-group loop and its K slices; one expert
+# with 33, 65 and 130 rows puts a group pair or a lone group of 1 or 2 rows
+# at the end.
+# the small-batch path forced: every call within CMOE_DECODE_MAX_A, and no
+# per-expert row test on the device (CMOE_DECODE_MAX_ROWS=0)
+PATHS = {"tiled": {"CMOE_DECODE_MAX_A": "0"},
+         "small-batch": {"CMOE_DECODE_MAX_A": "65536", "CMOE_DECODE_MAX_ROWS": "0"}}
 BOTH = [
     C("decode-small", 32, 512, 8, 2, 1024, "bf16"),
     C("one-token", 1, 128, 8, 2, 128, "bf16"),
     C("ragged-17", 17, 384, 16, 3, 384, "bf16"),
     C("single-expert", 130, 128, 1, 1, 128, "bf16"),
+    C("single-expert-33", 33, 128, 1, 1, 128, "bf16"),
+    C("single-expert-65", 65, 128, 1, 1, 128, "bf16"),
     C("mixtral-small", 700, 256, 8, 2, 512, "bf16"),
     C("k8-E256", 64, 128, 256, 8, 128, "bf16"),
     C("skewed-small", 2000, 256, 64, 2, 128, "bf16", {0: 4.0, 3: 4.0}),
@@ -99,7 +106,8 @@ BOTH = [
 @pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("cfg", BOTH, ids=[c.name for c in BOTH])
 def test_both_gemm_paths(cfg, path, monkeypatch):
-    monkeypatch.setenv("CMOE_DECODE_MAX_A", PATHS[path])
+    for key, val in PATHS[path].items():
+        monkeypatch.setenv(key, val)
     print(f"case {cfg} path {path}", flush=True)
     inp = synth.make_inputs(cfg)
     layer = make_layer(cfg, inp)

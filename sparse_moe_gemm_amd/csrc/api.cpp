@@ -78,8 +78,8 @@ struct colibri_moe {
     bool dec_fuse_silu;          // small-batch gate/up writes H itself (no K slices)
     bool fuse_combine;  // bf16 tiled path: combine in the down GEMM's epilogue
     int cus;        // compute units of the device (persistent GEMM grid)
-    int dec_max_a;  // bf16 calls with T*k <= dec_max_a take the small-batch path
-    int dec_gate_rows;  // ... when no expert holds more rows (0: always; see create)
+    int dec_max_a;      // bf16 calls with T*k <= dec_max_a may take the small-batch path,
+    int dec_gate_rows;  // those whose experts hold at most this many rows (0: all of them)
     int dec_split_gu, dec_split_dn;  // its K slices (gate/up, down)
 };
 
@@ -232,7 +232,7 @@ size_t layout_workspace(const colibri_moe* h, int64_t T, bool up_to, uint8_t* ba
     // Ys: the down GEMM's partial sums (kMaxSplit for bf16), and on the
     // small-batch path also the gate/up slice partials before SiLU.
     size_t ys_floats = (c.dtype == COLIBRI_MOE_BF16 ? (size_t)cmoe::kMaxSplit : 1) * A * d;
-    // (a call takes the small-batch path when A <= dec_max_a)
+    // (calls with A <= dec_max_a may take the small-batch path)
     if (c.dtype == COLIBRI_MOE_BF16 && h->dec_max_a > 0 && (up_to || A <= (size_t)h->dec_max_a)) {
         const size_t ad = std::min(A, (size_t)h->dec_max_a);
         if (!h->dec_fuse_silu)  // else the gate/up kernel writes H itself
@@ -371,7 +371,8 @@ colibri_moe_status_t colibri_moe_init(colibri_moe_t** out, const colibri_moe_con
     // 64-wide K stages (grouped_gemm64_kernel) for the bf16 gate/up GEMM
     // (with tile groups of 16 n-tiles): mixtral gate/up 1.76 -> 1.68 ms, one
     // expert of 8192 rows 1.66 -> 1.44 ms; the down GEMM keeps 32-wide stages
-    // (up to 12% slower with 64). Same sums in the same order, so outputs are
+    // (with 64: mixtral 915 -> 920 us, fine-grained 164 -> 167, skewed
+    // 428 -> 449, with the current epilogues). Same sums in the same order, so outputs are
     // bit-identical either way. CMOE_K64: bit 0 gate/up, bit 1 down, bit 2
     // gate/up whatever the rows per expert.
     h->k64 = env_int("CMOE_K64", 1, 0, 7);

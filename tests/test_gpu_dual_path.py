@@ -62,3 +62,21 @@ def test_device_path_choice(cfg, want, weights, monkeypatch):
         print(chosen, most, compare(cfg, inp, g), flush=True)
     else:
         print(chosen, most, flush=True)
+
+
+def test_row_limit_boundary(monkeypatch):
+    """The device compares the largest expert's rows with the limit
+    inclusively: a limit equal to that count takes the small-batch path, one
+    less the tiled path (both with every call enqueueing both paths)."""
+    cfg = C("e8-moderate", 120, 256, 8, 2, 512, "bf16")
+    print(f"dual-path boundary case {cfg}", flush=True)
+    monkeypatch.delenv("CMOE_DECODE_MAX_A", raising=False)
+    inp = synth.make_inputs(cfg)
+    small = _run(cfg, inp, 0, FORCED["small-batch"], monkeypatch)
+    tiled = _run(cfg, inp, 0, FORCED["tiled"], monkeypatch)
+    most = int(tiled["expert_counts"].max())
+    assert 1 < most < cfg.T and not np.array_equal(small["y"], tiled["y"])
+    for limit, ref in ((most, small), (most - 1, tiled)):
+        g = _run(cfg, inp, 0, {"CMOE_DECODE_MAX_ROWS": str(limit)}, monkeypatch)
+        for key in g:
+            assert np.array_equal(g[key], ref[key]), f"limit {limit}, most rows {most}: {key}"

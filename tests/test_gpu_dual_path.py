@@ -80,3 +80,29 @@ def test_row_limit_boundary(monkeypatch):
         g = _run(cfg, inp, 0, {"CMOE_DECODE_MAX_ROWS": str(limit)}, monkeypatch)
         for key in g:
             assert np.array_equal(g[key], ref[key]), f"limit {limit}, most rows {most}: {key}"
+
+
+def test_fused_combine_handle_alternating_calls(monkeypatch):
+    """A handle with the combine fused into the tiled down GEMM
+    (CMOE_FUSE_COMBINE=1): calls that enqueue both paths run the combine as
+    its own kernel, tiled-only calls (more than CMOE_DECODE_MAX_A assignments)
+    fuse it. Alternating the two must match a handle without the fusion bit
+    for bit, so the fused combine's arrival counts stay at zero between
+    calls."""
+    cfg = C("alternating", 1200, 256, 8, 2, 512, "bf16")
+    print(f"dual-path fused-combine case {cfg}", flush=True)
+    monkeypatch.delenv("CMOE_DECODE_MAX_A", raising=False)
+    monkeypatch.delenv("CMOE_DECODE_MAX_ROWS", raising=False)
+    inp = synth.make_inputs(cfg)
+    x = inp["x"]
+    sizes = [300, cfg.T, 60, cfg.T, 300]  # 600 and 120 assignments: both paths; 2400: tiled only
+    outs = {}
+    for fuse in ("0", "1"):
+        monkeypatch.setenv("CMOE_FUSE_COMBINE", fuse)
+        layer = make_layer(cfg, inp)
+        outs[fuse] = [run_gpu(layer, x[:n]) for n in sizes]
+        layer.close()
+    for i, (a, b) in enumerate(zip(outs["0"], outs["1"])):
+        for key in a:
+            assert np.array_equal(a[key], b[key]), f"call {i} ({sizes[i]} tokens): {key}"
+    print(compare(cfg, inp, outs["1"][1]), flush=True)
